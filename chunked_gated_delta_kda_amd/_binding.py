@@ -1,0 +1,196 @@
+"""ctypes binding of libkda (include/kda.h).
+
+Argument marshalling only: dtype, shape and device checks, allocation of the
+outputs and the workspace with torch, and the current HIP stream.  Every step
+of the computation runs in the HIP kernels of libkda.so; if the library is
+missing this module raises instead of computing anything elsewhere.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libkda.so"
+
+_STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
+                 3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_LAUNCH"}
+
+# Every symbol include/kda.h declares.
+EXPORTS = ("kda_fwd", "gdn_fwd", "kda_fwd_workspace_size", "gdn_fwd_workspace_size",
+           "kda_status_str", "kda_version")
+
+
+class LibKdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: Path | str | None = None):
+    """Load libkda.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"{p} is missing: build it with "
+                           f"`python -m chunked_gated_delta_kda_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    vp, u16p, f32p, i32p = (ctypes.c_void_p,) * 4
+    i32, f32, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd.argtypes = [u16p, u16p, u16p, u16p, u16p, f32p, f32p, f32, f32, f32p, f32p, i32p,
+                            i32, i32, i32, i32, i32, i32, u16p, vp, sz, vp]
+    lib.gdn_fwd.restype = ctypes.c_int
+    lib.gdn_fwd.argtypes = [u16p, u16p, u16p, f32p, u16p, f32, f32p, f32p, i32p, i32, i32, i32,
+                            i32, i32, i32, u16p, vp, sz, vp]
+    for name in ("kda_fwd_workspace_size", "gdn_fwd_workspace_size"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_size_t
+        fn.argtypes = [i32] * 6
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_status_str.argtypes = [ctypes.c_int]
+    lib.kda_version.restype = ctypes.c_int
+    lib.kda_version.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().kda_status_str(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().kda_version())
+
+
+def workspace_size(B, T, H, K, V, num_seqs=None, kind="kda") -> int:
+    fn = load().kda_fwd_workspace_size if kind == "kda" else load().gdn_fwd_workspace_size
+    return int(fn(B, T, H, K, V, B if num_seqs is None else num_seqs))
+
+
+# ---------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens, workspace,
+             kind, out=None, final_out=None):
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, K]")
+    dev = q.device
+    B, T, H, K = q.shape
+    _need(k, "k", torch.bfloat16, (B, T, H, K), dev)
+    if v.dim() != 4:
+        raise ValueError("v must be [B, T, H, V]")
+    V = v.shape[3]
+    _need(v, "v", torch.bfloat16, (B, T, H, V), dev)
+    _need(beta, "beta", torch.bfloat16, (B, T, H), dev)
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be 1-D with num_seqs + 1 entries")
+        if B != 1:
+            raise ValueError("cu_seqlens needs B == 1 (sequences packed along T)")
+        N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, K, V), dev)
+    if scale is None:
+        scale = K ** -0.5
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, (B, T, H, V), dev)
+    o = out
+    final = None
+    if output_final_state:
+        if final_out is None:
+            final_out = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+        else:
+            _need(final_out, "final_out", torch.float32, (N, H, K, V), dev)
+        final = final_out
+    need = workspace_size(B, T, H, K, V, N, kind)
+    if need == 0:
+        raise LibKdaError(2, status_str(2))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
+        raise LibKdaError(3, status_str(3))
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    return dict(B=B, T=T, H=H, K=K, V=V, N=N, scale=float(scale), o=o, final=final,
+                workspace=workspace, stream=stream)
+
+
+def kda_fwd(q, k, v, g, beta, A_log, dt_bias, lower_bound=-5.0, scale=None, initial_state=None,
+            output_final_state=True, cu_seqlens=None, workspace=None, out=None,
+            final_out=None):
+    """KDA forward on the GPU.  q, k, g [B,T,H,K] bf16; v [B,T,H,V] bf16; beta logits
+    [B,T,H] bf16; A_log [H] fp32; dt_bias [H,K] (or [H*K]) fp32; initial_state
+    [N,H,K,V] fp32 or None; cu_seqlens int32 [N+1] or None (B must then be 1).
+    ``workspace``, ``out`` and ``final_out`` optionally supply preallocated device
+    buffers.  Returns (o [B,T,H,V] bf16, final_state [N,H,K,V] fp32 or None)."""
+    torch = _torch()
+    a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens,
+                 workspace, "kda", out, final_out)
+    B, T, H, K = a["B"], a["T"], a["H"], a["K"]
+    _need(g, "g", torch.bfloat16, (B, T, H, K), q.device)
+    _need(A_log, "A_log", torch.float32, (H,), q.device)
+    _need(dt_bias, "dt_bias", torch.float32, None, q.device)
+    if dt_bias.numel() != H * K:
+        raise ValueError("dt_bias must hold H * K values ([H, K] or [H * K])")
+    st = load().kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                        _ptr(dt_bias), float(lower_bound), a["scale"], _ptr(initial_state),
+                        _ptr(a["final"]), _ptr(cu_seqlens), a["N"], B, T, H, K, a["V"],
+                        _ptr(a["o"]), _ptr(a["workspace"]),
+                        a["workspace"].numel() * a["workspace"].element_size(), a["stream"])
+    if st != 0:
+        raise LibKdaError(st, status_str(st))
+    return a["o"], a["final"]
+
+
+def gdn_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+            cu_seqlens=None, workspace=None, out=None, final_out=None):
+    """GDN forward on the GPU.  g is the fp32 log decay [B,T,H] (<= 0); beta are
+    probabilities [B,T,H] bf16, used as given.  Other arguments as kda_fwd."""
+    torch = _torch()
+    a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens,
+                 workspace, "gdn", out, final_out)
+    B, T, H = a["B"], a["T"], a["H"]
+    _need(g, "g", torch.float32, (B, T, H), q.device)
+    st = load().gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), a["scale"],
+                        _ptr(initial_state), _ptr(a["final"]), _ptr(cu_seqlens), a["N"], B, T,
+                        H, a["K"], a["V"], _ptr(a["o"]), _ptr(a["workspace"]),
+                        a["workspace"].numel() * a["workspace"].element_size(), a["stream"])
+    if st != 0:
+        raise LibKdaError(st, status_str(st))
+    return a["o"], a["final"]

@@ -1,0 +1,114 @@
+// kda_common.h -- shared device definitions for the gfx950 KDA / GDN kernels.
+//
+// Chunk size, MFMA operand layouts, the per-chunk record written by kda_prep
+// and read by kda_recur, and the transcendental helpers built on the gfx950
+// hardware instructions (v_exp_f32 = 2^x, v_log_f32 = log2 x, v_rcp_f32,
+// v_rsq_f32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Tokens per chunk.  The FlashKDA summary (discuss.pytorch.kr, section
+// "Flash Linear Attention과 비교") motivates 16: the 16x16 intra-chunk inverse is
+// cheap, and with the gate floored at -5 a 16-token cumulative decay stays
+// within 16*5 = 80 < ln(FLT_MAX) ~ 88.7, so the factored decays exp(+-G) fit
+// the fp32/bf16 exponent range without intra-chunk rescaling.
+constexpr int C = 16;
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float NORM_EPS = 1e-6f;
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) short short4_t;
+typedef __attribute__((ext_vector_type(4))) float floatx4;
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] B[32x16].
+// Lane l = r + 16 g (r = l % 16, g = l / 16) holds A row r and B column r,
+// eight k-slots each; element e of lane group g of A multiplies element e of
+// lane group g of B, so any assignment of real k indices to (g, e) works as
+// long as A and B use the same one.  D: lane l holds D[4g + i][r], i = 0..3.
+__device__ __forceinline__ floatx4 mfma32(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x16_bf16: lane l = r + 16 g holds A[r][4g + i], B[4g + i][r];
+// D as above.  The D layout of a 16x16 result therefore is exactly the B
+// layout of the next 16x16x16 product that contracts over D's row index.
+__device__ __forceinline__ floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
+                                                     __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) {
+    bf16x4 r;
+    r[0] = (bf16)x[0];
+    r[1] = (bf16)x[1];
+    r[2] = (bf16)x[2];
+    r[3] = (bf16)x[3];
+    return r;
+}
+
+// ---------------------------------------------------------------- math
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float rsq_hw(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^-|x|), with both
+// exponentials taken base 2.
+__device__ __forceinline__ float softplus_f(float x) {
+    float t = exp2_hw(-fabsf(x) * LOG2E);
+    return fmaxf(x, 0.f) + LN2 * log2_hw(1.f + t);
+}
+// sigmoid(x) = 1 / (1 + e^-x); saturates to exactly 0 or 1 for large |x|.
+__device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.f + exp2_hw(-x * LOG2E)); }
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// ---------------------------------------------------------------- record
+// Per (chunk slot, head) record written by kda_prep and read by kda_recur.
+// All matrices are stored in the exact per-lane order of the MFMA operand
+// that consumes them, so kda_recur reads each fragment with one 8- or
+// 16-byte load per lane and the whole record is one contiguous stream.
+//
+// Within a chunk of C = 16 tokens (row r), G[r][c] = sum_{s<=r} log a_s[c] and
+// Gam = exp(G):
+//   nKG  = -(k^ * Gam)         [16 x K]  A operand of 16x16x32 against S
+//   QG   =   q^ * Gam          [16 x K]  B operand of 16x16x32 against S^T
+//   KdT  = (k^ * Gam_C / Gam)^T[K x 16]  A operand of 16x16x16 against U'
+//   Aqk  = tril(QG (k^/Gam)^T) [16 x 16] B operand (transposed) for O^T
+//   Tb   = (I + A)^-1 diag(b)  [16 x 16] A operand for U' = Tb (V - KG S)
+//   GamC = Gam at the chunk's last row, fp32 [K]
+// with A[r][j] = b_r sum_c (k^ Gam)[r][c] (k^/Gam)[j][c] for j < r.
+//
+// K index order inside a 16x16x32 fragment: k-step j (32 channels), lane
+// group g, element e  ->  channel 32 j + 16 (e / 4) + 4 g + (e % 4).  This is
+// the order in which kda_recur's fp32 state tiles (D layout, 16 channels per
+// tile, lane group g holding rows 4g..4g+3) become the B/A operand of the
+// next chunk without any data movement.
+template <int K>
+struct Rec {
+    static constexpr int KSTEPS = K / 32;               // 16x16x32 k-steps
+    static constexpr int KTILES = K / 16;               // 16-row state tiles
+    static constexpr int NKG = 0;                       // bf16 [KSTEPS][4][16][8]
+    static constexpr int QG = NKG + C * K * 2;          // bf16 [KSTEPS][4][16][8]
+    static constexpr int KDT = QG + C * K * 2;          // bf16 [KTILES][4][16][4]
+    static constexpr int AQK = KDT + C * K * 2;         // bf16 [4][16][4]
+    static constexpr int TB = AQK + C * C * 2;          // bf16 [4][16][4]
+    static constexpr int GAMC = TB + C * C * 2;         // fp32 [K]
+    static constexpr int BYTES = GAMC + K * 4;
+};
+
+// channel of element e of lane group g in k-step j of a 16x16x32 fragment
+__host__ __device__ constexpr int frag32_channel(int j, int g, int e) {
+    return 32 * j + 16 * (e >> 2) + 4 * g + (e & 3);
+}
+
+}  // namespace kda

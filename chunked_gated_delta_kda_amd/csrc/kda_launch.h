@@ -1,0 +1,47 @@
+// kda_launch.h -- host-side launch interface between the C-ABI layer and the
+// two kernels.  Pointers are device pointers; bf16 tensors are passed as
+// uint16_t bit patterns.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct PrepArgs {
+    const uint16_t* q;         // [tokens, H, K] bf16
+    const uint16_t* k;         // [tokens, H, K] bf16
+    const uint16_t* g_kda;     // KDA: pre-activation gate [tokens, H, K] bf16
+    const float* g_gdn;        // GDN: log decay [tokens, H] fp32
+    const uint16_t* beta;      // [tokens, H] bf16 (KDA logits / GDN probabilities)
+    const float* A_log;        // [H] (KDA)
+    const float* dt_bias;      // [H, K] (KDA)
+    float lower_bound;         // KDA floor of the log decay
+    int32_t H;
+    int32_t n_seqs;
+    const int32_t* seq_start;  // [n_seqs + 1] flattened token offsets
+    const int32_t* chunk_off;  // [n_seqs + 1] first chunk slot of each sequence
+    unsigned char* rec;        // [slots, H, record bytes]
+};
+
+struct RecurArgs {
+    const uint16_t* v;             // [tokens, H, V] bf16
+    const unsigned char* rec;      // records from kda_prep
+    const float* initial_state;    // [n_seqs, H, K, V] or null (zeros)
+    float* final_state;            // [n_seqs, H, K, V] or null (not written)
+    uint16_t* o;                   // [tokens, H, V] bf16
+    float scale;
+    int32_t H;
+    int32_t V;
+    int32_t n_seqs;
+    const int32_t* seq_start;
+    const int32_t* chunk_off;
+};
+
+void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t total_tokens,
+                      int32_t* seq_start, int32_t* chunk_off, hipStream_t stream);
+void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream);
+void launch_recur(const RecurArgs& a, int K, hipStream_t stream);
+int record_bytes(int K);
+
+}  // namespace kda

@@ -1,0 +1,346 @@
+// kda_prep.hip -- token-parallel half of the chunked forward pass (gfx950).
+//
+// One workgroup per (16-token chunk, head).  It fuses the gate activation,
+// the sigmoid of beta, the in-chunk cumulative decay, the q/k L2 norms, the
+// two intra-chunk 16x16 matrices (bf16 MFMA over K), the exact inverse
+// (I + A)^-1 by the doubling product, and writes the chunk record that
+// kda_recur consumes (layout in kda_common.h).
+//
+// The split into a token-parallel kernel and a head-parallel recurrence
+// follows the FlashKDA summary (discuss.pytorch.kr, section "커널 퓨전(Kernel
+// Fusion) 전략의 분리"): gate activation, L2 norm, decay and the matrix inverse
+// go in the first kernel; the chunked delta recurrence and the output
+// projection in the second.  The gate, beta and norm definitions follow the
+// parameter table of the same page (section "FlashKDA의 KDA 연산 구조"); the
+// chunk size and the exact 16x16 inverse follow its section "Flash Linear
+// Attention과 비교".
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+// The doubling product: A strictly lower triangular (16 x 16) is nilpotent,
+// A^16 = 0, so with N = -A
+//   (I + A)^-1 = sum_{p=0}^{15} N^p = (I + N)(I + N^2)(I + N^4)(I + N^8)
+// exactly (no truncation).  Computed in fp32.
+constexpr int LDA = C + 1;  // padded row stride of the fp32 16x16 buffers
+
+template <int K>
+struct PrepSmem {
+    static constexpr int LDK = K + 8;       // padded bf16 row stride (bank spread)
+    float la[C][K];                         // log2 decay, then its in-chunk prefix sum
+    bf16 kg[C][LDK];                        // k^ * Gam
+    bf16 kig[C][LDK];                       // k^ / Gam
+    bf16 qg[C][LDK];                        // q^ * Gam
+    float nmat[C][LDA];                     // N = -A
+    float n2[C][LDA], n4[C][LDA], n8[C][LDA];
+    float p1[C][LDA], p2[C][LDA];
+    float beta[C];
+    alignas(16) unsigned char rec[Rec<K>::BYTES];
+};
+
+template <int K, bool GDN>
+__global__ __launch_bounds__(256) void kda_prep_kernel(PrepArgs a) {
+    constexpr int EPT = K / 16;  // channels per thread in the token-row phase
+    using R = Rec<K>;
+    __shared__ PrepSmem<K> sm;
+
+    const int slot = blockIdx.x;
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x;
+
+    // ---- locate the chunk: chunk_off[n] <= slot < chunk_off[n+1]
+    const int total = a.chunk_off[a.n_seqs];
+    if (slot >= total) return;  // uniform over the workgroup
+    int lo = 0, hi = a.n_seqs;  // invariant: chunk_off[lo] <= slot < chunk_off[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (a.chunk_off[mid] <= slot) lo = mid; else hi = mid;
+    }
+    const int n = lo;
+    const int64_t start = (int64_t)a.seq_start[n] + (int64_t)C * (slot - a.chunk_off[n]);
+    const int nvalid = (int)min((int64_t)C, (int64_t)a.seq_start[n + 1] - start);
+
+    // ---- phase 1: one token row per 16 threads, EPT channels per thread
+    const int r = tid >> 4;
+    const int cg = tid & 15;
+    const int c0 = cg * EPT;
+    const bool valid = r < nvalid;
+    const int64_t row = (start + r) * a.H + h;  // flattened (token, head) row
+
+    float q[EPT], k[EPT], la[EPT];
+    float b = 0.f;
+    if (valid) {
+        const uint16_t* qp = a.q + row * K + c0;
+        const uint16_t* kp = a.k + row * K + c0;
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+            uint2 qv = *reinterpret_cast<const uint2*>(qp + e);
+            uint2 kv = *reinterpret_cast<const uint2*>(kp + e);
+            q[e + 0] = bf2f(qv.x & 0xffff); q[e + 1] = bf2f(qv.x >> 16);
+            q[e + 2] = bf2f(qv.y & 0xffff); q[e + 3] = bf2f(qv.y >> 16);
+            k[e + 0] = bf2f(kv.x & 0xffff); k[e + 1] = bf2f(kv.x >> 16);
+            k[e + 2] = bf2f(kv.y & 0xffff); k[e + 3] = bf2f(kv.y >> 16);
+        }
+        if constexpr (GDN) {
+            // GDN: g is the log decay itself, one scalar per (token, head).
+            const float l2 = a.g_gdn[row] * LOG2E;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) la[e] = l2;
+            b = bf2f(a.beta[row]);
+        } else {
+            // KDA: log a = max(lb, -exp(A_log[h]) * softplus(g + dt_bias[h, c]))
+            const float rate = exp2_hw(a.A_log[h] * LOG2E);
+            const uint16_t* gp = a.g_kda + row * K + c0;
+            const float* dp = a.dt_bias + (int64_t)h * K + c0;
+#pragma unroll
+            for (int e = 0; e < EPT; e += 4) {
+                uint2 gv = *reinterpret_cast<const uint2*>(gp + e);
+                float4 dv = *reinterpret_cast<const float4*>(dp + e);
+                float x[4] = {bf2f(gv.x & 0xffff) + dv.x, bf2f(gv.x >> 16) + dv.y,
+                              bf2f(gv.y & 0xffff) + dv.z, bf2f(gv.y >> 16) + dv.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    la[e + u] = fmaxf(a.lower_bound, -rate * softplus_f(x[u])) * LOG2E;
+            }
+            b = sigmoid_f(bf2f(a.beta[row]));
+        }
+    } else {
+        // padding rows: beta = 0 and log decay = 0 leave the state unchanged
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) { q[e] = 0.f; k[e] = 0.f; la[e] = 0.f; }
+    }
+
+    // L2 norms: the 16 lanes of a row are consecutive lanes of one wave.
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) { sq += q[e] * q[e]; sk += k[e] * k[e]; }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        sq += __shfl_xor(sq, m, 64);
+        sk += __shfl_xor(sk, m, 64);
+    }
+    const float iq = rsq_hw(sq + NORM_EPS), ik = rsq_hw(sk + NORM_EPS);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) { q[e] *= iq; k[e] *= ik; sm.la[r][c0 + e] = la[e]; }
+    if (cg == 0) sm.beta[r] = b;
+    __syncthreads();
+
+    // ---- phase 2: in-chunk inclusive prefix sum of the log2 decay, per channel
+    if (tid < K) {
+        float acc = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < C; ++rr) { acc += sm.la[rr][tid]; sm.la[rr][tid] = acc; }
+    }
+    __syncthreads();
+
+    // ---- phase 3: decay factors and the K-side record pieces
+    {
+        float kd[EPT], kgv[EPT], qgv[EPT];
+        if constexpr (GDN) {
+            // scalar decay: every factor is exp2 of a non-positive difference
+            const float G = sm.la[r][0], GC = sm.la[C - 1][0];
+            const float gam = exp2_hw(G), gamd = exp2_hw(GC - G), gamc = exp2_hw(GC);
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                sm.kg[r][c0 + e] = (bf16)k[e];   // intra-chunk products use k^ and q^,
+                sm.kig[r][c0 + e] = (bf16)k[e];  // the decay is applied per element
+                sm.qg[r][c0 + e] = (bf16)q[e];
+                kgv[e] = k[e] * gam;
+                qgv[e] = q[e] * gam;
+                kd[e] = k[e] * gamd;
+                if (r == C - 1) reinterpret_cast<float*>(sm.rec + R::GAMC)[c0 + e] = gamc;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                const float G = sm.la[r][c0 + e];
+                const float GC = sm.la[C - 1][c0 + e];
+                const float gam = exp2_hw(G), gami = exp2_hw(-G), gamc = exp2_hw(GC);
+                kgv[e] = k[e] * gam;
+                qgv[e] = q[e] * gam;
+                sm.kg[r][c0 + e] = (bf16)kgv[e];
+                sm.kig[r][c0 + e] = (bf16)(k[e] * gami);
+                sm.qg[r][c0 + e] = (bf16)qgv[e];
+                kd[e] = k[e] * gamc * gami;
+                if (r == C - 1) reinterpret_cast<float*>(sm.rec + R::GAMC)[c0 + e] = gamc;
+            }
+        }
+        // nKG and QG in 16x16x32 fragment order: 4 consecutive channels
+        // c..c+3 (c % 4 == 0) land on 4 consecutive elements of one lane.
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+            const int c = c0 + e, j = c >> 5, w = c & 31;
+            const int gg = (w & 15) >> 2, ee = (w >> 4) << 2;
+            const int off = (((j * 4 + gg) * 16 + r) * 8 + ee) * 2;
+            bf16x4 nkg, qv;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                nkg[u] = (bf16)(-kgv[e + u]);
+                qv[u] = (bf16)qgv[e + u];
+            }
+            *reinterpret_cast<bf16x4*>(sm.rec + R::NKG + off) = nkg;
+            *reinterpret_cast<bf16x4*>(sm.rec + R::QG + off) = qv;
+        }
+        // KdT[b][g][m][i] = Kd[token 4g + i][channel 16b + m]
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int c = c0 + e;
+            const int off = ((((c >> 4) * 4 + (r >> 2)) * 16 + (c & 15)) * 4 + (r & 3)) * 2;
+            *reinterpret_cast<bf16*>(sm.rec + R::KDT + off) = (bf16)kd[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 4: A = diag(beta) strict_tril(KG KiG^T), Aqk = tril(QG KiG^T)
+    // (GDN: the same products of k^ and q^, times exp2(G_r - G_j) per element)
+    const int wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    if (wave < 2) {
+        const bf16 (*lhs)[PrepSmem<K>::LDK] = wave == 0 ? sm.kg : sm.qg;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < K / 32; ++j) {
+            bf16x8 av = *reinterpret_cast<const bf16x8*>(&lhs[lr][32 * j + 8 * lg]);
+            bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.kig[lr][32 * j + 8 * lg]);
+            acc = mfma32(av, bv, acc);
+        }
+        // lane holds M[4 lg + i][lr]: row rr = 4 lg + i, column jj = lr
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 4 * lg + i, jj = lr;
+            float m = acc[i];
+            if constexpr (GDN) {
+                if (jj <= rr) m *= exp2_hw(sm.la[rr][0] - sm.la[jj][0]);
+            }
+            if (wave == 0) {
+                // keep j < r; N = -A
+                sm.nmat[rr][jj] = jj < rr ? -sm.beta[rr] * m : 0.f;
+            } else {
+                const float v = jj <= rr ? m : 0.f;
+                const int off = (((jj >> 2) * 16 + rr) * 4 + (jj & 3)) * 2;
+                *reinterpret_cast<bf16*>(sm.rec + R::AQK + off) = (bf16)v;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 5: T = (I + N)(I + N^2)(I + N^4)(I + N^8), one element per thread
+    {
+        const int rr = tid >> 4, cc = tid & 15;
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < C; ++m) s += sm.nmat[rr][m] * sm.nmat[m][cc];
+        sm.n2[rr][cc] = s;
+        __syncthreads();
+        float s4 = 0.f, s3 = 0.f;
+#pragma unroll
+        for (int m = 0; m < C; ++m) {
+            s4 += sm.n2[rr][m] * sm.n2[m][cc];
+            s3 += sm.nmat[rr][m] * sm.n2[m][cc];
+        }
+        sm.n4[rr][cc] = s4;
+        // P1 = (I + N)(I + N^2) = I + N + N^2 + N^3
+        sm.p1[rr][cc] = (rr == cc ? 1.f : 0.f) + sm.nmat[rr][cc] + sm.n2[rr][cc] + s3;
+        __syncthreads();
+        float s8 = 0.f, t2 = 0.f;
+#pragma unroll
+        for (int m = 0; m < C; ++m) {
+            s8 += sm.n4[rr][m] * sm.n4[m][cc];
+            t2 += sm.p1[rr][m] * sm.n4[m][cc];
+        }
+        sm.n8[rr][cc] = s8;
+        sm.p2[rr][cc] = sm.p1[rr][cc] + t2;  // P2 = P1 (I + N^4)
+        __syncthreads();
+        float t3 = 0.f;
+#pragma unroll
+        for (int m = 0; m < C; ++m) t3 += sm.p2[rr][m] * sm.n8[m][cc];
+        const float T = sm.p2[rr][cc] + t3;  // P2 (I + N^8)
+        // Tb = T diag(beta), stored as Tb[g][m][i] = Tb[m][4g + i]
+        const int off = (((cc >> 2) * 16 + rr) * 4 + (cc & 3)) * 2;
+        *reinterpret_cast<bf16*>(sm.rec + R::TB + off) = (bf16)(T * sm.beta[cc]);
+    }
+    __syncthreads();
+
+    // ---- phase 6: stream the record out, 16 bytes per thread per step
+    uint4* dst = reinterpret_cast<uint4*>(a.rec + ((int64_t)slot * a.H + h) * R::BYTES);
+    const uint4* src = reinterpret_cast<const uint4*>(sm.rec);
+    for (int i = tid; i < R::BYTES / 16; i += 256) dst[i] = src[i];
+}
+
+// Sequence table: seq_start[0..N] (flattened token offsets) and
+// chunk_off[0..N] (prefix sums of ceil(len / C)).  The sequence ends are
+// clamped into [0, total_tokens] and made non-decreasing by a running
+// maximum, so a malformed cu_seqlens can never send a later access out of
+// bounds: lengths stay >= 0, they sum to at most total_tokens, and the chunk
+// count stays within ceil(total_tokens / C) + N.
+__device__ __forceinline__ int32_t block_scan(int32_t v, int32_t* buf, bool use_max) {
+    const int tid = threadIdx.x;
+    buf[tid] = v;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        const int32_t o = tid >= d ? buf[tid - d] : (use_max ? INT32_MIN : 0);
+        __syncthreads();
+        buf[tid] = use_max ? max(buf[tid], o) : buf[tid] + o;
+        __syncthreads();
+    }
+    return buf[tid];
+}
+
+__global__ __launch_bounds__(256) void kda_seq_table_kernel(const int32_t* cu, int32_t n_seqs,
+                                                            int32_t T, int64_t total_tokens,
+                                                            int32_t* seq_start,
+                                                            int32_t* chunk_off) {
+    __shared__ int32_t buf[256];
+    __shared__ int32_t ends[256];
+    const int tid = threadIdx.x;
+    int32_t prev_end = 0, carry = 0;  // identical in every thread
+    if (tid == 0) {
+        seq_start[0] = 0;
+        chunk_off[0] = 0;
+    }
+    for (int base = 0; base < n_seqs; base += 256) {
+        const int i = base + tid;  // sequence i spans [end_{i-1}, end_i)
+        int64_t e = prev_end;
+        if (i < n_seqs) e = cu ? (int64_t)cu[i + 1] : (int64_t)(i + 1) * T;
+        e = min(max(e, (int64_t)prev_end), total_tokens);
+        const int32_t end = block_scan((int32_t)e, buf, true);
+        ends[tid] = end;
+        __syncthreads();
+        const int32_t begin = tid == 0 ? prev_end : ends[tid - 1];
+        const int32_t chunks = (end - begin + C - 1) / C;
+        const int32_t off = block_scan(chunks, buf, false);
+        if (i < n_seqs) {
+            seq_start[i + 1] = end;
+            chunk_off[i + 1] = carry + off;
+        }
+        carry += buf[255];
+        prev_end = ends[255];
+        __syncthreads();
+    }
+}
+
+void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t total_tokens,
+                      int32_t* seq_start, int32_t* chunk_off, hipStream_t stream) {
+    hipLaunchKernelGGL(kda_seq_table_kernel, dim3(1), dim3(256), 0, stream, cu, n_seqs, T,
+                       total_tokens, seq_start, chunk_off);
+}
+
+template <int K, bool GDN>
+void launch_prep_t(const PrepArgs& a, int n_slots, hipStream_t stream) {
+    hipLaunchKernelGGL((kda_prep_kernel<K, GDN>), dim3(n_slots, a.H), dim3(256), 0, stream, a);
+}
+
+void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream) {
+    if (K == 128) {
+        if (gdn) launch_prep_t<128, true>(a, n_slots, stream);
+        else launch_prep_t<128, false>(a, n_slots, stream);
+    } else {
+        if (gdn) launch_prep_t<64, true>(a, n_slots, stream);
+        else launch_prep_t<64, false>(a, n_slots, stream);
+    }
+}
+
+int record_bytes(int K) { return K == 128 ? Rec<128>::BYTES : Rec<64>::BYTES; }
+
+}  // namespace kda

@@ -1,0 +1,119 @@
+/*
+ * kda.h -- C ABI of libkda: the chunkwise forward pass of gated delta-rule
+ * linear attention on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations:
+ *   kda_fwd  Kimi Delta Attention: per-channel decay computed from a
+ *            pre-activation gate, beta given as logits.
+ *   gdn_fwd  Gated DeltaNet: one scalar log decay per (token, head), beta
+ *            given as probabilities.
+ *
+ * Both compute, for every sequence and head, with the state S in [K, V] layout:
+ *   q^_t = q_t / sqrt(|q_t|^2 + 1e-6),  k^_t likewise
+ *   S_t  = (I - beta_t k^_t k^_t^T) Diag(alpha_t) S_{t-1} + beta_t k^_t v_t^T
+ *   o_t  = scale * S_t^T q^_t
+ * KDA: log alpha_t[c] = max(lower_bound, -exp(A_log[h]) * softplus(g_t[c] + dt_bias[h, c]))
+ *      beta_t = sigmoid(beta_t logit)
+ * GDN: log alpha_t[c] = g_t (the same for every channel), beta_t as given.
+ *
+ * Sources: the KDA parameter table of the FlashKDA summary on
+ * discuss.pytorch.kr (section "FlashKDA의 KDA 연산 구조": q, k, v, g, beta
+ * logits with the sigmoid inside, A_log, dt_bias [H, K], lower_bound in
+ * [-5, 0], optional initial/final state, fused q/k L2 norm and gate); the
+ * cuLA README's KDA example (section "KDA (Kimi Delta Attention) --
+ * Blackwell (SM10X)": fp32 [B, H, K, V] states, int32 cu_seqlens); the
+ * QwenLM/FlashQLA summary (section "간단한 사용 예시": the GDN call with g,
+ * beta, scale, initial_state and cu_seqlens).  The pages name the operations
+ * but print no equation; the formulas above are the reading this library
+ * implements.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major arrays.
+ *    bf16 tensors are passed as uint16_t bit patterns.
+ *  - Shapes: q, k [B, T, H, K]; v, o [B, T, H, V]; KDA g [B, T, H, K] bf16;
+ *    GDN g [B, T, H] fp32; beta [B, T, H] bf16; A_log [H] fp32; dt_bias
+ *    [H, K] fp32 (the same memory as a flat [H * K]); states [N, H, K, V]
+ *    fp32, where N = B for fixed-length batches and N = num_seqs when
+ *    cu_seqlens is given.
+ *  - Variable length: cu_seqlens (device, int32, num_seqs + 1 entries) packs
+ *    the sequences along T of a B = 1 batch: sequence i is tokens
+ *    [cu_seqlens[i], cu_seqlens[i+1]).  Expected: cu_seqlens[0] = 0,
+ *    non-decreasing, cu_seqlens[num_seqs] = T.  This is not checked (the
+ *    library never reads device memory on the host); the kernels clamp the
+ *    offsets into a non-decreasing sequence within [0, T], so a malformed
+ *    array gives unspecified results but no out-of-bounds access.  The
+ *    state restarts at every sequence boundary.
+ *  - initial_state may be NULL (zero state); final_state may be NULL (not
+ *    written).  An empty sequence returns its initial state.
+ *  - Only K, V in {64, 128} are supported.  B * T must be < 2^31.  Token
+ *    tensors (q, k, v, g, beta, o) may be NULL only when T == 0.
+ *  - Alignment: q, k, g (KDA), o at least 8 bytes; dt_bias 16 bytes;
+ *    workspace 256 bytes.
+ *  - Ownership: the caller allocates and frees every buffer, including the
+ *    workspace (at least *_workspace_size() bytes).  The library allocates
+ *    nothing, keeps no pointer after it returns and never synchronises.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream); results are valid once the stream reaches that point.  Outputs
+ *    must not alias inputs; concurrent calls must use distinct workspaces.
+ *  - Errors: every argument check runs on the host before any HIP call and a
+ *    failed check returns a KDA_ERR_* code with nothing enqueued.  A failed
+ *    launch returns KDA_ERR_LAUNCH.  No C++ exception crosses this ABI.
+ */
+#ifndef LIBKDA_KDA_H
+#define LIBKDA_KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, lower_bound, alignment */
+    KDA_ERR_UNSUPPORTED = 2, /* K or V outside {64, 128} */
+    KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    KDA_ERR_LAUNCH = 4       /* a kernel launch failed */
+};
+
+/* Bytes of device workspace that kda_fwd needs.  num_seqs: the number of
+ * packed sequences when cu_seqlens will be passed, else B.  Pure host
+ * function; returns 0 for invalid sizes. */
+size_t kda_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                              int32_t num_seqs);
+
+/* KDA forward.  beta holds logits (sigmoid applied inside); lower_bound must
+ * be finite and in [-5, 0]; scale must be finite (K^-0.5 is customary).
+ * num_seqs is read only when cu_seqlens is non-NULL (then B must be 1). */
+int kda_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+            const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
+            float scale, const float* initial_state, float* final_state,
+            const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+            int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/* Bytes of device workspace that gdn_fwd needs (same arguments). */
+size_t gdn_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                              int32_t num_seqs);
+
+/* GDN forward.  g is the fp32 log decay [B, T, H] and must be <= 0 (any
+ * magnitude: the scalar gate forms its in-chunk decays as exp(G_r - G_j) <= 1);
+ * beta holds probabilities in [0, 1], used as given. */
+int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+            const uint16_t* beta, float scale, const float* initial_state, float* final_state,
+            const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+            int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* kda_status_str(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKDA_KDA_H */

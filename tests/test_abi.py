@@ -1,0 +1,90 @@
+"""The C ABI on the host: the library loads without a GPU, exports every symbol
+include/kda.h declares, and rejects bad arguments on the host before any HIP
+call (so these calls are safe with fake pointers and no device)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import chunked_gated_delta_kda_amd as kda
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "kda.h"
+FAKE = ctypes.c_void_p(0x1000)  # 256-aligned, never dereferenced on these paths
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"libkda.so does not export {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert kda.version() == 100
+    for code in range(5):
+        assert kda.status_str(code)
+    assert kda.status_str(99) == "unknown status"
+
+
+def test_workspace_size_formula(lib):
+    rec = 3 * 16 * 128 * 2 + 2 * 16 * 16 * 2 + 128 * 4  # bytes per (chunk, head) at K=128
+    B, T, H, N = 2, 2048, 32, 2
+    meta = 256
+    want = meta + ((B * T + 15) // 16 + N) * H * rec
+    assert kda.workspace_size(B, T, H, 128, 128) == want
+    assert kda.workspace_size(1, 100, 1, 96, 128) == 0  # unsupported K
+    assert kda.workspace_size(0, 100, 1, 128, 128) == 0
+
+
+def _kda_call(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0,
+             scale=0.088, h0=None, hT=None, cu=None, N=0, B=1, T=16, H=1, K=128, V=128, o=FAKE,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return lib.kda_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"], a["dt_bias"],
+                       a["lb"], a["scale"], a["h0"], a["hT"], a["cu"], a["N"], a["B"], a["T"],
+                       a["H"], a["K"], a["V"], a["o"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(g=None), 1),
+    (dict(beta=None), 1), (dict(o=None), 1), (dict(A_log=None), 1), (dict(dt_bias=None), 1),
+    (dict(B=0), 1), (dict(T=-1), 1), (dict(H=0), 1),
+    (dict(lb=-5.5), 1), (dict(lb=0.5), 1), (dict(lb=float("nan")), 1),
+    (dict(scale=float("inf")), 1),
+    (dict(K=96), 2), (dict(V=256), 2),
+    (dict(cu=FAKE, B=2, N=2), 1), (dict(cu=FAKE, N=0), 1),
+    (dict(ws=None), 3), (dict(wsb=100), 3), (dict(ws=ctypes.c_void_p(0x1010)), 3),
+    (dict(q=ctypes.c_void_p(0x1002)), 1), (dict(dt_bias=ctypes.c_void_p(0x1008)), 1),
+    (dict(B=1 << 16, T=1 << 15), 1),
+])
+def test_kda_rejects_on_host(lib, over, code):
+    assert _kda_call(lib, **over) == code
+
+
+def test_gdn_rejects_on_host(lib):
+    args = [FAKE, FAKE, FAKE, None, FAKE, 0.1, None, None, None, 0, 1, 16, 1, 128, 128, FAKE,
+            FAKE, 1 << 30, None]
+    assert lib.gdn_fwd(*args) == 1  # null g
+    args[3] = FAKE
+    args[13] = 32
+    assert lib.gdn_fwd(*args) == 2  # unsupported K
+    args[13] = 128
+    args[17] = 10
+    assert lib.gdn_fwd(*args) == 3  # workspace too small
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        kda.load(tmp_path / "nope.so")

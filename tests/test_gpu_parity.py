@@ -1,0 +1,216 @@
+"""GPU parity: libkda (through its C ABI) against the fp64 oracle on seeded
+inputs, element by element, within the acceptance bounds of parity_util."""
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_kda_amd as kda
+from chunked_gated_delta_kda_amd import inputs
+from parity_util import (ABS_TOL, assert_close, check_parity, gpu_run, oracle_run, say,
+                         to64)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ small cases
+def test_config0_tiny():
+    check_parity(inputs.config(0))
+
+
+# odd lengths and head counts in the style of the pages' own test list
+ODD = [(1, 63, 1), (2, 500, 3), (2, 1000, 3), (3, 1024, 4)]
+
+
+@pytest.mark.parametrize("B,T,H", ODD, ids=lambda x: str(x))
+def test_odd_shapes(B, T, H):
+    w = inputs.kda_workload(B, T, H, 128, 128, seed=2000 + T + H, init_std=0.05,
+                            name=f"odd_B{B}_T{T}_H{H}")
+    check_parity(w)
+
+
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_head_dims_slow_decay(K, V):
+    # dt_bias = -6: softplus ~ 2.5e-3, decay ~ 0.9975 per token, so the initial
+    # state and every earlier chunk still matter at the end of the sequence
+    w = inputs.kda_workload(2, 300, 3, K, V, seed=3000 + K + V, dt_bias_value=-6.0,
+                            init_std=0.05, name=f"slow_K{K}_V{V}")
+    check_parity(w, first_tokens=32)
+
+
+def test_clamp_active():
+    # g ~ N(8, 1): softplus ~ 8 so the floor -5 binds on almost every channel and
+    # the in-chunk cumulative log decay reaches -80
+    w = inputs.kda_workload(2, 256, 4, 128, 128, seed=3100, g_mean=8.0, g_std=1.0,
+                            init_std=0.05, name="clamp_active")
+    check_parity(w, first_tokens=32)
+
+
+def test_lower_bound_other_than_default():
+    w = inputs.kda_workload(1, 200, 2, 128, 128, seed=3150, g_mean=4.0, g_std=1.0,
+                            lower_bound=-1.5, init_std=0.05, name="lower_bound_-1.5")
+    check_parity(w)
+
+
+@pytest.mark.parametrize("lengths", [[1, 15, 16, 17, 0, 100, 33],
+                                     [5],
+                                     [0, 0, 40],
+                                     [31, 1, 2, 250, 16, 64]])
+def test_varlen_slow_decay(lengths):
+    w = inputs.kda_workload(1, 0, 3, 128, 128, seed=3200 + sum(lengths), dt_bias_value=-6.0,
+                            init_std=0.05, lengths=lengths, name=f"varlen_{lengths}")
+    check_parity(w, first_tokens=32)
+
+
+def test_varlen_resets_state():
+    """Packed sequences equal separate runs of each sequence (GPU vs GPU, and each
+    against the oracle): the state restarts exactly at every boundary."""
+    lengths = [37, 80, 16, 51]
+    w = inputs.kda_workload(1, 0, 2, 128, 128, seed=3300, dt_bias_value=-6.0, init_std=0.05,
+                            lengths=lengths)
+    o, S = gpu_run(w)
+    cu = w.cu_seqlens.tolist()
+    for n in range(len(lengths)):
+        sl = slice(cu[n], cu[n + 1])
+        single = inputs.Workload("kda", f"seq{n}", w.q[:, sl].contiguous(),
+                                 w.k[:, sl].contiguous(), w.v[:, sl].contiguous(),
+                                 w.g[:, sl].contiguous(), w.beta[:, sl].contiguous(), w.A_log,
+                                 w.dt_bias, w.lower_bound, w.scale,
+                                 w.initial_state[n:n + 1].contiguous())
+        o1, S1 = gpu_run(single)
+        assert torch.equal(o[:, sl], o1), f"sequence {n}: packed output differs"
+        assert torch.equal(S[n:n + 1], S1), f"sequence {n}: packed state differs"
+
+
+def test_gdn_small():
+    w = inputs.gdn_workload(2, 300, 4, 128, 128, seed=3400, init_std=0.05)
+    check_parity(w, first_tokens=32)
+
+
+def test_gdn_slow_decay_varlen():
+    w = inputs.gdn_workload(1, 0, 3, 128, 128, seed=3500, init_std=0.05, decay_shift=-6.0,
+                            lengths=[100, 1, 0, 64, 77])
+    check_parity(w, first_tokens=32)
+
+
+def test_gdn_strong_decay_any_magnitude():
+    # log decay far below -5 per token: the scalar-gate path forms exp(G_r - G_j) <= 1
+    # directly, so no factor can overflow
+    w = inputs.gdn_workload(1, 128, 2, 64, 64, seed=3600, init_std=0.05)
+    w.g = torch.full_like(w.g, -30.0)
+    check_parity(w)
+
+
+def test_initial_state_none_equals_zeros():
+    w = inputs.kda_workload(1, 100, 2, 128, 128, seed=3700)
+    o1, S1 = gpu_run(w)
+    w.initial_state = torch.zeros(1, 2, 128, 128)
+    o2, S2 = gpu_run(w)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_state_continuation():
+    """run(0:T) equals run(T1:T) started from run(0:T1)'s final state, at a chunk
+    boundary and inside a chunk, within the acceptance bounds."""
+    w = inputs.kda_workload(1, 200, 2, 128, 128, seed=3800, dt_bias_value=-6.0, init_std=0.05)
+    o, S = gpu_run(w)
+    for T1 in (96, 101):
+        a = inputs.Workload("kda", "first", w.q[:, :T1].contiguous(), w.k[:, :T1].contiguous(),
+                            w.v[:, :T1].contiguous(), w.g[:, :T1].contiguous(),
+                            w.beta[:, :T1].contiguous(), w.A_log, w.dt_bias, w.lower_bound,
+                            w.scale, w.initial_state)
+        o1, S1 = gpu_run(a)
+        b = inputs.Workload("kda", "second", w.q[:, T1:].contiguous(), w.k[:, T1:].contiguous(),
+                            w.v[:, T1:].contiguous(), w.g[:, T1:].contiguous(),
+                            w.beta[:, T1:].contiguous(), w.A_log, w.dt_bias, w.lower_bound,
+                            w.scale, S1.cpu())
+        o2, S2 = gpu_run(b)
+        assert_close(f"continuation@{T1} o", to64(torch.cat([o1, o2], 1)), to64(o))
+        assert_close(f"continuation@{T1} state", to64(S2), to64(S))
+
+
+def test_deterministic_and_fully_written():
+    """Two runs are bitwise identical, including when the output, state and
+    workspace buffers start out filled with NaN (no element is left unwritten)."""
+    w = inputs.kda_workload(2, 250, 3, 128, 128, seed=3900, init_std=0.05)
+    o1, S1 = gpu_run(w)
+    nan_o = torch.full_like(o1, float("nan"))
+    nan_S = torch.full_like(S1, float("nan"))
+    ws = torch.full((kda.workspace_size(2, 250, 3, 128, 128),), 0xFF, dtype=torch.uint8,
+                    device=o1.device)
+    o2, S2 = gpu_run(w, workspace=ws, out=nan_o, final_out=nan_S)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_empty_sequence_length_zero():
+    w = inputs.kda_workload(2, 0, 2, 64, 64, seed=4000, init_std=0.05)
+    o, S = gpu_run(w)
+    assert o.numel() == 0
+    assert torch.equal(S.cpu(), w.initial_state)
+
+
+def test_page_shapes():
+    """The pages' usage example: B, T, H, K, V = 2, 2048, 32, 128, 128 gives o
+    [2, 2048, 32, 128] and a [2, 32, 128, 128] fp32 final state."""
+    import oracle_pins
+
+    gold = oracle_pins.load_golden("page_shapes.json")
+    w = inputs.kda_workload(gold["B"], gold["T"], gold["H"], gold["K"], gold["V"], seed=4100)
+    o, S = gpu_run(w)
+    assert list(o.shape) == gold["o_shape"] and list(S.shape) == gold["final_state_shape"]
+    assert S.dtype == torch.float32
+
+
+def test_hand_worked_examples():
+    """The hand-worked K = V = 2 examples need K >= 64 on the GPU; embedding them in
+    the first two channels (the rest zero) leaves the recurrence unchanged."""
+    import oracle_pins
+
+    for c in oracle_pins.load_golden("hand_worked.json")["cases"]:
+        a = c["inputs"]
+        say(f"[hand-worked] {c['name']}")
+
+        def pad(x, axis_len=64):
+            x = np.asarray(x, dtype=np.float64)
+            out = np.zeros(x.shape[:-1] + (axis_len,))
+            out[..., :x.shape[-1]] = x
+            return out
+
+        q, k, v = pad(a["q"]), pad(a["k"]), pad(a["v"])
+        beta = np.asarray(a["beta"], dtype=np.float64)
+        S0 = a.get("initial_state")
+        h0 = None
+        if S0 is not None:
+            h0 = np.zeros((1, 1, 64, 64))
+            h0[..., :2, :2] = np.asarray(S0)
+        bf = lambda x: torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)
+        if c["kind"] == "kda":
+            g = pad(a["g"])
+            dt = pad(a["dt_bias"])
+            w = inputs.Workload("kda", c["name"], bf(q), bf(k), bf(v), bf(g), bf(beta),
+                                torch.tensor(a["A_log"], dtype=torch.float32),
+                                torch.tensor(dt, dtype=torch.float32), a["lower_bound"],
+                                a["scale"], None if h0 is None else torch.tensor(
+                                    h0, dtype=torch.float32))
+        else:
+            w = inputs.Workload("gdn", c["name"], bf(q), bf(k), bf(v),
+                                torch.tensor(a["g"], dtype=torch.float32), bf(beta), None, None,
+                                -5.0, a["scale"], None if h0 is None else torch.tensor(
+                                    h0, dtype=torch.float32))
+        o, S = gpu_run(w)
+        want_o = np.asarray(c["expected"]["o"])
+        want_S = np.asarray(c["expected"]["final_state"])
+        assert_close("o", to64(o)[..., :2], want_o)
+        assert_close("final_state", to64(S)[..., :2, :2], want_S)
+
+
+# ------------------------------------------------------------------ full sizes
+# The benchmark workloads at their full sizes, in the launch configuration the
+# benchmark times; the oracle computes a sample of heads (every head is an
+# independent recurrence, so sampled heads are exact references).
+FULL = [(1, [0, 13, 31]), (2, [5]), (3, [0, 11]), (4, [7])]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg,heads", FULL, ids=lambda x: str(x))
+def test_full_config(cfg, heads):
+    check_parity(inputs.config(cfg), heads=heads)
