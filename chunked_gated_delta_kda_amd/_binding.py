@@ -18,7 +18,7 @@ _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED"
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_fwd", "gdn_fwd", "kda_fwd_workspace_size", "gdn_fwd_workspace_size",
-           "kda_status_str", "kda_version")
+           "kda_prep", "gdn_prep", "kda_recur", "kda_status_str", "kda_version")
 
 
 class LibKdaError(RuntimeError):
@@ -48,6 +48,15 @@ def load(path: Path | str | None = None):
     lib.gdn_fwd.restype = ctypes.c_int
     lib.gdn_fwd.argtypes = [u16p, u16p, u16p, f32p, u16p, f32, f32p, f32p, i32p, i32, i32, i32,
                             i32, i32, i32, u16p, vp, sz, vp]
+    lib.kda_prep.restype = ctypes.c_int
+    lib.kda_prep.argtypes = [u16p, u16p, u16p, u16p, f32p, f32p, f32, i32p, i32, i32, i32, i32,
+                             i32, i32, vp, sz, vp]
+    lib.gdn_prep.restype = ctypes.c_int
+    lib.gdn_prep.argtypes = [u16p, u16p, f32p, u16p, i32p, i32, i32, i32, i32, i32, i32, vp, sz,
+                             vp]
+    lib.kda_recur.restype = ctypes.c_int
+    lib.kda_recur.argtypes = [u16p, f32, f32p, f32p, i32, i32, i32, i32, i32, i32, i32, u16p, vp,
+                              sz, vp]
     for name in ("kda_fwd_workspace_size", "gdn_fwd_workspace_size"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_size_t
@@ -194,3 +203,42 @@ def gdn_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state
     if st != 0:
         raise LibKdaError(st, status_str(st))
     return a["o"], a["final"]
+
+
+def _check(st):
+    if st != 0:
+        raise LibKdaError(st, status_str(st))
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def kda_prep(q, k, g, beta, A_log, dt_bias, lower_bound, workspace, cu_seqlens=None, V=None):
+    """Token-parallel stage only: fills ``workspace`` (see kda_recur)."""
+    B, T, H, K = q.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    stream = ctypes.c_void_p(_torch().cuda.current_stream(q.device).cuda_stream)
+    _check(load().kda_prep(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
+                           float(lower_bound), _ptr(cu_seqlens), N, B, T, H, K, V or K,
+                           _ptr(workspace), _nbytes(workspace), stream))
+
+
+def gdn_prep(q, k, g, beta, workspace, cu_seqlens=None, V=None):
+    B, T, H, K = q.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    stream = ctypes.c_void_p(_torch().cuda.current_stream(q.device).cuda_stream)
+    _check(load().gdn_prep(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, B, T, H,
+                           K, V or K, _ptr(workspace), _nbytes(workspace), stream))
+
+
+def kda_recur(v, K, scale, workspace, out, initial_state=None, final_out=None, num_seqs=None):
+    """Head-parallel stage only: reads the workspace of the preceding prep call
+    (same sizes and packing; ``num_seqs`` set for packed sequences)."""
+    B, T, H, V = v.shape
+    varlen = num_seqs is not None
+    N = num_seqs if varlen else B
+    stream = ctypes.c_void_p(_torch().cuda.current_stream(v.device).cuda_stream)
+    _check(load().kda_recur(_ptr(v), float(scale), _ptr(initial_state), _ptr(final_out),
+                            1 if varlen else 0, N, B, T, H, K, V, _ptr(out), _ptr(workspace),
+                            _nbytes(workspace), stream))

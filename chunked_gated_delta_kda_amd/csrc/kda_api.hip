@@ -35,7 +35,8 @@ struct Common {
     const uint16_t *q, *k, *v, *beta;
     const float* initial_state;
     float* final_state;
-    const int32_t* cu;
+    const int32_t* cu;  // read on the device by the prep stage only
+    bool varlen;        // sequences packed along T (B == 1, N = num_seqs)
     int32_t num_seqs, B, T, H, K, V;
     uint16_t* o;
     void* ws;
@@ -52,7 +53,7 @@ int check_common(const Common& c, int32_t& N) {
     if (!supported_dim(c.K) || !supported_dim(c.V)) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)c.B * c.T >= ((int64_t)1 << 31)) return KDA_ERR_INVALID_ARG;
     if (!std::isfinite(c.scale)) return KDA_ERR_INVALID_ARG;
-    if (c.cu) {
+    if (c.varlen) {
         if (c.B != 1 || c.num_seqs < 1) return KDA_ERR_INVALID_ARG;
         N = c.num_seqs;
     } else {
@@ -60,35 +61,57 @@ int check_common(const Common& c, int32_t& N) {
     }
     if (!aligned(c.q, 8) || !aligned(c.k, 8) || !aligned(c.o, 8)) return KDA_ERR_INVALID_ARG;
     if (!c.ws || !aligned(c.ws, ALIGN)) return KDA_ERR_WORKSPACE;
-    if (c.ws_bytes < workspace_bytes_for(c.B, c.T, c.H, c.K, N, c.cu != nullptr))
+    if (c.ws_bytes < workspace_bytes_for(c.B, c.T, c.H, c.K, N, c.varlen))
         return KDA_ERR_WORKSPACE;
     return KDA_OK;
 }
 
-int run(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t stream) {
-    const bool varlen = c.cu != nullptr;
-    int32_t* seq_start = static_cast<int32_t*>(c.ws);
-    int32_t* chunk_off = seq_start + (N + 1);
-    unsigned char* rec = static_cast<unsigned char*>(c.ws) + meta_bytes(N);
-    const int64_t slots = max_slots(c.B, c.T, N, varlen);
-    if (slots > INT32_MAX || (int64_t)N * c.H * 2 > INT32_MAX) return KDA_ERR_INVALID_ARG;
+struct WsLayout {
+    int32_t* seq_start;
+    int32_t* chunk_off;
+    unsigned char* rec;
+    int64_t slots;
+};
 
+WsLayout layout(const Common& c, int32_t N) {
+    WsLayout w;
+    w.seq_start = static_cast<int32_t*>(c.ws);
+    w.chunk_off = w.seq_start + (N + 1);
+    w.rec = static_cast<unsigned char*>(c.ws) + meta_bytes(N);
+    w.slots = max_slots(c.B, c.T, N, c.varlen);
+    return w;
+}
+
+// Sequence table and kda_prep: fills the workspace.
+int run_prep(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t stream) {
+    const WsLayout w = layout(c, N);
+    if (w.slots > INT32_MAX || (int64_t)N * c.H * 2 > INT32_MAX) return KDA_ERR_INVALID_ARG;
     (void)hipGetLastError();  // clear a stale error from unrelated work
-    kda::launch_seq_table(c.cu, N, c.T, (int64_t)c.B * c.T, seq_start, chunk_off, stream);
-
+    if (c.varlen)
+        kda::launch_seq_table(c.cu, N, c.T, (int64_t)c.B * c.T, w.seq_start, w.chunk_off,
+                              stream);
     p.q = c.q;
     p.k = c.k;
     p.beta = c.beta;
     p.H = c.H;
     p.n_seqs = N;
-    p.seq_start = seq_start;
-    p.chunk_off = chunk_off;
-    p.rec = rec;
-    if (slots > 0) kda::launch_prep(p, c.K, gdn, (int)slots, stream);
+    p.packed = c.varlen;
+    p.T = c.T;
+    p.seq_start = w.seq_start;
+    p.chunk_off = w.chunk_off;
+    p.rec = w.rec;
+    if (w.slots > 0) kda::launch_prep(p, c.K, gdn, (int)w.slots, stream);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
 
+// kda_recur: consumes the workspace.
+int run_recur(const Common& c, int32_t N, hipStream_t stream) {
+    const WsLayout w = layout(c, N);
+    if ((int64_t)N * c.H * 2 > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
     kda::RecurArgs r;
     r.v = c.v;
-    r.rec = rec;
+    r.rec = w.rec;
     r.initial_state = c.initial_state;
     r.final_state = c.final_state;
     r.o = c.o;
@@ -96,11 +119,27 @@ int run(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t strea
     r.H = c.H;
     r.V = c.V;
     r.n_seqs = N;
-    r.seq_start = seq_start;
-    r.chunk_off = chunk_off;
+    r.packed = c.varlen;
+    r.T = c.T;
+    r.seq_start = w.seq_start;
+    r.chunk_off = w.chunk_off;
     kda::launch_recur(r, c.K, stream);
-
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int run(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t stream) {
+    int st = run_prep(c, N, p, gdn, stream);
+    return st != KDA_OK ? st : run_recur(c, N, stream);
+}
+
+// Checks of the KDA gate arguments.
+int check_kda_gate(int32_t T, const uint16_t* g, const float* A_log, const float* dt_bias,
+                   float lower_bound) {
+    if ((T > 0 && !g) || !A_log || !dt_bias) return KDA_ERR_INVALID_ARG;
+    if (!aligned(g, 8) || !aligned(dt_bias, 16)) return KDA_ERR_INVALID_ARG;
+    if (!std::isfinite(lower_bound) || lower_bound < -5.f || lower_bound > 0.f)
+        return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
 }
 
 }  // namespace
@@ -126,14 +165,12 @@ int kda_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
             int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
             void* stream) {
-    Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, num_seqs, B, T, H, K, V,
-             o, workspace, workspace_bytes, scale};
-    if ((T > 0 && !g) || !A_log || !dt_bias) return KDA_ERR_INVALID_ARG;
-    if (!aligned(g, 8) || !aligned(dt_bias, 16)) return KDA_ERR_INVALID_ARG;
-    if (!std::isfinite(lower_bound) || lower_bound < -5.f || lower_bound > 0.f)
-        return KDA_ERR_INVALID_ARG;
+    Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, cu_seqlens != nullptr,
+             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale};
+    int st = check_kda_gate(T, g, A_log, dt_bias, lower_bound);
+    if (st != KDA_OK) return st;
     int32_t N = 0;
-    int st = check_common(c, N);
+    st = check_common(c, N);
     if (st != KDA_OK) return st;
     kda::PrepArgs p{};
     p.g_kda = g;
@@ -148,8 +185,8 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
             int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
             void* stream) {
-    Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, num_seqs, B, T, H, K, V,
-             o, workspace, workspace_bytes, scale};
+    Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, cu_seqlens != nullptr,
+             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale};
     if (T > 0 && !g) return KDA_ERR_INVALID_ARG;
     int32_t N = 0;
     int st = check_common(c, N);
@@ -157,6 +194,52 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
     kda::PrepArgs p{};
     p.g_gdn = g;
     return run(c, N, p, true, static_cast<hipStream_t>(stream));
+}
+
+int kda_prep(const uint16_t* q, const uint16_t* k, const uint16_t* g, const uint16_t* beta,
+             const float* A_log, const float* dt_bias, float lower_bound,
+             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+             int32_t K, int32_t V, void* workspace, size_t workspace_bytes, void* stream) {
+    // v and o are not touched by this stage; stand-ins satisfy the shared checks
+    Common c{q, k, q, beta, nullptr, nullptr, cu_seqlens, cu_seqlens != nullptr, num_seqs, B,
+             T, H, K, V, const_cast<uint16_t*>(q), workspace, workspace_bytes, 1.f};
+    int st = check_kda_gate(T, g, A_log, dt_bias, lower_bound);
+    if (st != KDA_OK) return st;
+    int32_t N = 0;
+    st = check_common(c, N);
+    if (st != KDA_OK) return st;
+    kda::PrepArgs p{};
+    p.g_kda = g;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.lower_bound = lower_bound;
+    return run_prep(c, N, p, false, static_cast<hipStream_t>(stream));
+}
+
+int gdn_prep(const uint16_t* q, const uint16_t* k, const float* g, const uint16_t* beta,
+             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+             int32_t K, int32_t V, void* workspace, size_t workspace_bytes, void* stream) {
+    Common c{q, k, q, beta, nullptr, nullptr, cu_seqlens, cu_seqlens != nullptr, num_seqs, B,
+             T, H, K, V, const_cast<uint16_t*>(q), workspace, workspace_bytes, 1.f};
+    if (T > 0 && !g) return KDA_ERR_INVALID_ARG;
+    int32_t N = 0;
+    int st = check_common(c, N);
+    if (st != KDA_OK) return st;
+    kda::PrepArgs p{};
+    p.g_gdn = g;
+    return run_prep(c, N, p, true, static_cast<hipStream_t>(stream));
+}
+
+int kda_recur(const uint16_t* v, float scale, const float* initial_state, float* final_state,
+              int32_t varlen, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+              int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes, void* stream) {
+    // q, k, beta are not read by this stage; v stands in for them in the shared checks
+    Common c{v, v, v, v, initial_state, final_state, nullptr, varlen != 0, num_seqs, B, T, H,
+             K, V, o, workspace, workspace_bytes, scale};
+    int32_t N = 0;
+    int st = check_common(c, N);
+    if (st != KDA_OK) return st;
+    return run_recur(c, N, static_cast<hipStream_t>(stream));
 }
 
 const char* kda_status_str(int status) {

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 // Tokens per chunk.  The FlashKDA summary (discuss.pytorch.kr, section
@@ -28,6 +30,7 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((ext_vector_type(4))) float floatx4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // one 16-byte slice
 
 // ---------------------------------------------------------------- MFMA
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] B[32x16].
@@ -53,6 +56,17 @@ __device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) {
     r[2] = (bf16)x[2];
     r[3] = (bf16)x[3];
     return r;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).  Array
+// indices derived from I are constants from the first optimisation pass on,
+// so register arrays indexed by them never fall back to scratch memory.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // ---------------------------------------------------------------- math
@@ -109,6 +123,26 @@ struct Rec {
 // channel of element e of lane group g in k-step j of a 16x16x32 fragment
 __host__ __device__ constexpr int frag32_channel(int j, int g, int e) {
     return 32 * j + 16 * (e >> 2) + 4 * g + (e & 3);
+}
+
+// Flattened token range [t0, t1) and chunk-slot range [s0, s1) of sequence n.
+// Fixed-length batches need no table: sequence n is tokens [n T, (n+1) T)
+// and slots [n ceil(T/C), (n+1) ceil(T/C)).
+template <class Args>
+__device__ __forceinline__ void seq_span(const Args& a, int n, int64_t& t0, int64_t& t1, int& s0,
+                                         int& s1) {
+    if (!a.packed) {
+        const int nt = (a.T + C - 1) / C;
+        t0 = (int64_t)n * a.T;
+        t1 = t0 + a.T;
+        s0 = n * nt;
+        s1 = s0 + nt;
+    } else {
+        t0 = a.seq_start[n];
+        t1 = a.seq_start[n + 1];
+        s0 = a.chunk_off[n];
+        s1 = a.chunk_off[n + 1];
+    }
 }
 
 }  // namespace kda

@@ -19,8 +19,10 @@ struct PrepArgs {
     float lower_bound;         // KDA floor of the log decay
     int32_t H;
     int32_t n_seqs;
-    const int32_t* seq_start;  // [n_seqs + 1] flattened token offsets
-    const int32_t* chunk_off;  // [n_seqs + 1] first chunk slot of each sequence
+    int32_t packed;            // 0: fixed length (every sequence has T tokens)
+    int32_t T;                 // tokens per sequence when not packed
+    const int32_t* seq_start;  // packed: [n_seqs + 1] flattened token offsets
+    const int32_t* chunk_off;  // packed: [n_seqs + 1] first chunk slot of each sequence
     unsigned char* rec;        // [slots, H, record bytes]
 };
 
@@ -34,6 +36,8 @@ struct RecurArgs {
     int32_t H;
     int32_t V;
     int32_t n_seqs;
+    int32_t packed;
+    int32_t T;
     const int32_t* seq_start;
     const int32_t* chunk_off;
 };

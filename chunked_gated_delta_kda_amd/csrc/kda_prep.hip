@@ -49,17 +49,25 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(PrepArgs a) {
     const int h = blockIdx.y;
     const int tid = threadIdx.x;
 
-    // ---- locate the chunk: chunk_off[n] <= slot < chunk_off[n+1]
-    const int total = a.chunk_off[a.n_seqs];
-    if (slot >= total) return;  // uniform over the workgroup
-    int lo = 0, hi = a.n_seqs;  // invariant: chunk_off[lo] <= slot < chunk_off[hi]
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (a.chunk_off[mid] <= slot) lo = mid; else hi = mid;
+    // ---- locate the chunk: sequence n with chunk_off[n] <= slot < chunk_off[n+1]
+    int n;
+    if (!a.packed) {
+        n = slot / ((a.T + C - 1) / C);  // launched only when T > 0
+        if (n >= a.n_seqs) return;  // uniform over the workgroup
+    } else {
+        if (slot >= a.chunk_off[a.n_seqs]) return;
+        int lo = 0, hi = a.n_seqs;  // invariant: chunk_off[lo] <= slot < chunk_off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.chunk_off[mid] <= slot) lo = mid; else hi = mid;
+        }
+        n = lo;
     }
-    const int n = lo;
-    const int64_t start = (int64_t)a.seq_start[n] + (int64_t)C * (slot - a.chunk_off[n]);
-    const int nvalid = (int)min((int64_t)C, (int64_t)a.seq_start[n + 1] - start);
+    int64_t t0, t1;
+    int s0, s1;
+    seq_span(a, n, t0, t1, s0, s1);
+    const int64_t start = t0 + (int64_t)C * (slot - s0);
+    const int nvalid = (int)min((int64_t)C, t1 - start);
 
     // ---- phase 1: one token row per 16 threads, EPT channels per thread
     const int r = tid >> 4;

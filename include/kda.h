@@ -106,6 +106,36 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
             int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
             void* stream);
 
+/* The two stages of kda_fwd / gdn_fwd, callable on their own (same
+ * conventions; kda_fwd is exactly kda_prep followed by kda_recur).
+ *
+ * kda_prep / gdn_prep: the token-parallel stage.  Gate activation, sigmoid
+ * of beta (KDA), in-chunk cumulative decay, q/k L2 norm, the intra-chunk
+ * matrices and the exact inverse of (I + A); writes the sequence table and
+ * one record per (16-token chunk, head) into the workspace.  The FlashKDA
+ * summary (discuss.pytorch.kr, section "커널 퓨전(Kernel Fusion) 전략의 분리")
+ * puts exactly these operations in its first, token-parallel kernel.
+ *
+ * kda_recur: the head-parallel stage.  The sequential inter-chunk state
+ * update and the output, reading the workspace that the preceding prep call
+ * filled on the same stream with the same B, T, H, K, V and sequence
+ * packing (varlen != 0 when that call received cu_seqlens, with the same
+ * num_seqs).  The same page assigns the chunked delta recurrence and the
+ * output projection to its second, head-parallel kernel.  It serves both
+ * KDA and GDN workspaces. */
+int kda_prep(const uint16_t* q, const uint16_t* k, const uint16_t* g, const uint16_t* beta,
+             const float* A_log, const float* dt_bias, float lower_bound,
+             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+             int32_t K, int32_t V, void* workspace, size_t workspace_bytes, void* stream);
+
+int gdn_prep(const uint16_t* q, const uint16_t* k, const float* g, const uint16_t* beta,
+             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+             int32_t K, int32_t V, void* workspace, size_t workspace_bytes, void* stream);
+
+int kda_recur(const uint16_t* v, float scale, const float* initial_state, float* final_state,
+              int32_t varlen, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+              int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* kda_status_str(int status);
 

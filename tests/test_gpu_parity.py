@@ -214,3 +214,25 @@ FULL = [(1, [0, 13, 31]), (2, [5]), (3, [0, 11]), (4, [7])]
 @pytest.mark.parametrize("cfg,heads", FULL, ids=lambda x: str(x))
 def test_full_config(cfg, heads):
     check_parity(inputs.config(cfg), heads=heads)
+
+
+def test_stages_equal_fused_call():
+    """kda_prep followed by kda_recur (the two ABI stages, as the benchmark times
+    them) gives bitwise the same result as kda_fwd; the same for gdn_prep."""
+    for w in (inputs.kda_workload(2, 200, 3, 128, 128, seed=4200, init_std=0.05),
+              inputs.gdn_workload(1, 0, 2, 128, 64, seed=4300, lengths=[50, 0, 77])):
+        o, S = gpu_run(w)
+        d = w.to("cuda:0")
+        ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.K, w.V, w.n_seqs),
+                         dtype=torch.uint8, device="cuda:0")
+        if w.kind == "kda":
+            kda.kda_prep(d["q"], d["k"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
+                         w.lower_bound, ws, d["cu_seqlens"], V=w.V)
+        else:
+            kda.gdn_prep(d["q"], d["k"], d["g"], d["beta"], ws, d["cu_seqlens"], V=w.V)
+        o2 = torch.empty_like(o)
+        S2 = torch.empty_like(S)
+        kda.kda_recur(d["v"], w.K, w.scale, ws, o2, d["initial_state"], S2,
+                      num_seqs=None if w.cu_seqlens is None else w.n_seqs)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(S, S2)
