@@ -33,8 +33,11 @@ def build(verbose: bool = False, extra_flags=()) -> Path:
     os.close(fd)
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function",
-           # packed fp32 VALU ops are left to be formed by nobody: plain float code only
+           # no packed fp32 VALU ops anywhere: plain float code only
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA results in VGPRs: the kernels convert and rescale their
+           # accumulators on the VALU every chunk, so AGPR round trips would cost
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            f"-I{INCLUDE}", f"-I{CSRC}", *extra_flags,
            *[str(CSRC / s) for s in SOURCES], "-o", tmp]
     if verbose:

@@ -59,7 +59,8 @@ int check_common(const Common& c, int32_t& N) {
     } else {
         N = c.B;
     }
-    if (!aligned(c.q, 8) || !aligned(c.k, 8) || !aligned(c.o, 8)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.o, 8))
+        return KDA_ERR_INVALID_ARG;
     if (!c.ws || !aligned(c.ws, ALIGN)) return KDA_ERR_WORKSPACE;
     if (c.ws_bytes < workspace_bytes_for(c.B, c.T, c.H, c.K, N, c.varlen))
         return KDA_ERR_WORKSPACE;
@@ -136,7 +137,7 @@ int run(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t strea
 int check_kda_gate(int32_t T, const uint16_t* g, const float* A_log, const float* dt_bias,
                    float lower_bound) {
     if ((T > 0 && !g) || !A_log || !dt_bias) return KDA_ERR_INVALID_ARG;
-    if (!aligned(g, 8) || !aligned(dt_bias, 16)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(g, 16) || !aligned(dt_bias, 16)) return KDA_ERR_INVALID_ARG;
     if (!std::isfinite(lower_bound) || lower_bound < -5.f || lower_bound > 0.f)
         return KDA_ERR_INVALID_ARG;
     return KDA_OK;

@@ -96,33 +96,42 @@ __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uin
 // Gam = exp(G):
 //   nKG  = -(k^ * Gam)         [16 x K]  A operand of 16x16x32 against S
 //   QG   =   q^ * Gam          [16 x K]  B operand of 16x16x32 against S^T
-//   KdT  = (k^ * Gam_C / Gam)^T[K x 16]  A operand of 16x16x16 against U'
+//   KdT  = (k^ * Gam_C / Gam)^T[K x 16]  A operand of 16x16x16 against U',
+//                                        one 16-channel state tile at a time
 //   Aqk  = tril(QG (k^/Gam)^T) [16 x 16] B operand (transposed) for O^T
 //   Tb   = (I + A)^-1 diag(b)  [16 x 16] A operand for U' = Tb (V - KG S)
-//   GamC = Gam at the chunk's last row, fp32 [K]
+//   GamC = Gam at the chunk's last row, fp32 [K] in tile-channel order
 // with A[r][j] = b_r sum_c (k^ Gam)[r][c] (k^/Gam)[j][c] for j < r.
 //
-// K index order inside a 16x16x32 fragment: k-step j (32 channels), lane
-// group g, element e  ->  channel 32 j + 16 (e / 4) + 4 g + (e % 4).  This is
-// the order in which kda_recur's fp32 state tiles (D layout, 16 channels per
-// tile, lane group g holding rows 4g..4g+3) become the B/A operand of the
-// next chunk without any data movement.
+// Channel orders.  Inside a 16x16x32 fragment, k-step j, lane group g and
+// element e hold channel 32 j + 8 g + e (8 contiguous channels per lane, so
+// prep loads and stores them as 16-byte vectors).  kda_recur keeps the state
+// as K/16 tiles of 16 channels in MFMA D layout (lane group g holds tile rows
+// 4g..4g+3); tile t, row r holds channel
+//   rho(t, r) = 32 (t / 2) + 8 (r / 4) + 4 (t % 2) + (r % 4),
+// chosen so that tiles 2j and 2j+1, elements 0..3 of lane group g, are
+// exactly channels 32 j + 8 g + 0..7: the fp32 state tiles become the bf16
+// B (and A) operand of the next chunk's 16x16x32 products with no data
+// movement.  KdT and GamC are stored in tile order.
 template <int K>
 struct Rec {
     static constexpr int KSTEPS = K / 32;               // 16x16x32 k-steps
     static constexpr int KTILES = K / 16;               // 16-row state tiles
     static constexpr int NKG = 0;                       // bf16 [KSTEPS][4][16][8]
     static constexpr int QG = NKG + C * K * 2;          // bf16 [KSTEPS][4][16][8]
-    static constexpr int KDT = QG + C * K * 2;          // bf16 [KTILES][4][16][4]
+    static constexpr int KDT = QG + C * K * 2;          // bf16 [KTILES][4][16][4]:
+                                                        //   [t][g][m][i] = Kd[4g+i][rho(t,m)]
     static constexpr int AQK = KDT + C * K * 2;         // bf16 [4][16][4]
     static constexpr int TB = AQK + C * C * 2;          // bf16 [4][16][4]
-    static constexpr int GAMC = TB + C * C * 2;         // fp32 [K]
+    static constexpr int GAMC = TB + C * C * 2;         // fp32 [K]: [t][r] = Gam_C[rho(t,r)]
     static constexpr int BYTES = GAMC + K * 4;
 };
 
 // channel of element e of lane group g in k-step j of a 16x16x32 fragment
-__host__ __device__ constexpr int frag32_channel(int j, int g, int e) {
-    return 32 * j + 16 * (e >> 2) + 4 * g + (e & 3);
+__host__ __device__ constexpr int frag_channel(int j, int g, int e) { return 32 * j + 8 * g + e; }
+// channel of row r of state tile t
+__host__ __device__ constexpr int tile_channel(int t, int r) {
+    return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
 }
 
 // Flattened token range [t0, t1) and chunk-slot range [s0, s1) of sequence n.

@@ -19,41 +19,95 @@
 
 namespace kda {
 
-// The doubling product: A strictly lower triangular (16 x 16) is nilpotent,
-// A^16 = 0, so with N = -A
-//   (I + A)^-1 = sum_{p=0}^{15} N^p = (I + N)(I + N^2)(I + N^4)(I + N^8)
-// exactly (no truncation).  Computed in fp32.
-constexpr int LDA = C + 1;  // padded row stride of the fp32 16x16 buffers
+// One wave per (16-token chunk, head).  Lane l = m + 16 g owns token row m
+// of the chunk and, for every k-step j, the 8 contiguous channels
+// 32 j + 8 g .. +7: exactly the row-m slice of a 16x16x32 MFMA fragment.
+// Every intra-chunk product therefore reads its operands straight from
+// registers, the q/k/g loads and the nKG/QG record stores are 16-byte
+// vectors, and the wave needs no barrier.
+//
+//  - gate:   log2 a = max(lb, -exp(A_log[h]) softplus(g + dt_bias)) log2(e)
+//  - cumsum: inclusive prefix over the 16 rows = 16-lane DPP row scan
+//  - norms:  sum of squares over the 4 lane groups of a row (2 xor shuffles)
+//  - A, A^T, Aqk^T: bf16 MFMA over K on the fragments
+//  - (I + A)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8), N = -A, exact because
+//    A is strictly lower triangular (A^16 = 0).  With the MFMA primitive
+//    M(P, Q) = P^T Q on D-layout operands (the D layout of P read as an A
+//    operand is P^T), every matrix is kept together with its transpose, so
+//    no product needs a layout change.  Operands are fp16 (|N| <= 1 and the
+//    powers stay far below the fp16 range for a 16 x 16 triangle), products
+//    accumulate in fp32.
+namespace {
 
-template <int K>
-struct PrepSmem {
-    static constexpr int LDK = K + 8;       // padded bf16 row stride (bank spread)
-    float la[C][K];                         // log2 decay, then its in-chunk prefix sum
-    bf16 kg[C][LDK];                        // k^ * Gam
-    bf16 kig[C][LDK];                       // k^ / Gam
-    bf16 qg[C][LDK];                        // q^ * Gam
-    float nmat[C][LDA];                     // N = -A
-    float n2[C][LDA], n4[C][LDA], n8[C][LDA];
-    float p1[C][LDA], p2[C][LDA];
-    float beta[C];
-    alignas(16) unsigned char rec[Rec<K>::BYTES];
-};
+constexpr int ROW_SHR1 = 0x111, ROW_SHR2 = 0x112, ROW_SHR4 = 0x114, ROW_SHR8 = 0x118;
+
+typedef __attribute__((ext_vector_type(4))) _Float16 halfx4;
+
+__device__ __forceinline__ float row_scan16(float x) {
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR1, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR2, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR4, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR8, 0xf, 0xf, false);
+    return x;
+}
+
+__device__ __forceinline__ float lane_val(float x, int src) { return __shfl(x, src, 64); }
+
+__device__ __forceinline__ halfx4 to_h4(floatx4 x) {
+    halfx4 r;
+    r[0] = (_Float16)x[0];
+    r[1] = (_Float16)x[1];
+    r[2] = (_Float16)x[2];
+    r[3] = (_Float16)x[3];
+    return r;
+}
+
+// M(P, Q) = P^T Q for 16 x 16 matrices given in D layout.
+__device__ __forceinline__ floatx4 mt(floatx4 p, floatx4 q) {
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(to_h4(p), to_h4(q), zero, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 add4(floatx4 a, floatx4 b) {
+    floatx4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = a[i] + b[i];
+    return r;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 v, float* f) {
+    const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f[2 * u] = bf2f(w[u] & 0xffff);
+        f[2 * u + 1] = bf2f(w[u] >> 16);
+    }
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* f, float s = 1.f) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)(s * f[e]);
+    return r;
+}
+
+}  // namespace
 
 template <int K, bool GDN>
-__global__ __launch_bounds__(256) void kda_prep_kernel(PrepArgs a) {
-    constexpr int EPT = K / 16;  // channels per thread in the token-row phase
+__global__ __launch_bounds__(64) void kda_prep_kernel(PrepArgs a) {
+    constexpr int KS = K / 32;  // 16-byte channel slices per lane
     using R = Rec<K>;
-    __shared__ PrepSmem<K> sm;
+    __shared__ __attribute__((aligned(16))) uint16_t kdt_s[C * K];  // KdT transpose
 
     const int slot = blockIdx.x;
     const int h = blockIdx.y;
-    const int tid = threadIdx.x;
+    const int L = threadIdx.x, m = L & 15, g = L >> 4;
 
     // ---- locate the chunk: sequence n with chunk_off[n] <= slot < chunk_off[n+1]
     int n;
     if (!a.packed) {
         n = slot / ((a.T + C - 1) / C);  // launched only when T > 0
-        if (n >= a.n_seqs) return;  // uniform over the workgroup
+        if (n >= a.n_seqs) return;
     } else {
         if (slot >= a.chunk_off[a.n_seqs]) return;
         int lo = 0, hi = a.n_seqs;  // invariant: chunk_off[lo] <= slot < chunk_off[hi]
@@ -68,212 +122,179 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(PrepArgs a) {
     seq_span(a, n, t0, t1, s0, s1);
     const int64_t start = t0 + (int64_t)C * (slot - s0);
     const int nvalid = (int)min((int64_t)C, t1 - start);
+    const bool valid = m < nvalid;
+    const int64_t row = (start + m) * a.H + h;  // flattened (token, head) row
 
-    // ---- phase 1: one token row per 16 threads, EPT channels per thread
-    const int r = tid >> 4;
-    const int cg = tid & 15;
-    const int c0 = cg * EPT;
-    const bool valid = r < nvalid;
-    const int64_t row = (start + r) * a.H + h;  // flattened (token, head) row
-
-    float q[EPT], k[EPT], la[EPT];
-    float b = 0.f;
-    if (valid) {
-        const uint16_t* qp = a.q + row * K + c0;
-        const uint16_t* kp = a.k + row * K + c0;
+    // ---- every global load up front, from an always-valid row (padding rows
+    // re-read the chunk's first row and are zeroed by value), so the wave
+    // waits for memory once; q, k, g stay packed bf16 until their slice is used
+    const int64_t lrow = (start + (valid ? m : 0)) * a.H + h;
+    u32x4 qr[KS], kr[KS], gr[KS];
+    floatx4 dtr[KS][2];
 #pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-            uint2 qv = *reinterpret_cast<const uint2*>(qp + e);
-            uint2 kv = *reinterpret_cast<const uint2*>(kp + e);
-            q[e + 0] = bf2f(qv.x & 0xffff); q[e + 1] = bf2f(qv.x >> 16);
-            q[e + 2] = bf2f(qv.y & 0xffff); q[e + 3] = bf2f(qv.y >> 16);
-            k[e + 0] = bf2f(kv.x & 0xffff); k[e + 1] = bf2f(kv.x >> 16);
-            k[e + 2] = bf2f(kv.y & 0xffff); k[e + 3] = bf2f(kv.y >> 16);
+    for (int j = 0; j < KS; ++j) {
+        const int c = 32 * j + 8 * g;
+        qr[j] = *reinterpret_cast<const u32x4*>(a.q + lrow * K + c);
+        kr[j] = *reinterpret_cast<const u32x4*>(a.k + lrow * K + c);
+        if constexpr (!GDN) {
+            gr[j] = *reinterpret_cast<const u32x4*>(a.g_kda + lrow * K + c);
+            dtr[j][0] = *reinterpret_cast<const floatx4*>(a.dt_bias + (int64_t)h * K + c);
+            dtr[j][1] = *reinterpret_cast<const floatx4*>(a.dt_bias + (int64_t)h * K + c + 4);
         }
-        if constexpr (GDN) {
-            // GDN: g is the log decay itself, one scalar per (token, head).
-            const float l2 = a.g_gdn[row] * LOG2E;
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) la[e] = l2;
-            b = bf2f(a.beta[row]);
-        } else {
-            // KDA: log a = max(lb, -exp(A_log[h]) * softplus(g + dt_bias[h, c]))
-            const float rate = exp2_hw(a.A_log[h] * LOG2E);
-            const uint16_t* gp = a.g_kda + row * K + c0;
-            const float* dp = a.dt_bias + (int64_t)h * K + c0;
-#pragma unroll
-            for (int e = 0; e < EPT; e += 4) {
-                uint2 gv = *reinterpret_cast<const uint2*>(gp + e);
-                float4 dv = *reinterpret_cast<const float4*>(dp + e);
-                float x[4] = {bf2f(gv.x & 0xffff) + dv.x, bf2f(gv.x >> 16) + dv.y,
-                              bf2f(gv.y & 0xffff) + dv.z, bf2f(gv.y >> 16) + dv.w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    la[e + u] = fmaxf(a.lower_bound, -rate * softplus_f(x[u])) * LOG2E;
-            }
-            b = sigmoid_f(bf2f(a.beta[row]));
-        }
-    } else {
-        // padding rows: beta = 0 and log decay = 0 leave the state unchanged
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) { q[e] = 0.f; k[e] = 0.f; la[e] = 0.f; }
     }
+    const float braw = bf2f(a.beta[lrow]);
+    const float graw = GDN ? a.g_gdn[lrow] : 0.f;
+    const float rate = GDN ? 0.f : exp2_hw(a.A_log[h] * LOG2E);
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        qr[j] = valid ? qr[j] : zero4;
+        kr[j] = valid ? kr[j] : zero4;
+    }
+    // beta: KDA logits through the sigmoid, GDN probabilities as given; 0 on padding
+    const float b = valid ? (GDN ? braw : sigmoid_f(braw)) : 0.f;
+    const float la_row = valid ? graw * LOG2E : 0.f;
 
-    // L2 norms: the 16 lanes of a row are consecutive lanes of one wave.
+    // ---- L2 norms: a row's channels live in lanes m, m+16, m+32, m+48
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) { sq += q[e] * q[e]; sk += k[e] * k[e]; }
+    for (int j = 0; j < KS; ++j) {
+        float x[8], y[8];
+        unpack8(qr[j], x);
+        unpack8(kr[j], y);
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        sq += __shfl_xor(sq, m, 64);
-        sk += __shfl_xor(sk, m, 64);
+        for (int e = 0; e < 8; ++e) { sq += x[e] * x[e]; sk += y[e] * y[e]; }
     }
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    sk += __shfl_xor(sk, 16, 64);
+    sk += __shfl_xor(sk, 32, 64);
     const float iq = rsq_hw(sq + NORM_EPS), ik = rsq_hw(sk + NORM_EPS);
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) { q[e] *= iq; k[e] *= ik; sm.la[r][c0 + e] = la[e]; }
-    if (cg == 0) sm.beta[r] = b;
-    __syncthreads();
 
-    // ---- phase 2: in-chunk inclusive prefix sum of the log2 decay, per channel
-    if (tid < K) {
-        float acc = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < C; ++rr) { acc += sm.la[rr][tid]; sm.la[rr][tid] = acc; }
+    // GDN: in-chunk inclusive prefix of the scalar log2 decay, and its total
+    float G_row = 0.f, GC_row = 0.f;
+    if constexpr (GDN) {
+        G_row = row_scan16(la_row);
+        GC_row = lane_val(G_row, 15 + 16 * g);
     }
-    __syncthreads();
 
-    // ---- phase 3: decay factors and the K-side record pieces
-    {
-        float kd[EPT], kgv[EPT], qgv[EPT];
-        if constexpr (GDN) {
-            // scalar decay: every factor is exp2 of a non-positive difference
-            const float G = sm.la[r][0], GC = sm.la[C - 1][0];
-            const float gam = exp2_hw(G), gamd = exp2_hw(GC - G), gamc = exp2_hw(GC);
+    // ---- one 8-channel slice at a time: gate, prefix sum over the 16 rows
+    // (a 16-lane DPP scan), decay factors, record pieces, and this slice's
+    // contribution to the intra-chunk products.  mfma32(X, Y) gives D = X Y^T:
+    // lane (n, g) holds element i of D at row 4g + i, column n.
+    unsigned char* rec = a.rec + ((int64_t)slot * a.H + h) * R::BYTES;
+    floatx4 dA = {0.f, 0.f, 0.f, 0.f}, dAT = dA, dQT = dA;
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                sm.kg[r][c0 + e] = (bf16)k[e];   // intra-chunk products use k^ and q^,
-                sm.kig[r][c0 + e] = (bf16)k[e];  // the decay is applied per element
-                sm.qg[r][c0 + e] = (bf16)q[e];
-                kgv[e] = k[e] * gam;
-                qgv[e] = q[e] * gam;
-                kd[e] = k[e] * gamd;
-                if (r == C - 1) reinterpret_cast<float*>(sm.rec + R::GAMC)[c0 + e] = gamc;
+    for (int j = 0; j < KS; ++j) {
+        float qn[8], kn[8];
+        unpack8(qr[j], qn);
+        unpack8(kr[j], kn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { qn[e] *= iq; kn[e] *= ik; }
+        float kgv[8], qgv[8], kiv[8], kd[8], gamc[8];
+        if constexpr (GDN) {
+            const float gam = exp2_hw(G_row), gkd = exp2_hw(GC_row - G_row), gc = exp2_hw(GC_row);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kgv[e] = kn[e] * gam;
+                qgv[e] = qn[e] * gam;
+                kd[e] = kn[e] * gkd;
+                gamc[e] = gc;
             }
         } else {
+            float x[8];
+            unpack8(gr[j], x);
+            const floatx4 d0 = dtr[j][0], d1 = dtr[j][1];
+            const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                const float G = sm.la[r][c0 + e];
-                const float GC = sm.la[C - 1][c0 + e];
-                const float gam = exp2_hw(G), gami = exp2_hw(-G), gamc = exp2_hw(GC);
-                kgv[e] = k[e] * gam;
-                qgv[e] = q[e] * gam;
-                sm.kg[r][c0 + e] = (bf16)kgv[e];
-                sm.kig[r][c0 + e] = (bf16)(k[e] * gami);
-                sm.qg[r][c0 + e] = (bf16)qgv[e];
-                kd[e] = k[e] * gamc * gami;
-                if (r == C - 1) reinterpret_cast<float*>(sm.rec + R::GAMC)[c0 + e] = gamc;
+            for (int e = 0; e < 8; ++e) {
+                // padding rows keep log decay 0 (decay 1)
+                const float la =
+                    valid ? fmaxf(a.lower_bound, -rate * softplus_f(x[e] + dv[e])) * LOG2E : 0.f;
+                const float G = row_scan16(la);
+                const float GC = lane_val(G, 15 + 16 * g);
+                const float gam = exp2_hw(G);
+                kgv[e] = kn[e] * gam;
+                qgv[e] = qn[e] * gam;
+                kiv[e] = kn[e] * exp2_hw(-G);
+                kd[e] = kn[e] * exp2_hw(GC - G);
+                gamc[e] = gam;  // row 15 holds Gam_C
             }
         }
-        // nKG and QG in 16x16x32 fragment order: 4 consecutive channels
-        // c..c+3 (c % 4 == 0) land on 4 consecutive elements of one lane.
-#pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-            const int c = c0 + e, j = c >> 5, w = c & 31;
-            const int gg = (w & 15) >> 2, ee = (w >> 4) << 2;
-            const int off = (((j * 4 + gg) * 16 + r) * 8 + ee) * 2;
-            bf16x4 nkg, qv;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                nkg[u] = (bf16)(-kgv[e + u]);
-                qv[u] = (bf16)qgv[e + u];
-            }
-            *reinterpret_cast<bf16x4*>(sm.rec + R::NKG + off) = nkg;
-            *reinterpret_cast<bf16x4*>(sm.rec + R::QG + off) = qv;
+        *reinterpret_cast<bf16x8*>(rec + R::NKG + (j * 64 + L) * 16) = pack8(kgv, -1.f);
+        *reinterpret_cast<bf16x8*>(rec + R::QG + (j * 64 + L) * 16) = pack8(qgv);
+        // GamC in tile order: channel 32 j + 8 g + e is tile 2j + e/4, row 4g + e%4
+        if (m == C - 1) {
+            float* gp = reinterpret_cast<float*>(rec + R::GAMC);
+            const floatx4 lo = {gamc[0], gamc[1], gamc[2], gamc[3]};
+            const floatx4 hi = {gamc[4], gamc[5], gamc[6], gamc[7]};
+            *reinterpret_cast<floatx4*>(gp + 32 * j + 4 * g) = lo;
+            *reinterpret_cast<floatx4*>(gp + 32 * j + 16 + 4 * g) = hi;
         }
-        // KdT[b][g][m][i] = Kd[token 4g + i][channel 16b + m]
+        // KdT[t][g'][m'][i'] = Kd[token 4g'+i'][rho(t, m')]: transposed through LDS
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const int c = c0 + e;
-            const int off = ((((c >> 4) * 4 + (r >> 2)) * 16 + (c & 15)) * 4 + (r & 3)) * 2;
-            *reinterpret_cast<bf16*>(sm.rec + R::KDT + off) = (bf16)kd[e];
+        for (int e = 0; e < 8; ++e) {
+            const int t = 2 * j + (e >> 2), r = 4 * g + (e & 3);
+            kdt_s[((t * 4 + (m >> 2)) * 16 + r) * 4 + (m & 3)] =
+                __builtin_bit_cast(uint16_t, (bf16)kd[e]);
+        }
+        if constexpr (GDN) {
+            // the intra-chunk products use k^ and q^; the decay is applied per element
+            const bf16x8 kf = pack8(kn), qf = pack8(qn);
+            dA = mfma32(kf, kf, dA);
+            dQT = mfma32(kf, qf, dQT);
+        } else {
+            const bf16x8 kgf = pack8(kgv), kif = pack8(kiv), qgf = pack8(qgv);
+            dA = mfma32(kgf, kif, dA);    // KG KiG^T
+            dAT = mfma32(kif, kgf, dAT);  // KiG KG^T
+            dQT = mfma32(kif, qgf, dQT);  // KiG QG^T = Aqk^T
         }
     }
-    __syncthreads();
+    if constexpr (GDN) dAT = dA;  // k^ k^T is symmetric
 
-    // ---- phase 4: A = diag(beta) strict_tril(KG KiG^T), Aqk = tril(QG KiG^T)
-    // (GDN: the same products of k^ and q^, times exp2(G_r - G_j) per element)
-    const int wave = tid >> 6, lane = tid & 63;
-    const int lr = lane & 15, lg = lane >> 4;
-    if (wave < 2) {
-        const bf16 (*lhs)[PrepSmem<K>::LDK] = wave == 0 ? sm.kg : sm.qg;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
 #pragma unroll
-        for (int j = 0; j < K / 32; ++j) {
-            bf16x8 av = *reinterpret_cast<const bf16x8*>(&lhs[lr][32 * j + 8 * lg]);
-            bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.kig[lr][32 * j + 8 * lg]);
-            acc = mfma32(av, bv, acc);
-        }
-        // lane holds M[4 lg + i][lr]: row rr = 4 lg + i, column jj = lr
+    for (int p = 0; p < C * K * 2 / (64 * 16); ++p)
+        *reinterpret_cast<u32x4*>(rec + R::KDT + (p * 64 + L) * 16) =
+            *reinterpret_cast<const u32x4*>(kdt_s + (p * 64 + L) * 8);
+
+    float br[4], Gr[4];  // beta and (GDN) log decay of rows 4g .. 4g+3
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 4 * lg + i, jj = lr;
-            float m = acc[i];
-            if constexpr (GDN) {
-                if (jj <= rr) m *= exp2_hw(sm.la[rr][0] - sm.la[jj][0]);
-            }
-            if (wave == 0) {
-                // keep j < r; N = -A
-                sm.nmat[rr][jj] = jj < rr ? -sm.beta[rr] * m : 0.f;
-            } else {
-                const float v = jj <= rr ? m : 0.f;
-                const int off = (((jj >> 2) * 16 + rr) * 4 + (jj & 3)) * 2;
-                *reinterpret_cast<bf16*>(sm.rec + R::AQK + off) = (bf16)v;
-            }
-        }
+    for (int i = 0; i < 4; ++i) {
+        br[i] = lane_val(b, 4 * g + i);
+        if constexpr (GDN) Gr[i] = lane_val(G_row, 4 * g + i);
     }
-    __syncthreads();
-
-    // ---- phase 5: T = (I + N)(I + N^2)(I + N^4)(I + N^8), one element per thread
-    {
-        const int rr = tid >> 4, cc = tid & 15;
-        float s = 0.f;
+    floatx4 N, NT;
+    bf16x4 aqk;
 #pragma unroll
-        for (int m = 0; m < C; ++m) s += sm.nmat[rr][m] * sm.nmat[m][cc];
-        sm.n2[rr][cc] = s;
-        __syncthreads();
-        float s4 = 0.f, s3 = 0.f;
-#pragma unroll
-        for (int m = 0; m < C; ++m) {
-            s4 += sm.n2[rr][m] * sm.n2[m][cc];
-            s3 += sm.nmat[rr][m] * sm.n2[m][cc];
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;  // this element's row; its column is m
+        float dec_rm = 1.f, dec_mr = 1.f;
+        if constexpr (GDN) {
+            dec_rm = r > m ? exp2_hw(Gr[i] - G_row) : 0.f;  // exp(G_r - G_m), r > m
+            dec_mr = m >= r ? exp2_hw(G_row - Gr[i]) : 0.f;  // exp(G_m - G_r), m >= r
         }
-        sm.n4[rr][cc] = s4;
-        // P1 = (I + N)(I + N^2) = I + N + N^2 + N^3
-        sm.p1[rr][cc] = (rr == cc ? 1.f : 0.f) + sm.nmat[rr][cc] + sm.n2[rr][cc] + s3;
-        __syncthreads();
-        float s8 = 0.f, t2 = 0.f;
-#pragma unroll
-        for (int m = 0; m < C; ++m) {
-            s8 += sm.n4[rr][m] * sm.n4[m][cc];
-            t2 += sm.p1[rr][m] * sm.n4[m][cc];
-        }
-        sm.n8[rr][cc] = s8;
-        sm.p2[rr][cc] = sm.p1[rr][cc] + t2;  // P2 = P1 (I + N^4)
-        __syncthreads();
-        float t3 = 0.f;
-#pragma unroll
-        for (int m = 0; m < C; ++m) t3 += sm.p2[rr][m] * sm.n8[m][cc];
-        const float T = sm.p2[rr][cc] + t3;  // P2 (I + N^8)
-        // Tb = T diag(beta), stored as Tb[g][m][i] = Tb[m][4g + i]
-        const int off = (((cc >> 2) * 16 + rr) * 4 + (cc & 3)) * 2;
-        *reinterpret_cast<bf16*>(sm.rec + R::TB + off) = (bf16)(T * sm.beta[cc]);
+        N[i] = m < r ? -br[i] * dA[i] * dec_rm : 0.f;          // N[r][m], m < r
+        NT[i] = r < m ? -b * dAT[i] * dec_mr : 0.f;            // N^T[r][m] = N[m][r], r < m
+        aqk[i] = (bf16)(r <= m ? dQT[i] * dec_mr : 0.f);     // Aqk[m][r], r <= m
     }
-    __syncthreads();
+    *reinterpret_cast<bf16x4*>(rec + R::AQK + L * 8) = aqk;
 
-    // ---- phase 6: stream the record out, 16 bytes per thread per step
-    uint4* dst = reinterpret_cast<uint4*>(a.rec + ((int64_t)slot * a.H + h) * R::BYTES);
-    const uint4* src = reinterpret_cast<const uint4*>(sm.rec);
-    for (int i = tid; i < R::BYTES / 16; i += 256) dst[i] = src[i];
+    // ---- T^T = ((I + N)(I + N^2)(I + N^4)(I + N^8))^T by transposed products
+    const floatx4 N2 = mt(NT, N), N2T = mt(N, NT);
+    const floatx4 N4 = mt(N2T, N2), N4T = mt(N2, N2T);
+    const floatx4 N8 = mt(N4T, N4);
+    floatx4 I4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) I4[i] = (4 * g + i == m) ? 1.f : 0.f;
+    const floatx4 P1T = add4(add4(I4, NT), add4(N2T, mt(N2, NT)));  // (I + N + N^2 + N^3)^T
+    const floatx4 P2T = add4(P1T, mt(N4, P1T));                     // (P1 (I + N^4))^T
+    const floatx4 TT = add4(P2T, mt(N8, P2T));                      // (P2 (I + N^8))^T
+    // Tb = T diag(b): the record holds Tb[m][4g + i] = (diag(b) T^T)[4g + i][m]
+    bf16x4 tb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tb[i] = (bf16)(br[i] * TT[i]);
+    *reinterpret_cast<bf16x4*>(rec + R::TB + L * 8) = tb;
 }
 
 // Sequence table: seq_start[0..N] (flattened token offsets) and
@@ -336,7 +357,7 @@ void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t tota
 
 template <int K, bool GDN>
 void launch_prep_t(const PrepArgs& a, int n_slots, hipStream_t stream) {
-    hipLaunchKernelGGL((kda_prep_kernel<K, GDN>), dim3(n_slots, a.H), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((kda_prep_kernel<K, GDN>), dim3(n_slots, a.H), dim3(64), 0, stream, a);
 }
 
 void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream) {

@@ -24,9 +24,11 @@
 // Memory pipeline: the loop is a strict chain (chunk i+1 needs the state
 // after chunk i), so the HBM latency of the per-chunk inputs must be hidden
 // by loading far ahead.  Every lane of the workgroup loads a 16-byte slice of
-// the record and of the chunk's V tile DEPTH chunks ahead into registers; one
-// chunk ahead the slices are written to an LDS double buffer from which the
-// waves read their MFMA fragments.  One barrier per chunk.
+// the record and of the chunk's V tile DEPTH+2 chunks ahead into registers;
+// two chunks ahead the slices are written to one of three LDS buffers; one
+// chunk ahead each wave reads its MFMA operands from LDS into registers, so
+// the chunk being computed reads only its decay vector.  One barrier per
+// chunk.
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -49,10 +51,11 @@ struct StageLayout {
 
 template <int K, int NW, int DEPTH>
 __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
+    static_assert(DEPTH % 2 == 0 && DEPTH >= 2, "the operand double buffer needs an even depth");
     using R = Rec<K>;
     using L = StageLayout<K, NW>;
     constexpr int KS = K / 32, KT = K / 16;
-    __shared__ __attribute__((aligned(16))) unsigned char stage[2][L::PADDED];
+    __shared__ __attribute__((aligned(16))) unsigned char stage[3][L::PADDED];
 
     // XCD-aware placement: workgroups are dealt to the 8 XCDs round robin, so
     // blocks b and b + 8 share an XCD (and its L2).  The VS column blocks of
@@ -71,15 +74,16 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
     const int cw = wave * 16;            // this wave's first column within the block
     const int cb = vs * L::VCOLS;        // the block's first value column
 
-    // state tiles: S[t][i] = S[16 t + 4 lg + i][cb + cw + lr]
+    // state tiles: S[t][i] = S[rho(t, 4 lg + i)][cb + cw + lr] (channel order of kda_common.h)
     floatx4 S[KT];
     const int64_t st = ((int64_t)n * a.H + h) * K * a.V + cb + cw + lr;
 #pragma unroll
     for (int t = 0; t < KT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            S[t][i] = a.initial_state ? a.initial_state[st + (int64_t)(16 * t + 4 * lg + i) * a.V]
-                                      : 0.f;
+            S[t][i] = a.initial_state
+                          ? a.initial_state[st + (int64_t)tile_channel(t, 4 * lg + i) * a.V]
+                          : 0.f;
 
     int64_t t0, t1;
     int s0, s1;
@@ -99,21 +103,32 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
     // re-read the last slice, and V slices past the chunk's last token re-read
     // its first token.  Straight-line loads let the compiler count them and
     // wait for exactly the oldest chunk instead of draining the queue.
+    // Per-lane parts of the addresses are fixed; only the chunk's base moves.
+    int64_t lane_off[L::PPL];
+    int lane_tok[L::PPL];
+    bool lane_rec[L::PPL];
+#pragma unroll
+    for (int j = 0; j < L::PPL; ++j) {
+        const int p = min(j * L::THREADS + tid, L::PIECES - 1);
+        lane_rec[j] = p < L::REC_PIECES;
+        const int q = max(p - L::REC_PIECES, 0);
+        lane_tok[j] = q / L::VPR;
+        lane_off[j] = lane_rec[j] ? (int64_t)p * 16
+                                  : ((int64_t)lane_tok[j] * vstride + (q % L::VPR) * 8) * 2;
+    }
     auto issue = [&](u32x4 (&dst)[L::PPL], int c) {
         c = min(c, nch - 1);
         const unsigned char* rec = rec_h + (int64_t)(s0 + c) * rec_stride;
         const int64_t start = t0 + (int64_t)C * c;
         const int nvalid = (int)min((int64_t)C, t1 - start);
+        const unsigned char* vb = reinterpret_cast<const unsigned char*>(vcol + start * vstride);
 #pragma unroll
         for (int j = 0; j < L::PPL; ++j) {
-            const int p = min(j * L::THREADS + tid, L::PIECES - 1);
-            const int q = max(p - L::REC_PIECES, 0);
-            int tok = q / L::VPR;
-            tok = tok < nvalid ? tok : 0;
-            const unsigned char* vaddr = reinterpret_cast<const unsigned char*>(
-                vcol + (start + tok) * vstride + (q % L::VPR) * 8);
-            const unsigned char* addr = p < L::REC_PIECES ? rec + p * 16 : vaddr;
-            dst[j] = *reinterpret_cast<const u32x4*>(addr);
+            // a V slice of a token past the end re-reads the chunk's first token
+            const int64_t off = (lane_rec[j] || lane_tok[j] < nvalid)
+                                    ? lane_off[j]
+                                    : lane_off[j] - (int64_t)lane_tok[j] * vstride * 2;
+            dst[j] = *reinterpret_cast<const u32x4*>((lane_rec[j] ? rec : vb) + off);
         }
     };
     // Slices past the end land in the buffer's padding.
@@ -123,8 +138,44 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
             *reinterpret_cast<u32x4*>(buf + (j * L::THREADS + tid) * 16) = src[j];
     };
 
-    // One chunk, every operand read from the LDS buffer.
-    auto compute = [&](const unsigned char* buf, int c) {
+    // A chunk's operands, read from its LDS buffer one chunk ahead of use.
+    struct Frags {
+        bf16x8 nkg[KS];
+        bf16x4 kdt[KT], aqk, tb;
+        float v[4];
+    };
+    auto read_frags = [&](Frags& f, const unsigned char* buf) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+            f.nkg[j] = *reinterpret_cast<const bf16x8*>(buf + R::NKG + (j * 64 + lane) * 16);
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            f.kdt[t] = *reinterpret_cast<const bf16x4*>(buf + R::KDT + (t * 64 + lane) * 8);
+        f.aqk = *reinterpret_cast<const bf16x4*>(buf + R::AQK + lane * 8);
+        f.tb = *reinterpret_cast<const bf16x4*>(buf + R::TB + lane * 8);
+        const uint16_t* vt = reinterpret_cast<const uint16_t*>(buf + L::V_OFF);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.v[i] = bf2f(vt[(4 * lg + i) * L::VCOLS + cw + lr]);
+    };
+
+    // QG and the decay Gam_C of the chunk being computed come from its buffer;
+    // they are read before the next chunk's operands so that waiting for them
+    // never waits for the prefetch (LDS reads complete in order).
+    struct Own {
+        bf16x8 qg[KS];
+        floatx4 gc[KT];
+    };
+    auto read_own = [&](Own& w, const unsigned char* buf) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+            w.qg[j] = *reinterpret_cast<const bf16x8*>(buf + R::QG + (j * 64 + lane) * 16);
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            w.gc[t] = *reinterpret_cast<const floatx4*>(buf + R::GAMC + (16 * t + 4 * lg) * 4);
+    };
+
+    // One chunk from register operands.
+    auto compute = [&](const Frags& f, const Own& w, int c) {
         const int64_t start = t0 + (int64_t)C * c;
         const int nvalid = (int)min((int64_t)C, t1 - start);
         // bf16 operand copy of the state: k-step j pairs tiles 2j and 2j+1
@@ -136,73 +187,65 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
                 sb[j][e] = (bf16)S[2 * j][e];
                 sb[j][4 + e] = (bf16)S[2 * j + 1][e];
             }
-        // decay the state now; the rank-C update accumulates onto it below
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const floatx4 gc =
-                *reinterpret_cast<const floatx4*>(buf + R::GAMC + (16 * t + 4 * lg) * 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[t][i] *= gc[i];
-        }
         floatx4 Y;
-        const uint16_t* vt = reinterpret_cast<const uint16_t*>(buf + L::V_OFF);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = 4 * lg + i;
-            Y[i] = tok < nvalid ? bf2f(vt[tok * L::VCOLS + cw + lr]) : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) Y[i] = (4 * lg + i < nvalid) ? f.v[i] : 0.f;
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            const bf16x8 nkg =
-                *reinterpret_cast<const bf16x8*>(buf + R::NKG + (j * 64 + lane) * 16);
-            Y = mfma32(nkg, sb[j], Y);  // V - KG S
-        }
+        for (int j = 0; j < KS; ++j) Y = mfma32(f.nkg[j], sb[j], Y);  // V - KG S
         floatx4 OT = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            const bf16x8 qg = *reinterpret_cast<const bf16x8*>(buf + R::QG + (j * 64 + lane) * 16);
-            OT = mfma32(sb[j], qg, OT);  // S^T QG^T
-        }
-        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-        const bf16x4 tb = *reinterpret_cast<const bf16x4*>(buf + R::TB + lane * 8);
-        const bf16x4 ub = to_bf16x4(mfma16(tb, to_bf16x4(Y), zero));  // U'
+        for (int j = 0; j < KS; ++j) OT = mfma32(sb[j], w.qg[j], OT);  // S^T QG^T
+        // decay the state; the rank-C update accumulates onto it
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const bf16x4 kdt =
-                *reinterpret_cast<const bf16x4*>(buf + R::KDT + (t * 64 + lane) * 8);
-            S[t] = mfma16(kdt, ub, S[t]);
-        }
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[t][i] *= w.gc[t][i];
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+        const bf16x4 ub = to_bf16x4(mfma16(f.tb, to_bf16x4(Y), zero));  // U'
+#pragma unroll
+        for (int t = 0; t < KT; ++t) S[t] = mfma16(f.kdt[t], ub, S[t]);
         // + U'^T Aqk^T, accumulated apart and added on the VALU: a 16x16x16 MFMA
         // must not take the result of a 16x16x32 MFMA as its accumulator input
         // (that dependent pair gave wrong sums on gfx950)
-        const bf16x4 aqk = *reinterpret_cast<const bf16x4*>(buf + R::AQK + lane * 8);
-        const floatx4 OI = mfma16(ub, aqk, zero);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) OT[i] += OI[i];
+        const floatx4 OI = mfma16(ub, f.aqk, zero);
         // OT[i] = O[token lr][column cb + cw + 4 lg + i]
         if (lr < nvalid) {
             bf16x4 ov;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ov[i] = (bf16)(a.scale * OT[i]);
+            for (int i = 0; i < 4; ++i) ov[i] = (bf16)(a.scale * (OT[i] + OI[i]));
             *reinterpret_cast<bf16x4*>(a.o + (start + lr) * vstride + (int64_t)h * a.V + cb + cw +
                                        4 * lg) = ov;
         }
     };
 
     if (nch > 0) {
-        // prologue: chunks 0 .. DEPTH-1 in flight, chunk 0 staged
+        // Pipeline, iteration c: chunk c + 2 + DEPTH loads into registers,
+        // chunk c + 2 is written to LDS buffer (c + 2) % 3, chunk c + 1's
+        // operands are read from buffer (c + 1) % 3 into registers, and chunk c
+        // computes (reading only its decay from buffer c % 3).  One barrier.
+        Frags fr[2];
         static_for<0, DEPTH>([&](auto d) { issue(ring[d], d); });
         commit(ring[0], stage[0]);
+        commit(ring[1 % DEPTH], stage[1]);
         __syncthreads();
         issue(ring[0], DEPTH);
+        issue(ring[1 % DEPTH], DEPTH + 1);
+        read_frags(fr[0], stage[0]);
+        int sc = 0;  // buffer of chunk c: c % 3
         for (int base = 0; base < nch; base += DEPTH) {
             static_for<0, DEPTH>([&](auto u) {
-                constexpr int nx = (u + 1) % DEPTH;  // ring slot of chunk c + 1
+                constexpr int nx2 = (u + 2) % DEPTH;  // ring slot of chunk c + 2
+                constexpr int cur = u & 1;            // DEPTH is even
                 const int c = base + u;
-                commit(ring[nx], stage[(c + 1) & 1]);
-                issue(ring[nx], c + 1 + DEPTH);
-                if (c < nch) compute(stage[c & 1], c);  // uniform over the workgroup
+                const int s1b = sc == 2 ? 0 : sc + 1, s2b = sc == 0 ? 2 : sc - 1;
+                Own own;
+                read_own(own, stage[sc]);        // chunk c
+                commit(ring[nx2], stage[s2b]);  // chunk c + 2
+                issue(ring[nx2], c + 2 + DEPTH);
+                read_frags(fr[cur ^ 1], stage[s1b]);  // chunk c + 1
+                if (c < nch) compute(fr[cur], own, c);  // uniform over the workgroup
                 __syncthreads();
+                sc = s1b;
             });
         }
     }
@@ -212,7 +255,7 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
         for (int t = 0; t < KT; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                a.final_state[st + (int64_t)(16 * t + 4 * lg + i) * a.V] = S[t][i];
+                a.final_state[st + (int64_t)tile_channel(t, 4 * lg + i) * a.V] = S[t][i];
     }
 }
 
@@ -221,7 +264,7 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
 #define KDA_RECUR_WAVES 4
 #endif
 #ifndef KDA_RECUR_DEPTH
-#define KDA_RECUR_DEPTH 8
+#define KDA_RECUR_DEPTH 4
 #endif
 constexpr int RECUR_WAVES = KDA_RECUR_WAVES;
 constexpr int RECUR_DEPTH = KDA_RECUR_DEPTH;

@@ -47,8 +47,8 @@
  *    written).  An empty sequence returns its initial state.
  *  - Only K, V in {64, 128} are supported.  B * T must be < 2^31.  Token
  *    tensors (q, k, v, g, beta, o) may be NULL only when T == 0.
- *  - Alignment: q, k, g (KDA), o at least 8 bytes; dt_bias 16 bytes;
- *    workspace 256 bytes.
+ *  - Alignment: q, k, v, g (KDA), dt_bias 16 bytes; o 8 bytes; workspace
+ *    256 bytes.
  *  - Ownership: the caller allocates and frees every buffer, including the
  *    workspace (at least *_workspace_size() bytes).  The library allocates
  *    nothing, keeps no pointer after it returns and never synchronises.
