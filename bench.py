@@ -30,7 +30,7 @@ ROOT = Path(__file__).resolve().parent
 METRIC = "chunk_kda fwd tokens/sec, B2 T2048 H32 K=V=128; HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-C = 16
+C = 32  # tokens per chunk (two 16-token blocks)
 
 
 def source_digest() -> str:
@@ -42,8 +42,9 @@ def source_digest() -> str:
 
 
 def algorithmic_bytes(B, T, H, K, V, N, init=True, final=True):
-    """Compulsory HBM bytes of the method and of each kernel (K=V=128 record of
-    13824 B per (chunk, head)), for T a multiple of the chunk."""
+    """Compulsory HBM bytes of the method and of each kernel, for T a multiple of
+    the chunk.  The per-(chunk, head) record holds nKG, QG and KdT (C x K bf16
+    each), Aqk and Tb (C x C bf16 each) and Gamma_C (K fp32): 29184 B at K = 128."""
     th = B * T * H
     states = N * H * K * V * 4 * ((1 if init else 0) + (1 if final else 0))
     rec_per_th = (3 * C * K * 2 + 2 * C * C * 2 + K * 4) / C

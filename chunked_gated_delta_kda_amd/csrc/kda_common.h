@@ -13,12 +13,26 @@
 
 namespace kda {
 
-// Tokens per chunk.  The FlashKDA summary (discuss.pytorch.kr, section
-// "Flash Linear Attention과 비교") motivates 16: the 16x16 intra-chunk inverse is
-// cheap, and with the gate floored at -5 a 16-token cumulative decay stays
-// within 16*5 = 80 < ln(FLT_MAX) ~ 88.7, so the factored decays exp(+-G) fit
-// the fp32/bf16 exponent range without intra-chunk rescaling.
-constexpr int C = 16;
+// Tokens per chunk: C = 16 NB, processed as NB blocks of 16 tokens.
+// The FlashKDA summary (discuss.pytorch.kr, section "Flash Linear Attention과
+// 비교") motivates the 16-token block: with the gate floored at -5 a 16-token
+// cumulative decay stays within 16*5 = 80 < ln(FLT_MAX) ~ 88.7, so the
+// factored in-block decays exp(+-G) fit the fp32/bf16 exponent range without
+// rescaling, and the 16x16 inverse is cheap.  Larger chunks (FLA's default is
+// 64) need the rescaling that page mentions; here it is per 16-token block:
+// every cross-block product is formed from two factors that are both <= 1
+// (decay from the earlier block's end), and the chunk's (I + A)^-1 is block
+// lower triangular.  NB = 2 halves the sequential steps of the recurrence
+// and lets its state update run on full-rate 16x16x32 MFMA.
+#ifndef KDA_CHUNK_BLOCKS
+#define KDA_CHUNK_BLOCKS 2
+#endif
+constexpr int NB = KDA_CHUNK_BLOCKS;
+static_assert(NB == 1 || NB == 2, "chunks of 16 or 32 tokens");
+constexpr int C = 16 * NB;
+// elements per lane of an operand that contracts over the chunk's tokens:
+// token k-slot (g, e) of such an operand is 16 (e / 4) + 4 g + (e % 4)
+constexpr int EL = 4 * NB;
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -47,6 +61,17 @@ __device__ __forceinline__ floatx4 mfma32(bf16x8 a, bf16x8 b, floatx4 c) {
 __device__ __forceinline__ floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
                                                      __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+}
+
+// Operand that contracts over the chunk's tokens: EL bf16 per lane.
+typedef __attribute__((ext_vector_type(EL))) __bf16 bf16xEL;
+// D += A B over the C tokens: 16x16x16 for one block, 16x16x32 for two.
+__device__ __forceinline__ floatx4 mfma_tok(bf16xEL a, bf16xEL b, floatx4 c) {
+#if KDA_CHUNK_BLOCKS == 1
+    return mfma16(a, b, c);
+#else
+    return mfma32(a, b, c);
+#endif
 }
 
 __device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) {
@@ -90,22 +115,25 @@ __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uin
 // Per (chunk slot, head) record written by kda_prep and read by kda_recur.
 // All matrices are stored in the exact per-lane order of the MFMA operand
 // that consumes them, so kda_recur reads each fragment with one 8- or
-// 16-byte load per lane and the whole record is one contiguous stream.
+// 16-byte access per lane and the whole record is one contiguous stream.
 //
-// Within a chunk of C = 16 tokens (row r), G[r][c] = sum_{s<=r} log a_s[c] and
-// Gam = exp(G):
-//   nKG  = -(k^ * Gam)         [16 x K]  A operand of 16x16x32 against S
-//   QG   =   q^ * Gam          [16 x K]  B operand of 16x16x32 against S^T
-//   KdT  = (k^ * Gam_C / Gam)^T[K x 16]  A operand of 16x16x16 against U',
-//                                        one 16-channel state tile at a time
-//   Aqk  = tril(QG (k^/Gam)^T) [16 x 16] B operand (transposed) for O^T
-//   Tb   = (I + A)^-1 diag(b)  [16 x 16] A operand for U' = Tb (V - KG S)
-//   GamC = Gam at the chunk's last row, fp32 [K] in tile-channel order
+// Within a chunk (token r), G[r][c] = sum_{s<=r} log a_s[c] and Gam = exp(G):
+//   nKG  = -(k^ * Gam)           [C x K]  per 16-token block: A operand of
+//                                         16x16x32 against S
+//   QG   =   q^ * Gam            [C x K]  per block: B operand against S^T
+//   KdT  = (k^ * Gam_C / Gam)^T  [K x C]  per 16-channel state tile: A operand
+//                                         contracting over the C tokens
+//   Aqk  = tril(QG (k^/Gam)^T)   [C x C]  per 16-token output block: B operand
+//                                         (transposed) contracting over tokens
+//   Tb   = (I + A)^-1 diag(b)    [C x C]  per 16-token row block: A operand of
+//                                         U' = Tb (V - KG S)
+//   GamC = Gam at the chunk's last token, fp32 [K] in tile-channel order
 // with A[r][j] = b_r sum_c (k^ Gam)[r][c] (k^/Gam)[j][c] for j < r.
-//
-// Channel orders.  Inside a 16x16x32 fragment, k-step j, lane group g and
-// element e hold channel 32 j + 8 g + e (8 contiguous channels per lane, so
-// prep loads and stores them as 16-byte vectors).  kda_recur keeps the state
+// Token k-slots follow EL above; channel orders follow below.
+// Channel orders.  Inside a 16x16x32 fragment that contracts over channels,
+// k-step j, lane group g and element e hold channel 32 j + 8 g + e (8
+// contiguous channels per lane, so prep loads and stores them as 16-byte
+// vectors).  kda_recur keeps the state
 // as K/16 tiles of 16 channels in MFMA D layout (lane group g holds tile rows
 // 4g..4g+3); tile t, row r holds channel
 //   rho(t, r) = 32 (t / 2) + 8 (r / 4) + 4 (t % 2) + (r % 4),
@@ -115,15 +143,17 @@ __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uin
 // movement.  KdT and GamC are stored in tile order.
 template <int K>
 struct Rec {
-    static constexpr int KSTEPS = K / 32;               // 16x16x32 k-steps
-    static constexpr int KTILES = K / 16;               // 16-row state tiles
-    static constexpr int NKG = 0;                       // bf16 [KSTEPS][4][16][8]
-    static constexpr int QG = NKG + C * K * 2;          // bf16 [KSTEPS][4][16][8]
-    static constexpr int KDT = QG + C * K * 2;          // bf16 [KTILES][4][16][4]:
-                                                        //   [t][g][m][i] = Kd[4g+i][rho(t,m)]
-    static constexpr int AQK = KDT + C * K * 2;         // bf16 [4][16][4]
-    static constexpr int TB = AQK + C * C * 2;          // bf16 [4][16][4]
-    static constexpr int GAMC = TB + C * C * 2;         // fp32 [K]: [t][r] = Gam_C[rho(t,r)]
+    static constexpr int KSTEPS = K / 32;      // 16x16x32 k-steps over channels
+    static constexpr int KTILES = K / 16;      // 16-channel state tiles
+    static constexpr int NKG = 0;              // bf16 [NB][KSTEPS][4][16][8]
+    static constexpr int QG = NKG + C * K * 2; // bf16 [NB][KSTEPS][4][16][8]
+    static constexpr int KDT = QG + C * K * 2; // bf16 [KTILES][4][16][EL]:
+                                               //   [t][g][m][e] = Kd[tok(g,e)][rho(t,m)]
+    static constexpr int AQK = KDT + C * K * 2;  // bf16 [NB][4][16][EL]:
+                                                 //   [a][g][n][e] = Aqk[16a+n][tok(g,e)]
+    static constexpr int TB = AQK + C * C * 2;   // bf16 [NB][4][16][EL]:
+                                                 //   [b][g][m][e] = Tb[16b+m][tok(g,e)]
+    static constexpr int GAMC = TB + C * C * 2;  // fp32 [K]: [t][r] = Gam_C[rho(t,r)]
     static constexpr int BYTES = GAMC + K * 4;
 };
 

@@ -19,24 +19,29 @@
 
 namespace kda {
 
-// One wave per (16-token chunk, head).  Lane l = m + 16 g owns token row m
-// of the chunk and, for every k-step j, the 8 contiguous channels
-// 32 j + 8 g .. +7: exactly the row-m slice of a 16x16x32 MFMA fragment.
-// Every intra-chunk product therefore reads its operands straight from
-// registers, the q/k/g loads and the nKG/QG record stores are 16-byte
-// vectors, and the wave needs no barrier.
+// One workgroup per (chunk, head) with one wave per 16-token block.  Lane
+// l = m + 16 g of wave b owns token row 16 b + m of the chunk and, for every
+// k-step j, the 8 contiguous channels 32 j + 8 g .. +7: exactly the row-m
+// slice of a 16x16x32 MFMA fragment.  Every intra-block product therefore
+// reads its operands straight from registers, and the q/k/g loads and the
+// nKG/QG record stores are 16-byte vectors.
 //
 //  - gate:   log2 a = max(lb, -exp(A_log[h]) softplus(g + dt_bias)) log2(e)
-//  - cumsum: inclusive prefix over the 16 rows = 16-lane DPP row scan
+//  - cumsum: inclusive prefix over a block's 16 rows = 16-lane DPP row scan;
+//            block totals are exchanged through LDS
 //  - norms:  sum of squares over the 4 lane groups of a row (2 xor shuffles)
-//  - A, A^T, Aqk^T: bf16 MFMA over K on the fragments
-//  - (I + A)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8), N = -A, exact because
-//    A is strictly lower triangular (A^16 = 0).  With the MFMA primitive
-//    M(P, Q) = P^T Q on D-layout operands (the D layout of P read as an A
-//    operand is P^T), every matrix is kept together with its transpose, so
-//    no product needs a layout change.  Operands are fp16 (|N| <= 1 and the
-//    powers stay far below the fp16 range for a 16 x 16 triangle), products
-//    accumulate in fp32.
+//  - in-block A, A^T, Aqk^T: bf16 MFMA over K with the factored decays
+//            (k^ Gam)(k^/Gam)^T, exact in range because |G| <= 80 in a block
+//            (GDN: products of k^, q^ times exp(G_r - G_j) <= 1 per element)
+//  - cross-block A10, Aqk10^T (two blocks): (k^ Gam_loc1)(k^ Gam_end0/Gam0)^T,
+//            both factors <= 1
+//  - (I + A)^-1 per block = (I + N)(I + N^2)(I + N^4)(I + N^8), N = -A,
+//    exact because A is strictly lower triangular (A^16 = 0).  With the MFMA
+//    primitive M(P, Q) = P^T Q on D-layout operands (the D layout of P read as
+//    an A operand is P^T), every matrix is kept together with its transpose,
+//    so no product needs a layout change.  Operands are fp16 (|N| <= 1 and
+//    its powers stay far below the fp16 range for a 16 x 16 triangle),
+//    products accumulate in fp32.  Two blocks: T10 = -T11 A10 T00.
 namespace {
 
 constexpr int ROW_SHR1 = 0x111, ROW_SHR2 = 0x112, ROW_SHR4 = 0x114, ROW_SHR8 = 0x118;
@@ -91,23 +96,39 @@ __device__ __forceinline__ bf16x8 pack8(const float* f, float s = 1.f) {
     return r;
 }
 
+// One token-contraction operand from two 4-element halves (block 0, block 1).
+__device__ __forceinline__ bf16xEL pack_tok(floatx4 lo, floatx4 hi) {
+    bf16xEL r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = (bf16)lo[i];
+        if constexpr (NB == 2) r[4 + i] = (bf16)hi[i];
+    }
+    return r;
+}
+
 }  // namespace
 
 template <int K, bool GDN>
-__global__ __launch_bounds__(64) void kda_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     constexpr int KS = K / 32;  // 16-byte channel slices per lane
     using R = Rec<K>;
-    __shared__ __attribute__((aligned(16))) uint16_t kdt_s[C * K];  // KdT transpose
+    __shared__ __attribute__((aligned(16))) uint16_t kdt_s[C * K];   // KdT transpose
+    __shared__ __attribute__((aligned(16))) float gend_s[NB][K];     // block log2-decay totals
+    __shared__ __attribute__((aligned(16))) bf16x8 kd0_s[NB == 2 ? KS * 64 : 1];  // block 0
+    __shared__ __attribute__((aligned(16))) floatx4 t00_s[64];       // block 0's T, D layout
+    __shared__ float beta0_s[16];
 
     const int slot = blockIdx.x;
     const int h = blockIdx.y;
-    const int L = threadIdx.x, m = L & 15, g = L >> 4;
+    const int blk = threadIdx.x >> 6;  // this wave's 16-token block
+    const int L = threadIdx.x & 63, m = L & 15, g = L >> 4;
 
     // ---- locate the chunk: sequence n with chunk_off[n] <= slot < chunk_off[n+1]
     int n;
     if (!a.packed) {
         n = slot / ((a.T + C - 1) / C);  // launched only when T > 0
-        if (n >= a.n_seqs) return;
+        if (n >= a.n_seqs) return;       // uniform over the workgroup
     } else {
         if (slot >= a.chunk_off[a.n_seqs]) return;
         int lo = 0, hi = a.n_seqs;  // invariant: chunk_off[lo] <= slot < chunk_off[hi]
@@ -120,15 +141,15 @@ __global__ __launch_bounds__(64) void kda_prep_kernel(PrepArgs a) {
     int64_t t0, t1;
     int s0, s1;
     seq_span(a, n, t0, t1, s0, s1);
-    const int64_t start = t0 + (int64_t)C * (slot - s0);
-    const int nvalid = (int)min((int64_t)C, t1 - start);
-    const bool valid = m < nvalid;
-    const int64_t row = (start + m) * a.H + h;  // flattened (token, head) row
+    const int64_t start = t0 + (int64_t)C * (slot - s0);  // first token of the chunk
+    const int nvalid = (int)min((int64_t)C, t1 - start);   // >= 1
+    const int row_in_chunk = 16 * blk + m;
+    const bool valid = row_in_chunk < nvalid;
 
     // ---- every global load up front, from an always-valid row (padding rows
     // re-read the chunk's first row and are zeroed by value), so the wave
     // waits for memory once; q, k, g stay packed bf16 until their slice is used
-    const int64_t lrow = (start + (valid ? m : 0)) * a.H + h;
+    const int64_t lrow = (start + (valid ? row_in_chunk : 0)) * a.H + h;
     u32x4 qr[KS], kr[KS], gr[KS];
     floatx4 dtr[KS][2];
 #pragma unroll
@@ -153,7 +174,6 @@ __global__ __launch_bounds__(64) void kda_prep_kernel(PrepArgs a) {
     }
     // beta: KDA logits through the sigmoid, GDN probabilities as given; 0 on padding
     const float b = valid ? (GDN ? braw : sigmoid_f(braw)) : 0.f;
-    const float la_row = valid ? graw * LOG2E : 0.f;
 
     // ---- L2 norms: a row's channels live in lanes m, m+16, m+32, m+48
     float sq = 0.f, sk = 0.f;
@@ -171,19 +191,41 @@ __global__ __launch_bounds__(64) void kda_prep_kernel(PrepArgs a) {
     sk += __shfl_xor(sk, 32, 64);
     const float iq = rsq_hw(sq + NORM_EPS), ik = rsq_hw(sk + NORM_EPS);
 
-    // GDN: in-chunk inclusive prefix of the scalar log2 decay, and its total
-    float G_row = 0.f, GC_row = 0.f;
+    // ---- in-block inclusive prefix sums of the log2 decay (padding rows add 0)
+    float G[KS][8];  // KDA: per channel; GDN uses G[0][0] as the row's value
     if constexpr (GDN) {
-        G_row = row_scan16(la_row);
-        GC_row = lane_val(G_row, 15 + 16 * g);
+        G[0][0] = row_scan16(valid ? graw * LOG2E : 0.f);
+        if (m == 15 && g == 0) gend_s[blk][0] = G[0][0];
+    } else {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            float x[8];
+            unpack8(gr[j], x);
+            const floatx4 d0 = dtr[j][0], d1 = dtr[j][1];
+            const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float la =
+                    valid ? fmaxf(a.lower_bound, -rate * softplus_f(x[e] + dv[e])) * LOG2E : 0.f;
+                G[j][e] = row_scan16(la);
+            }
+            if (m == 15) {  // the block total of these channels
+                const floatx4 lo = {G[j][0], G[j][1], G[j][2], G[j][3]};
+                const floatx4 hi = {G[j][4], G[j][5], G[j][6], G[j][7]};
+                *reinterpret_cast<floatx4*>(&gend_s[blk][32 * j + 8 * g]) = lo;
+                *reinterpret_cast<floatx4*>(&gend_s[blk][32 * j + 8 * g + 4]) = hi;
+            }
+        }
     }
+    __syncthreads();
 
-    // ---- one 8-channel slice at a time: gate, prefix sum over the 16 rows
-    // (a 16-lane DPP scan), decay factors, record pieces, and this slice's
-    // contribution to the intra-chunk products.  mfma32(X, Y) gives D = X Y^T:
-    // lane (n, g) holds element i of D at row 4g + i, column n.
+    // ---- decay factors, record fragments, in-block (and cross-block) products.
+    // mfma32(X, Y) gives D = X Y^T: lane (n, g) holds element i of D at row
+    // 4g + i, column n.
     unsigned char* rec = a.rec + ((int64_t)slot * a.H + h) * R::BYTES;
-    floatx4 dA = {0.f, 0.f, 0.f, 0.f}, dAT = dA, dQT = dA;
+    floatx4 dA = {0.f, 0.f, 0.f, 0.f}, dAT = dA, dQT = dA, dX = dA, dXQT = dA;
+    bf16x8 kgl_f[KS], qgl_f[KS];  // block 1's local KG and QG (cross-block products)
+    float gcv[KS][8];             // Gam_C per channel (written by one row)
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
         float qn[8], kn[8];
@@ -191,94 +233,113 @@ __global__ __launch_bounds__(64) void kda_prep_kernel(PrepArgs a) {
         unpack8(kr[j], kn);
 #pragma unroll
         for (int e = 0; e < 8; ++e) { qn[e] *= iq; kn[e] *= ik; }
-        float kgv[8], qgv[8], kiv[8], kd[8], gamc[8];
-        if constexpr (GDN) {
-            const float gam = exp2_hw(G_row), gkd = exp2_hw(GC_row - G_row), gc = exp2_hw(GC_row);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kgv[e] = kn[e] * gam;
-                qgv[e] = qn[e] * gam;
-                kd[e] = kn[e] * gkd;
-                gamc[e] = gc;
-            }
-        } else {
-            float x[8];
-            unpack8(gr[j], x);
-            const floatx4 d0 = dtr[j][0], d1 = dtr[j][1];
-            const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // padding rows keep log decay 0 (decay 1)
-                const float la =
-                    valid ? fmaxf(a.lower_bound, -rate * softplus_f(x[e] + dv[e])) * LOG2E : 0.f;
-                const float G = row_scan16(la);
-                const float GC = lane_val(G, 15 + 16 * g);
-                const float gam = exp2_hw(G);
-                kgv[e] = kn[e] * gam;
-                qgv[e] = qn[e] * gam;
-                kiv[e] = kn[e] * exp2_hw(-G);
-                kd[e] = kn[e] * exp2_hw(GC - G);
-                gamc[e] = gam;  // row 15 holds Gam_C
-            }
-        }
-        *reinterpret_cast<bf16x8*>(rec + R::NKG + (j * 64 + L) * 16) = pack8(kgv, -1.f);
-        *reinterpret_cast<bf16x8*>(rec + R::QG + (j * 64 + L) * 16) = pack8(qgv);
-        // GamC in tile order: channel 32 j + 8 g + e is tile 2j + e/4, row 4g + e%4
-        if (m == C - 1) {
-            float* gp = reinterpret_cast<float*>(rec + R::GAMC);
-            const floatx4 lo = {gamc[0], gamc[1], gamc[2], gamc[3]};
-            const floatx4 hi = {gamc[4], gamc[5], gamc[6], gamc[7]};
-            *reinterpret_cast<floatx4*>(gp + 32 * j + 4 * g) = lo;
-            *reinterpret_cast<floatx4*>(gp + 32 * j + 16 + 4 * g) = hi;
-        }
-        // KdT[t][g'][m'][i'] = Kd[token 4g'+i'][rho(t, m')]: transposed through LDS
+        float gown[8], goth[8];  // this block's and the other block's totals
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int t = 2 * j + (e >> 2), r = 4 * g + (e & 3);
-            kdt_s[((t * 4 + (m >> 2)) * 16 + r) * 4 + (m & 3)] =
+            const int c = GDN ? 0 : 32 * j + 8 * g + e;
+            gown[e] = gend_s[blk][c];
+            goth[e] = NB == 2 ? gend_s[1 - blk][c] : 0.f;
+        }
+        float kg[8], qg[8], kgl[8], qgl[8], kil[8], kdl[8], kd[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float Gl = GDN ? G[0][0] : G[j][e];
+            const float gl = exp2_hw(Gl);
+            kgl[e] = kn[e] * gl;                       // block-local Gam
+            qgl[e] = qn[e] * gl;
+            kil[e] = GDN ? kn[e] : kn[e] * exp2_hw(-Gl);
+            kdl[e] = kn[e] * exp2_hw(gown[e] - Gl);   // decay to the block's end
+            // global factors: block 1 carries block 0's total decay, block 0's Kd
+            // carries block 1's
+            const float before = (NB == 2 && blk == 1) ? exp2_hw(goth[e]) : 1.f;
+            const float after = (NB == 2 && blk == 0) ? exp2_hw(goth[e]) : 1.f;
+            kg[e] = kgl[e] * before;
+            qg[e] = qgl[e] * before;
+            kd[e] = kdl[e] * after;
+            gcv[j][e] = exp2_hw(gown[e] + goth[e]);
+        }
+        *reinterpret_cast<bf16x8*>(rec + R::NKG + ((blk * KS + j) * 64 + L) * 16) = pack8(kg, -1.f);
+        *reinterpret_cast<bf16x8*>(rec + R::QG + ((blk * KS + j) * 64 + L) * 16) = pack8(qg);
+        // KdT[t][g'][m'][e'] = Kd[tok(g', e')][rho(t, m')]: transposed through LDS
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = 2 * j + (e >> 2), mm = 4 * g + (e & 3);
+            const int ee = 4 * blk + (m & 3);
+            kdt_s[((t * 4 + (m >> 2)) * 16 + mm) * EL + ee] =
                 __builtin_bit_cast(uint16_t, (bf16)kd[e]);
         }
+        const bf16x8 kglf = pack8(kgl), qglf = pack8(qgl);
         if constexpr (GDN) {
-            // the intra-chunk products use k^ and q^; the decay is applied per element
+            // in-block products of k^ and q^; the decay is applied per element
             const bf16x8 kf = pack8(kn), qf = pack8(qn);
             dA = mfma32(kf, kf, dA);
             dQT = mfma32(kf, qf, dQT);
         } else {
-            const bf16x8 kgf = pack8(kgv), kif = pack8(kiv), qgf = pack8(qgv);
-            dA = mfma32(kgf, kif, dA);    // KG KiG^T
-            dAT = mfma32(kif, kgf, dAT);  // KiG KG^T
-            dQT = mfma32(kif, qgf, dQT);  // KiG QG^T = Aqk^T
+            const bf16x8 kif = pack8(kil);
+            dA = mfma32(kglf, kif, dA);    // KG KiG^T
+            dAT = mfma32(kif, kglf, dAT);  // KiG KG^T
+            dQT = mfma32(kif, qglf, dQT);  // KiG QG^T = Aqk^T
+        }
+        if constexpr (NB == 2) {
+            if (blk == 0) kd0_s[j * 64 + L] = pack8(kdl);
+            kgl_f[j] = kglf;
+            qgl_f[j] = qglf;
         }
     }
     if constexpr (GDN) dAT = dA;  // k^ k^T is symmetric
-
-    __syncthreads();
+    // Gam_C, tile order: channel 32 j + 8 g + e is tile 2j + e/4, row 4g + e%4
+    if (blk == 0 && m == 15) {
+        float* gp = reinterpret_cast<float*>(rec + R::GAMC);
 #pragma unroll
-    for (int p = 0; p < C * K * 2 / (64 * 16); ++p)
-        *reinterpret_cast<u32x4*>(rec + R::KDT + (p * 64 + L) * 16) =
-            *reinterpret_cast<const u32x4*>(kdt_s + (p * 64 + L) * 8);
+        for (int j = 0; j < KS; ++j) {
+            const floatx4 lo = {gcv[j][0], gcv[j][1], gcv[j][2], gcv[j][3]};
+            const floatx4 hi = {gcv[j][4], gcv[j][5], gcv[j][6], gcv[j][7]};
+            *reinterpret_cast<floatx4*>(gp + 32 * j + 4 * g) = lo;
+            *reinterpret_cast<floatx4*>(gp + 32 * j + 16 + 4 * g) = hi;
+        }
+    }
+    if (blk == 0 && g == 0) beta0_s[m] = b;
+    __syncthreads();
 
-    float br[4], Gr[4];  // beta and (GDN) log decay of rows 4g .. 4g+3
+    // KdT out, 16 bytes per lane per step
+#pragma unroll
+    for (int p = 0; p < C * K * 2 / (64 * NB * 16); ++p) {
+        const int off = (p * 64 * NB + threadIdx.x) * 16;
+        *reinterpret_cast<u32x4*>(rec + R::KDT + off) =
+            *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(kdt_s) + off);
+    }
+    if constexpr (NB == 2) {
+        if (blk == 1) {
+            // A10 = diag(b1) KG1loc Kd0loc^T and Aqk10^T = Kd0loc QG1loc^T
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                const bf16x8 kd0 = kd0_s[j * 64 + L];  // row m of block 0, as operand
+                dX = mfma32(kgl_f[j], kd0, dX);
+                dXQT = mfma32(kd0, qgl_f[j], dXQT);
+            }
+        }
+    }
+
+    // ---- masks, the in-block N, N^T and Aqk
+    float br[4], Gr[4];  // beta and (GDN) prefix log decay of rows 4g .. 4g+3
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         br[i] = lane_val(b, 4 * g + i);
-        if constexpr (GDN) Gr[i] = lane_val(G_row, 4 * g + i);
+        if constexpr (GDN) Gr[i] = lane_val(G[0][0], 4 * g + i);
     }
-    floatx4 N, NT;
-    bf16x4 aqk;
+    floatx4 N, NT, aq;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;  // this element's row; its column is m
         float dec_rm = 1.f, dec_mr = 1.f;
         if constexpr (GDN) {
-            dec_rm = r > m ? exp2_hw(Gr[i] - G_row) : 0.f;  // exp(G_r - G_m), r > m
-            dec_mr = m >= r ? exp2_hw(G_row - Gr[i]) : 0.f;  // exp(G_m - G_r), m >= r
+            dec_rm = r > m ? exp2_hw(Gr[i] - G[0][0]) : 0.f;   // exp(G_r - G_m), r > m
+            dec_mr = m >= r ? exp2_hw(G[0][0] - Gr[i]) : 0.f;  // exp(G_m - G_r), m >= r
         }
-        N[i] = m < r ? -br[i] * dA[i] * dec_rm : 0.f;          // N[r][m], m < r
-        NT[i] = r < m ? -b * dAT[i] * dec_mr : 0.f;            // N^T[r][m] = N[m][r], r < m
-        aqk[i] = (bf16)(r <= m ? dQT[i] * dec_mr : 0.f);     // Aqk[m][r], r <= m
+        N[i] = m < r ? -br[i] * dA[i] * dec_rm : 0.f;  // N[r][m], m < r
+        NT[i] = r < m ? -b * dAT[i] * dec_mr : 0.f;    // N^T[r][m] = N[m][r], r < m
+        aq[i] = r <= m ? dQT[i] * dec_mr : 0.f;        // Aqk[m][r], r <= m
     }
-    *reinterpret_cast<bf16x4*>(rec + R::AQK + L * 8) = aqk;
 
     // ---- T^T = ((I + N)(I + N^2)(I + N^4)(I + N^8))^T by transposed products
     const floatx4 N2 = mt(NT, N), N2T = mt(N, NT);
@@ -290,11 +351,41 @@ __global__ __launch_bounds__(64) void kda_prep_kernel(PrepArgs a) {
     const floatx4 P1T = add4(add4(I4, NT), add4(N2T, mt(N2, NT)));  // (I + N + N^2 + N^3)^T
     const floatx4 P2T = add4(P1T, mt(N4, P1T));                     // (P1 (I + N^4))^T
     const floatx4 TT = add4(P2T, mt(N8, P2T));                      // (P2 (I + N^8))^T
-    // Tb = T diag(b): the record holds Tb[m][4g + i] = (diag(b) T^T)[4g + i][m]
-    bf16x4 tb;
+    if constexpr (NB == 2) {
+        if (blk == 0) {
+            // T itself for the coupling block: T = P2 + P2 N^8 with P2 = P1 + P1 N^4
+            const floatx4 P1 = add4(add4(I4, N), add4(N2, mt(NT, N2)));
+            const floatx4 P2 = add4(P1, mt(P1T, N4));
+            t00_s[L] = add4(P2, mt(P2T, N8));
+        }
+    }
+
+    // ---- records Aqk (output block blk) and Tb (row block blk)
+    floatx4 aq_lo = aq, aq_hi = {0.f, 0.f, 0.f, 0.f};
+    floatx4 tb_lo, tb_hi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tb[i] = (bf16)(br[i] * TT[i]);
-    *reinterpret_cast<bf16x4*>(rec + R::TB + L * 8) = tb;
+    for (int i = 0; i < 4; ++i) tb_lo[i] = br[i] * TT[i];  // Tb[m][4g+i] = T[m][4g+i] b_{4g+i}
+    if constexpr (NB == 2) {
+        __syncthreads();  // T00 and the block-0 betas are in LDS
+        if (blk == 1) {
+            // T10^T = -T00^T A10^T T11^T = -M(T00, M(A10, T11^T))
+            floatx4 A10;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) A10[i] = br[i] * dX[i];  // A10[r][j] = b1_r (...)
+            const floatx4 Z = mt(A10, TT);
+            const floatx4 T10T = mt(t00_s[L], Z);
+            // row block 1: columns of block 0 then block 1
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                tb_hi[i] = tb_lo[i];                              // Tb11
+                tb_lo[i] = -beta0_s[4 * g + i] * T10T[i];         // Tb10
+                aq_hi[i] = aq[i];                                 // Aqk11
+                aq_lo[i] = dXQT[i];                               // Aqk10 (all j < r)
+            }
+        }
+    }
+    *reinterpret_cast<bf16xEL*>(rec + R::AQK + (blk * 64 + L) * (2 * EL)) = pack_tok(aq_lo, aq_hi);
+    *reinterpret_cast<bf16xEL*>(rec + R::TB + (blk * 64 + L) * (2 * EL)) = pack_tok(tb_lo, tb_hi);
 }
 
 // Sequence table: seq_start[0..N] (flattened token offsets) and
@@ -357,7 +448,8 @@ void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t tota
 
 template <int K, bool GDN>
 void launch_prep_t(const PrepArgs& a, int n_slots, hipStream_t stream) {
-    hipLaunchKernelGGL((kda_prep_kernel<K, GDN>), dim3(n_slots, a.H), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((kda_prep_kernel<K, GDN>), dim3(n_slots, a.H), dim3(64 * NB), 0, stream,
+                       a);
 }
 
 void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream) {

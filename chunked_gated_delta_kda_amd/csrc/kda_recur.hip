@@ -138,44 +138,23 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
             *reinterpret_cast<u32x4*>(buf + (j * L::THREADS + tid) * 16) = src[j];
     };
 
-    // A chunk's operands, read from its LDS buffer one chunk ahead of use.
+    // nKG, the first operand on the state's critical path, is read from the
+    // chunk's LDS buffer one chunk ahead of use; everything else is read from
+    // the chunk's own buffer while its products run.
     struct Frags {
-        bf16x8 nkg[KS];
-        bf16x4 kdt[KT], aqk, tb;
-        float v[4];
+        bf16x8 nkg[NB][KS];
     };
     auto read_frags = [&](Frags& f, const unsigned char* buf) {
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
-            f.nkg[j] = *reinterpret_cast<const bf16x8*>(buf + R::NKG + (j * 64 + lane) * 16);
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
-            f.kdt[t] = *reinterpret_cast<const bf16x4*>(buf + R::KDT + (t * 64 + lane) * 8);
-        f.aqk = *reinterpret_cast<const bf16x4*>(buf + R::AQK + lane * 8);
-        f.tb = *reinterpret_cast<const bf16x4*>(buf + R::TB + lane * 8);
-        const uint16_t* vt = reinterpret_cast<const uint16_t*>(buf + L::V_OFF);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f.v[i] = bf2f(vt[(4 * lg + i) * L::VCOLS + cw + lr]);
+            for (int j = 0; j < KS; ++j)
+                f.nkg[b][j] = *reinterpret_cast<const bf16x8*>(
+                    buf + R::NKG + ((b * KS + j) * 64 + lane) * 16);
     };
 
-    // QG and the decay Gam_C of the chunk being computed come from its buffer;
-    // they are read before the next chunk's operands so that waiting for them
-    // never waits for the prefetch (LDS reads complete in order).
-    struct Own {
-        bf16x8 qg[KS];
-        floatx4 gc[KT];
-    };
-    auto read_own = [&](Own& w, const unsigned char* buf) {
-#pragma unroll
-        for (int j = 0; j < KS; ++j)
-            w.qg[j] = *reinterpret_cast<const bf16x8*>(buf + R::QG + (j * 64 + lane) * 16);
-#pragma unroll
-        for (int t = 0; t < KT; ++t)
-            w.gc[t] = *reinterpret_cast<const floatx4*>(buf + R::GAMC + (16 * t + 4 * lg) * 4);
-    };
-
-    // One chunk from register operands.
-    auto compute = [&](const Frags& f, const Own& w, int c) {
+    // One chunk: nKG from registers, the rest from the chunk's buffer.
+    auto compute = [&](const Frags& f, const unsigned char* buf, int c) {
         const int64_t start = t0 + (int64_t)C * c;
         const int nvalid = (int)min((int64_t)C, t1 - start);
         // bf16 operand copy of the state: k-step j pairs tiles 2j and 2j+1
@@ -187,42 +166,101 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
                 sb[j][e] = (bf16)S[2 * j][e];
                 sb[j][4 + e] = (bf16)S[2 * j + 1][e];
             }
-        floatx4 Y;
+        // -KG_b S for each 16-token block b
+        floatx4 Y[NB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Y[i] = (4 * lg + i < nvalid) ? f.v[i] : 0.f;
+        for (int b = 0; b < NB; ++b) {
+            Y[b] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < KS; ++j) Y = mfma32(f.nkg[j], sb[j], Y);  // V - KG S
-        floatx4 OT = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < KS; ++j) Y[b] = mfma32(f.nkg[b][j], sb[j], Y[b]);
+        }
+        // O_ob^T = S^T QG_ob^T for each 16-token output block ob
+        floatx4 OT[NB];
 #pragma unroll
-        for (int j = 0; j < KS; ++j) OT = mfma32(sb[j], w.qg[j], OT);  // S^T QG^T
+        for (int ob = 0; ob < NB; ++ob) {
+            OT[ob] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                const bf16x8 qg = *reinterpret_cast<const bf16x8*>(
+                    buf + R::QG + ((ob * KS + j) * 64 + lane) * 16);
+                OT[ob] = mfma32(sb[j], qg, OT[ob]);
+            }
+        }
         // decay the state; the rank-C update accumulates onto it
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
+        for (int t = 0; t < KT; ++t) {
+            const floatx4 gc =
+                *reinterpret_cast<const floatx4*>(buf + R::GAMC + (16 * t + 4 * lg) * 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[t][i] *= w.gc[t][i];
+            for (int i = 0; i < 4; ++i) S[t][i] *= gc[i];
+        }
+        // Y_b = V_b - KG_b S (padding tokens read 0)
+        const uint16_t* vt = reinterpret_cast<const uint16_t*>(buf + L::V_OFF);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = 16 * b + 4 * lg + i;
+                const float v = bf2f(vt[tok * L::VCOLS + cw + lr]);
+                Y[b][i] += tok < nvalid ? v : 0.f;
+            }
+        // U' = Tb Y over the chunk's tokens, one 16-token row block at a time
         const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-        const bf16x4 ub = to_bf16x4(mfma16(f.tb, to_bf16x4(Y), zero));  // U'
+        bf16xEL yc, uc;
 #pragma unroll
-        for (int t = 0; t < KT; ++t) S[t] = mfma16(f.kdt[t], ub, S[t]);
-        // + U'^T Aqk^T, accumulated apart and added on the VALU: a 16x16x16 MFMA
-        // must not take the result of a 16x16x32 MFMA as its accumulator input
-        // (that dependent pair gave wrong sums on gfx950)
-        const floatx4 OI = mfma16(ub, f.aqk, zero);
-        // OT[i] = O[token lr][column cb + cw + 4 lg + i]
-        if (lr < nvalid) {
-            bf16x4 ov;
+        for (int i = 0; i < 4; ++i) {
+            yc[i] = (bf16)Y[0][i];
+            if constexpr (NB == 2) yc[4 + i] = (bf16)Y[NB - 1][i];
+        }
+        floatx4 U[NB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ov[i] = (bf16)(a.scale * (OT[i] + OI[i]));
-            *reinterpret_cast<bf16x4*>(a.o + (start + lr) * vstride + (int64_t)h * a.V + cb + cw +
-                                       4 * lg) = ov;
+        for (int b = 0; b < NB; ++b) {
+            const bf16xEL tb =
+                *reinterpret_cast<const bf16xEL*>(buf + R::TB + (b * 64 + lane) * (2 * EL));
+            U[b] = mfma_tok(tb, yc, zero);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uc[i] = (bf16)U[0][i];
+            if constexpr (NB == 2) uc[4 + i] = (bf16)U[NB - 1][i];
+        }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const bf16xEL kdt =
+                *reinterpret_cast<const bf16xEL*>(buf + R::KDT + (t * 64 + lane) * (2 * EL));
+            S[t] = mfma_tok(kdt, uc, S[t]);
+        }
+        // + U'^T Aqk^T.  With one block the 16x16x16 product is accumulated apart
+        // and added on the VALU: a 16x16x16 MFMA must not take the result of a
+        // 16x16x32 MFMA as its accumulator input (that dependent pair gave wrong
+        // sums on gfx950).  With two blocks both products are 16x16x32.
+#pragma unroll
+        for (int ob = 0; ob < NB; ++ob) {
+            const bf16xEL aqk =
+                *reinterpret_cast<const bf16xEL*>(buf + R::AQK + (ob * 64 + lane) * (2 * EL));
+            if constexpr (NB == 1) {
+                const floatx4 OI = mfma_tok(uc, aqk, zero);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) OT[ob][i] += OI[i];
+            } else {
+                OT[ob] = mfma_tok(uc, aqk, OT[ob]);
+            }
+            // OT[ob][i] = O[token 16 ob + lr][column cb + cw + 4 lg + i]
+            if (16 * ob + lr < nvalid) {
+                bf16x4 ov;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[i] = (bf16)(a.scale * OT[ob][i]);
+                *reinterpret_cast<bf16x4*>(a.o + (start + 16 * ob + lr) * vstride +
+                                           (int64_t)h * a.V + cb + cw + 4 * lg) = ov;
+            }
         }
     };
 
     if (nch > 0) {
         // Pipeline, iteration c: chunk c + 2 + DEPTH loads into registers,
-        // chunk c + 2 is written to LDS buffer (c + 2) % 3, chunk c + 1's
-        // operands are read from buffer (c + 1) % 3 into registers, and chunk c
-        // computes (reading only its decay from buffer c % 3).  One barrier.
+        // chunk c + 2 is written to LDS buffer (c + 2) % 3, chunk c + 1's nKG is
+        // read from buffer (c + 1) % 3 into registers, and chunk c computes
+        // (reading its other operands from buffer c % 3).  One barrier.
         Frags fr[2];
         static_for<0, DEPTH>([&](auto d) { issue(ring[d], d); });
         commit(ring[0], stage[0]);
@@ -238,12 +276,10 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
                 constexpr int cur = u & 1;            // DEPTH is even
                 const int c = base + u;
                 const int s1b = sc == 2 ? 0 : sc + 1, s2b = sc == 0 ? 2 : sc - 1;
-                Own own;
-                read_own(own, stage[sc]);        // chunk c
                 commit(ring[nx2], stage[s2b]);  // chunk c + 2
                 issue(ring[nx2], c + 2 + DEPTH);
-                read_frags(fr[cur ^ 1], stage[s1b]);  // chunk c + 1
-                if (c < nch) compute(fr[cur], own, c);  // uniform over the workgroup
+                read_frags(fr[cur ^ 1], stage[s1b]);          // chunk c + 1
+                if (c < nch) compute(fr[cur], stage[sc], c);  // uniform over the workgroup
                 __syncthreads();
                 sc = s1b;
             });
@@ -264,7 +300,7 @@ __global__ __launch_bounds__(64 * NW) void kda_recur_kernel(RecurArgs a) {
 #define KDA_RECUR_WAVES 4
 #endif
 #ifndef KDA_RECUR_DEPTH
-#define KDA_RECUR_DEPTH 4
+#define KDA_RECUR_DEPTH 2
 #endif
 constexpr int RECUR_WAVES = KDA_RECUR_WAVES;
 constexpr int RECUR_DEPTH = KDA_RECUR_DEPTH;

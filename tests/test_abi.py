@@ -38,10 +38,11 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_size_formula(lib):
-    rec = 3 * 16 * 128 * 2 + 2 * 16 * 16 * 2 + 128 * 4  # bytes per (chunk, head) at K=128
+    C = 32  # tokens per chunk
+    rec = 3 * C * 128 * 2 + 2 * C * C * 2 + 128 * 4  # bytes per (chunk, head) at K=128
     B, T, H, N = 2, 2048, 32, 2
     meta = 256
-    want = meta + ((B * T + 15) // 16 + N) * H * rec
+    want = meta + ((B * T + C - 1) // C + N) * H * rec
     assert kda.workspace_size(B, T, H, 128, 128) == want
     assert kda.workspace_size(1, 100, 1, 96, 128) == 0  # unsupported K
     assert kda.workspace_size(0, 100, 1, 128, 128) == 0
