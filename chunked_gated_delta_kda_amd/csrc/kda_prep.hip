@@ -1,10 +1,10 @@
 // kda_prep.hip -- token-parallel half of the chunked forward pass (gfx950).
 //
-// One workgroup per (16-token chunk, head).  It fuses the gate activation,
-// the sigmoid of beta, the in-chunk cumulative decay, the q/k L2 norms, the
-// two intra-chunk 16x16 matrices (bf16 MFMA over K), the exact inverse
-// (I + A)^-1 by the doubling product, and writes the chunk record that
-// kda_recur consumes (layout in kda_common.h).
+// One workgroup per (chunk, head), one wave per 16-token block of the chunk.
+// It fuses the gate activation, the sigmoid of beta, the in-chunk cumulative
+// decay, the q/k L2 norms, the intra-chunk matrices (bf16 MFMA over K), the
+// exact inverse (I + A)^-1 by the doubling product, and writes the chunk
+// record that kda_recur consumes (layout in kda_common.h).
 //
 // The split into a token-parallel kernel and a head-parallel recurrence
 // follows the FlashKDA summary (discuss.pytorch.kr, section "커널 퓨전(Kernel

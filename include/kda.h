@@ -112,7 +112,7 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
  * kda_prep / gdn_prep: the token-parallel stage.  Gate activation, sigmoid
  * of beta (KDA), in-chunk cumulative decay, q/k L2 norm, the intra-chunk
  * matrices and the exact inverse of (I + A); writes the sequence table and
- * one record per (16-token chunk, head) into the workspace.  The FlashKDA
+ * one record per (32-token chunk, head) into the workspace.  The FlashKDA
  * summary (discuss.pytorch.kr, section "커널 퓨전(Kernel Fusion) 전략의 분리")
  * puts exactly these operations in its first, token-parallel kernel.
  *
