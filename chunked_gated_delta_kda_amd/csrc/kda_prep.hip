@@ -225,7 +225,6 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     unsigned char* rec = a.rec + ((int64_t)slot * a.H + h) * R::BYTES;
     floatx4 dA = {0.f, 0.f, 0.f, 0.f}, dAT = dA, dQT = dA, dX = dA, dXQT = dA;
     bf16x8 kgl_f[KS], qgl_f[KS];  // block 1's local KG and QG (cross-block products)
-    float gcv[KS][8];             // Gam_C per channel (written by one row)
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
         float qn[8], kn[8];
@@ -256,7 +255,6 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
             kg[e] = kgl[e] * before;
             qg[e] = qgl[e] * before;
             kd[e] = kdl[e] * after;
-            gcv[j][e] = exp2_hw(gown[e] + goth[e]);
         }
         *reinterpret_cast<bf16x8*>(rec + R::NKG + ((blk * KS + j) * 64 + L) * 16) = pack8(kg, -1.f);
         *reinterpret_cast<bf16x8*>(rec + R::QG + ((blk * KS + j) * 64 + L) * 16) = pack8(qg);
@@ -292,8 +290,14 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         float* gp = reinterpret_cast<float*>(rec + R::GAMC);
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
-            const floatx4 lo = {gcv[j][0], gcv[j][1], gcv[j][2], gcv[j][3]};
-            const floatx4 hi = {gcv[j][4], gcv[j][5], gcv[j][6], gcv[j][7]};
+            float gcv[8];  // the chunk's total decay of this lane's channels
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = GDN ? 0 : 32 * j + 8 * g + e;
+                gcv[e] = exp2_hw(gend_s[0][c] + (NB == 2 ? gend_s[NB - 1][c] : 0.f));
+            }
+            const floatx4 lo = {gcv[0], gcv[1], gcv[2], gcv[3]};
+            const floatx4 hi = {gcv[4], gcv[5], gcv[6], gcv[7]};
             *reinterpret_cast<floatx4*>(gp + 32 * j + 4 * g) = lo;
             *reinterpret_cast<floatx4*>(gp + 32 * j + 16 + 4 * g) = hi;
         }
