@@ -105,6 +105,54 @@ def cpu_baseline(w, budget_s):
                        f"input up-cast excluded")}
 
 
+def bench_decode(args, torch, kda, inputs, dev):
+    """One decode step (kda_decode) per timed step for N sequences x 32 heads at
+    K = V = 128, the state updated in place; its bytes are the state read and
+    written once plus the token's q, k, g, v, beta and o."""
+    N, H, K, V = args.decode_seqs, 32, 128, 128
+    w = inputs.kda_workload(N, 1, H, K, V, seed=1100, init_std=0.05, name="decode")
+    d = w.to(dev)
+    q, k, v, g, beta = (d[n][:, 0].contiguous() for n in ("q", "k", "v", "g", "beta"))
+    state = d["initial_state"].clone()
+    out = torch.empty((N, H, V), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kda.kda_decode(q, k, v, g, beta, d["A_log"], d["dt_bias"], w.lower_bound, w.scale,
+                       state, state, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    pairs = N * H
+    nbytes = pairs * (2 * K * V * 4 + 2 * K * 2 + 2 * K + 2 * V + 2 + 2 * V) + H * 4 + H * K * 4
+    achieved = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "kda decode step tokens/sec (one token per sequence), H32 K=V=128",
+        "value": round(N / (elapsed / args.steps), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32 state, bf16 tokens",
+        "data": "synthetic",
+        "config": {"workload": f"kda_decode_N{N}_H{H}_K{K}", "N": N, "H": H, "K": K, "V": V},
+        "roofline": {"bound": "hbm", "kernel": "kda_decode", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(nbytes),
+                     "avg_launch_us": round(us, 2)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +161,10 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="instead of the forward pass, time the single-token decode step "
+                         "(kda_decode) for --decode-seqs sequences x 32 heads, K=V=128")
+    ap.add_argument("--decode-seqs", type=int, default=64)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, copy BYTES bytes device-to-device "
                          "--steps times (the known-size reference for HBM byte counters)")
@@ -145,6 +197,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "steps": args.steps}), flush=True)
+        return
+
+    if args.decode:
+        bench_decode(args, torch, kda, inputs, dev)
         return
 
     base = inputs.config(1)

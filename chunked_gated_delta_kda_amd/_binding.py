@@ -18,7 +18,8 @@ _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED"
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_fwd", "gdn_fwd", "kda_fwd_workspace_size", "gdn_fwd_workspace_size",
-           "kda_prep", "gdn_prep", "kda_recur", "kda_status_str", "kda_version")
+           "kda_prep", "gdn_prep", "kda_recur", "kda_decode", "gdn_decode", "kda_status_str",
+           "kda_version")
 
 
 class LibKdaError(RuntimeError):
@@ -57,6 +58,12 @@ def load(path: Path | str | None = None):
     lib.kda_recur.restype = ctypes.c_int
     lib.kda_recur.argtypes = [u16p, f32, f32p, f32p, i32, i32, i32, i32, i32, i32, i32, u16p, vp,
                               sz, vp]
+    lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [u16p, u16p, u16p, u16p, u16p, f32p, f32p, f32, f32, f32p, f32p,
+                               i32, i32, i32, i32, u16p, vp]
+    lib.gdn_decode.restype = ctypes.c_int
+    lib.gdn_decode.argtypes = [u16p, u16p, u16p, f32p, u16p, f32, f32p, f32p, i32, i32, i32, i32,
+                               u16p, vp]
     for name in ("kda_fwd_workspace_size", "gdn_fwd_workspace_size"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_size_t
@@ -242,3 +249,58 @@ def kda_recur(v, K, scale, workspace, out, initial_state=None, final_out=None, n
     _check(load().kda_recur(_ptr(v), float(scale), _ptr(initial_state), _ptr(final_out),
                             1 if varlen else 0, N, B, T, H, K, V, _ptr(out), _ptr(workspace),
                             _nbytes(workspace), stream))
+
+
+def _decode_prepare(q, k, v, beta, scale, state, state_out, out):
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, K]")
+    dev = q.device
+    N, H, K = q.shape
+    _need(k, "k", torch.bfloat16, (N, H, K), dev)
+    if v.dim() != 3:
+        raise ValueError("v must be [N, H, V]")
+    V = v.shape[2]
+    _need(v, "v", torch.bfloat16, (N, H, V), dev)
+    _need(beta, "beta", torch.bfloat16, (N, H), dev)
+    if state is not None:
+        _need(state, "state", torch.float32, (N, H, K, V), dev)
+    if state_out is None:
+        state_out = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    else:
+        _need(state_out, "state_out", torch.float32, (N, H, K, V), dev)
+    if out is None:
+        out = torch.empty((N, H, V), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, (N, H, V), dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    return N, H, K, V, float(K ** -0.5 if scale is None else scale), state_out, out, stream
+
+
+def kda_decode(q, k, v, g, beta, A_log, dt_bias, lower_bound=-5.0, scale=None, state=None,
+               state_out=None, out=None):
+    """One KDA step for N sequences: q, k, g [N,H,K] bf16; v [N,H,V] bf16; beta logits
+    [N,H] bf16; state [N,H,K,V] fp32 or None (zeros).  ``state_out`` may be ``state``
+    (update in place).  Returns (o [N,H,V] bf16, new state [N,H,K,V] fp32)."""
+    torch = _torch()
+    N, H, K, V, sc, so, o, stream = _decode_prepare(q, k, v, beta, scale, state, state_out, out)
+    _need(g, "g", torch.bfloat16, (N, H, K), q.device)
+    _need(A_log, "A_log", torch.float32, (H,), q.device)
+    _need(dt_bias, "dt_bias", torch.float32, None, q.device)
+    if dt_bias.numel() != H * K:
+        raise ValueError("dt_bias must hold H * K values ([H, K] or [H * K])")
+    _check(load().kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                             _ptr(dt_bias), float(lower_bound), sc, _ptr(state), _ptr(so), N, H,
+                             K, V, _ptr(o), stream))
+    return o, so
+
+
+def gdn_decode(q, k, v, g, beta, scale=None, state=None, state_out=None, out=None):
+    """One GDN step: g is the fp32 log decay [N,H]; beta probabilities [N,H] bf16."""
+    torch = _torch()
+    N, H, K, V, sc, so, o, stream = _decode_prepare(q, k, v, beta, scale, state, state_out, out)
+    _need(g, "g", torch.float32, (N, H), q.device)
+    _check(load().gdn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), sc, _ptr(state),
+                             _ptr(so), N, H, K, V, _ptr(o), stream))
+    return o, so

@@ -1,6 +1,6 @@
 // kda_api.hip -- the C ABI of libkda (declared in include/kda.h): host-side
-// argument checks, workspace layout and the three launches
-// (sequence table, kda_prep, kda_recur) on the caller's stream.
+// argument checks, workspace layout and the launches (sequence table,
+// kda_prep, kda_recur; the decode step) on the caller's stream.
 #include <cmath>
 #include <cstdint>
 
@@ -143,6 +143,31 @@ int check_kda_gate(int32_t T, const uint16_t* g, const float* A_log, const float
     return KDA_OK;
 }
 
+// Checks shared by the decode entry points.
+int check_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* beta,
+                 float scale, const float* state_in, float* state_out, int32_t N, int32_t H,
+                 int32_t K, int32_t V, const uint16_t* o) {
+    if (N < 1 || H < 1) return KDA_ERR_INVALID_ARG;
+    if (!q || !k || !v || !beta || !state_out || !o) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(K) || !supported_dim(V)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H * (V / 64) >= ((int64_t)1 << 31)) return KDA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 8) || !aligned(o, 8) ||
+        !aligned(state_out, 16) || !aligned(state_in, 16))
+        return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+int run_decode(kda::DecodeArgs& d, int32_t N, int32_t H, int32_t K, int32_t V, bool gdn,
+               hipStream_t stream) {
+    d.H = H;
+    d.V = V;
+    d.n_pairs = N * H;
+    (void)hipGetLastError();
+    kda::launch_decode(d, K, gdn, stream);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,6 +266,49 @@ int kda_recur(const uint16_t* v, float scale, const float* initial_state, float*
     int st = check_common(c, N);
     if (st != KDA_OK) return st;
     return run_recur(c, N, static_cast<hipStream_t>(stream));
+}
+
+int kda_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+               const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
+               float scale, const float* state_in, float* state_out, int32_t N, int32_t H,
+               int32_t K, int32_t V, uint16_t* o, void* stream) {
+    int st = check_decode(q, k, v, beta, scale, state_in, state_out, N, H, K, V, o);
+    if (st != KDA_OK) return st;
+    st = check_kda_gate(1, g, A_log, dt_bias, lower_bound);
+    if (st != KDA_OK) return st;
+    kda::DecodeArgs d{};
+    d.q = q;
+    d.k = k;
+    d.v = v;
+    d.g_kda = g;
+    d.beta = beta;
+    d.A_log = A_log;
+    d.dt_bias = dt_bias;
+    d.lower_bound = lower_bound;
+    d.scale = scale;
+    d.state_in = state_in;
+    d.state_out = state_out;
+    d.o = o;
+    return run_decode(d, N, H, K, V, false, static_cast<hipStream_t>(stream));
+}
+
+int gdn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+               const uint16_t* beta, float scale, const float* state_in, float* state_out,
+               int32_t N, int32_t H, int32_t K, int32_t V, uint16_t* o, void* stream) {
+    int st = check_decode(q, k, v, beta, scale, state_in, state_out, N, H, K, V, o);
+    if (st != KDA_OK) return st;
+    if (!g) return KDA_ERR_INVALID_ARG;
+    kda::DecodeArgs d{};
+    d.q = q;
+    d.k = k;
+    d.v = v;
+    d.g_gdn = g;
+    d.beta = beta;
+    d.scale = scale;
+    d.state_in = state_in;
+    d.state_out = state_out;
+    d.o = o;
+    return run_decode(d, N, H, K, V, true, static_cast<hipStream_t>(stream));
 }
 
 const char* kda_status_str(int status) {

@@ -42,10 +42,30 @@ struct RecurArgs {
     const int32_t* chunk_off;
 };
 
+struct DecodeArgs {
+    const uint16_t* q;         // [pairs, K] bf16 (pairs = N * H, head fastest)
+    const uint16_t* k;         // [pairs, K] bf16
+    const uint16_t* v;         // [pairs, V] bf16
+    const uint16_t* g_kda;     // KDA: pre-activation gate [pairs, K] bf16
+    const float* g_gdn;        // GDN: log decay [pairs] fp32
+    const uint16_t* beta;      // [pairs] bf16 (KDA logits / GDN probabilities)
+    const float* A_log;        // [H] (KDA)
+    const float* dt_bias;      // [H, K] (KDA)
+    float lower_bound;
+    float scale;
+    const float* state_in;     // [pairs, K, V] fp32 or null (zeros)
+    float* state_out;          // [pairs, K, V] fp32 (may equal state_in)
+    uint16_t* o;               // [pairs, V] bf16
+    int32_t H;
+    int32_t V;
+    int32_t n_pairs;
+};
+
 void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t total_tokens,
                       int32_t* seq_start, int32_t* chunk_off, hipStream_t stream);
 void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream);
 void launch_recur(const RecurArgs& a, int K, hipStream_t stream);
+void launch_decode(const DecodeArgs& a, int K, bool gdn, hipStream_t stream);
 int record_bytes(int K);
 
 }  // namespace kda

@@ -137,6 +137,35 @@ int kda_recur(const uint16_t* v, float scale, const float* initial_state, float*
               int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
+/* One recurrent step per sequence: the single-token form of the same
+ * recurrence, for decoding after a prefill (the cuLA pages list decode
+ * kernels on their inference roadmap: cuLA blog, section "Status &
+ * Roadmap"; the gate, beta and norm are those of FlashKDA's parameter table,
+ * discuss.pytorch.kr, section "FlashKDA의 KDA 연산 구조").  For each of the
+ * N sequences and H heads, with S the [K, V] state:
+ *   S' = (I - beta k^ k^T) Diag(alpha) S + beta k^ v^T,   o = scale S'^T q^
+ * where alpha, beta and the normalised q^, k^ are formed exactly as in
+ * kda_fwd / gdn_fwd for one token.  Running it T times from a state gives the
+ * same states and outputs (up to rounding) as the forward pass over those T
+ * tokens.
+ *
+ * Layouts (device pointers, contiguous): q, k [N, H, K] bf16; v, o [N, H, V]
+ * bf16; KDA g [N, H, K] bf16 and GDN g [N, H] fp32 (log decay <= 0); beta
+ * [N, H] bf16 (KDA logits, GDN probabilities); A_log [H], dt_bias [H, K]
+ * fp32; state_in, state_out [N, H, K, V] fp32.  state_in may be NULL (zero
+ * state) and may equal state_out (update in place); state_out is required.
+ * No workspace.  Alignment: q, k, state_in, state_out 16 bytes; v, o 8 bytes.
+ * Errors as for the forward pass (lower_bound in [-5, 0], finite scale,
+ * K and V in {64, 128}); nothing is enqueued when a check fails. */
+int kda_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+               const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
+               float scale, const float* state_in, float* state_out, int32_t N, int32_t H,
+               int32_t K, int32_t V, uint16_t* o, void* stream);
+
+int gdn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+               const uint16_t* beta, float scale, const float* state_in, float* state_out,
+               int32_t N, int32_t H, int32_t K, int32_t V, uint16_t* o, void* stream);
+
 const char* kda_status_str(int status);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

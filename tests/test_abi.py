@@ -89,3 +89,34 @@ def test_gdn_rejects_on_host(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         kda.load(tmp_path / "nope.so")
+
+
+def _decode_call(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0,
+             scale=0.088, s_in=None, s_out=FAKE, N=2, H=4, K=128, V=128, o=FAKE, stream=None)
+    a.update(over)
+    return lib.kda_decode(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"], a["dt_bias"],
+                          a["lb"], a["scale"], a["s_in"], a["s_out"], a["N"], a["H"], a["K"],
+                          a["V"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(g=None), 1),
+    (dict(beta=None), 1), (dict(o=None), 1), (dict(s_out=None), 1), (dict(A_log=None), 1),
+    (dict(dt_bias=None), 1), (dict(N=0), 1), (dict(H=0), 1), (dict(lb=-6.0), 1),
+    (dict(scale=float("nan")), 1), (dict(K=32), 2), (dict(V=96), 2),
+    (dict(s_in=ctypes.c_void_p(0x1004)), 1), (dict(q=ctypes.c_void_p(0x1008)), 1),
+])
+def test_kda_decode_rejects_on_host(lib, over, code):
+    assert _decode_call(lib, **over) == code
+
+
+def test_gdn_decode_rejects_on_host(lib):
+    args = [FAKE, FAKE, FAKE, None, FAKE, 0.1, None, FAKE, 2, 4, 128, 128, FAKE, None]
+    assert lib.gdn_decode(*args) == 1  # null g
+    args[3] = FAKE
+    args[10] = 48
+    assert lib.gdn_decode(*args) == 2  # unsupported K
+    args[10] = 128
+    args[7] = None
+    assert lib.gdn_decode(*args) == 1  # null state_out
