@@ -18,8 +18,8 @@ _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED"
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_fwd", "gdn_fwd", "kda_fwd_workspace_size", "gdn_fwd_workspace_size",
-           "kda_prep", "gdn_prep", "kda_recur", "kda_decode", "gdn_decode", "kda_status_str",
-           "kda_version")
+           "kda_fwd_split_workspace_size", "kda_fwd_split", "gdn_fwd_split", "kda_prep",
+           "gdn_prep", "kda_recur", "kda_decode", "gdn_decode", "kda_status_str", "kda_version")
 
 
 class LibKdaError(RuntimeError):
@@ -49,6 +49,14 @@ def load(path: Path | str | None = None):
     lib.gdn_fwd.restype = ctypes.c_int
     lib.gdn_fwd.argtypes = [u16p, u16p, u16p, f32p, u16p, f32, f32p, f32p, i32p, i32, i32, i32,
                             i32, i32, i32, u16p, vp, sz, vp]
+    lib.kda_fwd_split.restype = ctypes.c_int
+    lib.kda_fwd_split.argtypes = [u16p, u16p, u16p, u16p, u16p, f32p, f32p, f32, f32, f32p, f32p,
+                                  i32p, i32, i32, i32, i32, i32, i32, u16p, vp, sz, i32, vp]
+    lib.gdn_fwd_split.restype = ctypes.c_int
+    lib.gdn_fwd_split.argtypes = [u16p, u16p, u16p, f32p, u16p, f32, f32p, f32p, i32p, i32, i32,
+                                  i32, i32, i32, i32, u16p, vp, sz, i32, vp]
+    lib.kda_fwd_split_workspace_size.restype = ctypes.c_size_t
+    lib.kda_fwd_split_workspace_size.argtypes = [i32] * 7
     lib.kda_prep.restype = ctypes.c_int
     lib.kda_prep.argtypes = [u16p, u16p, u16p, u16p, f32p, f32p, f32, i32p, i32, i32, i32, i32,
                              i32, i32, vp, sz, vp]
@@ -85,9 +93,12 @@ def version() -> int:
     return int(load().kda_version())
 
 
-def workspace_size(B, T, H, K, V, num_seqs=None, kind="kda") -> int:
+def workspace_size(B, T, H, K, V, num_seqs=None, kind="kda", segment_chunks=None) -> int:
+    n = B if num_seqs is None else num_seqs
+    if segment_chunks is not None:
+        return int(load().kda_fwd_split_workspace_size(B, T, H, K, V, n, int(segment_chunks)))
     fn = load().kda_fwd_workspace_size if kind == "kda" else load().gdn_fwd_workspace_size
-    return int(fn(B, T, H, K, V, B if num_seqs is None else num_seqs))
+    return int(fn(B, T, H, K, V, n))
 
 
 # ---------------------------------------------------------------- marshalling
@@ -118,7 +129,7 @@ def _need(t, name, dtype, shape=None, device=None):
 
 
 def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens, workspace,
-             kind, out=None, final_out=None):
+             kind, out=None, final_out=None, segment_chunks=None):
     torch = _torch()
     _need(q, "q", torch.bfloat16)
     if q.dim() != 4:
@@ -155,7 +166,7 @@ def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens
         else:
             _need(final_out, "final_out", torch.float32, (N, H, K, V), dev)
         final = final_out
-    need = workspace_size(B, T, H, K, V, N, kind)
+    need = workspace_size(B, T, H, K, V, N, kind, segment_chunks)
     if need == 0:
         raise LibKdaError(2, status_str(2))
     if workspace is None:
@@ -169,44 +180,47 @@ def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens
 
 def kda_fwd(q, k, v, g, beta, A_log, dt_bias, lower_bound=-5.0, scale=None, initial_state=None,
             output_final_state=True, cu_seqlens=None, workspace=None, out=None,
-            final_out=None):
+            final_out=None, segment_chunks=None):
     """KDA forward on the GPU.  q, k, g [B,T,H,K] bf16; v [B,T,H,V] bf16; beta logits
     [B,T,H] bf16; A_log [H] fp32; dt_bias [H,K] (or [H*K]) fp32; initial_state
     [N,H,K,V] fp32 or None; cu_seqlens int32 [N+1] or None (B must then be 1).
     ``workspace``, ``out`` and ``final_out`` optionally supply preallocated device
-    buffers.  Returns (o [B,T,H,V] bf16, final_state [N,H,K,V] fp32 or None)."""
+    buffers.  ``segment_chunks`` (None: automatic) controls sequence splitting
+    (kda_fwd_split).  Returns (o [B,T,H,V] bf16, final_state [N,H,K,V] fp32 or None)."""
     torch = _torch()
     a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens,
-                 workspace, "kda", out, final_out)
+                 workspace, "kda", out, final_out, segment_chunks)
     B, T, H, K = a["B"], a["T"], a["H"], a["K"]
     _need(g, "g", torch.bfloat16, (B, T, H, K), q.device)
     _need(A_log, "A_log", torch.float32, (H,), q.device)
     _need(dt_bias, "dt_bias", torch.float32, None, q.device)
     if dt_bias.numel() != H * K:
         raise ValueError("dt_bias must hold H * K values ([H, K] or [H * K])")
-    st = load().kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
-                        _ptr(dt_bias), float(lower_bound), a["scale"], _ptr(initial_state),
-                        _ptr(a["final"]), _ptr(cu_seqlens), a["N"], B, T, H, K, a["V"],
-                        _ptr(a["o"]), _ptr(a["workspace"]),
-                        a["workspace"].numel() * a["workspace"].element_size(), a["stream"])
+    st = load().kda_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                              _ptr(dt_bias), float(lower_bound), a["scale"], _ptr(initial_state),
+                              _ptr(a["final"]), _ptr(cu_seqlens), a["N"], B, T, H, K, a["V"],
+                              _ptr(a["o"]), _ptr(a["workspace"]),
+                              a["workspace"].numel() * a["workspace"].element_size(),
+                              0 if segment_chunks is None else int(segment_chunks), a["stream"])
     if st != 0:
         raise LibKdaError(st, status_str(st))
     return a["o"], a["final"]
 
 
 def gdn_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
-            cu_seqlens=None, workspace=None, out=None, final_out=None):
+            cu_seqlens=None, workspace=None, out=None, final_out=None, segment_chunks=None):
     """GDN forward on the GPU.  g is the fp32 log decay [B,T,H] (<= 0); beta are
     probabilities [B,T,H] bf16, used as given.  Other arguments as kda_fwd."""
     torch = _torch()
     a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens,
-                 workspace, "gdn", out, final_out)
+                 workspace, "gdn", out, final_out, segment_chunks)
     B, T, H = a["B"], a["T"], a["H"]
     _need(g, "g", torch.float32, (B, T, H), q.device)
-    st = load().gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), a["scale"],
-                        _ptr(initial_state), _ptr(a["final"]), _ptr(cu_seqlens), a["N"], B, T,
-                        H, a["K"], a["V"], _ptr(a["o"]), _ptr(a["workspace"]),
-                        a["workspace"].numel() * a["workspace"].element_size(), a["stream"])
+    st = load().gdn_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), a["scale"],
+                              _ptr(initial_state), _ptr(a["final"]), _ptr(cu_seqlens), a["N"],
+                              B, T, H, a["K"], a["V"], _ptr(a["o"]), _ptr(a["workspace"]),
+                              a["workspace"].numel() * a["workspace"].element_size(),
+                              0 if segment_chunks is None else int(segment_chunks), a["stream"])
     if st != 0:
         raise LibKdaError(st, status_str(st))
     return a["o"], a["final"]

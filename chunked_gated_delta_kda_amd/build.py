@@ -16,7 +16,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libkda.so"
-SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_decode.hip", "kda_split.hip"]
 ARCH = "gfx950"
 
 

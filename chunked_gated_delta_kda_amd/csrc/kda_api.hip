@@ -1,6 +1,7 @@
 // kda_api.hip -- the C ABI of libkda (declared in include/kda.h): host-side
 // argument checks, workspace layout and the launches (sequence table,
 // kda_prep, kda_recur; the decode step) on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -25,8 +26,57 @@ int64_t max_slots(int32_t B, int32_t T, int32_t N, bool varlen) {
 
 size_t meta_bytes(int32_t N) { return align_up(2 * sizeof(int32_t) * ((size_t)N + 1)); }
 
-size_t workspace_bytes_for(int32_t B, int32_t T, int32_t H, int32_t K, int32_t N, bool varlen) {
-    return meta_bytes(N) + (size_t)max_slots(B, T, N, varlen) * H * kda::record_bytes(K);
+// Sequence splitting: segments of L chunks (L = 0: none).  n_virt bounds the
+// number of segments (each sequence has at most 1 + chunks / L of them).
+struct SplitPlan {
+    int32_t L;
+    int64_t n_virt;
+};
+
+constexpr int32_t SPLIT_MIN_CHUNKS = 64;   // shortest segment the automatic choice makes
+constexpr int32_t SPLIT_TARGET_BLOCKS = 512;  // second-pass workgroups it aims for
+constexpr int32_t RECUR_COLS = 32;         // value columns per kda_recur workgroup
+constexpr float SPLIT_BOUND_LIMIT = -40.f; // log2: transitions below 2^-40 are negligible
+
+// request: < 0 never split, 0 automatic, > 0 segment length in chunks.
+SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t V, int32_t N, bool varlen,
+                     int32_t request) {
+    SplitPlan p{0, 0};
+    const int64_t slots = max_slots(B, T, N, varlen);
+    if (request < 0 || slots == 0) return p;
+    int64_t L = request;
+    if (request == 0) {
+        // only when the (sequence, head, column block) workgroups leave most
+        // CUs idle and the sequences are long
+        const int64_t blocks = (int64_t)N * H * (V / RECUR_COLS);
+        const int64_t avg = (slots + N - 1) / N;
+        if (blocks >= SPLIT_TARGET_BLOCKS / 4 || avg < 2 * SPLIT_MIN_CHUNKS) return p;
+        const int64_t segs = (SPLIT_TARGET_BLOCKS + blocks - 1) / blocks;
+        L = std::max<int64_t>(SPLIT_MIN_CHUNKS, (avg + segs - 1) / segs);
+        if (L >= avg) return p;
+    }
+    p.L = (int32_t)std::min<int64_t>(L, INT32_MAX);
+    p.n_virt = N + (slots + p.L - 1) / p.L;
+    return p;
+}
+
+size_t bound_bytes(int64_t slots, int32_t H) { return align_up((size_t)slots * H * sizeof(float)); }
+
+size_t split_bytes(const SplitPlan& p, int32_t N, int32_t H, int32_t K, int32_t V) {
+    if (p.L == 0) return 0;
+    const size_t nv = (size_t)p.n_virt;
+    const size_t tables = align_up(sizeof(int32_t) * (2 * (nv + 1) + nv + ((size_t)N + 1)));
+    const size_t flags = align_up(sizeof(int32_t) * nv * H);
+    const size_t states = align_up(sizeof(float) * nv * H * K * V);
+    const size_t trans = align_up(sizeof(float) * nv * H * K * K);
+    return tables + flags + 2 * states + trans;
+}
+
+size_t workspace_bytes_for(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t N,
+                           bool varlen, const SplitPlan& sp) {
+    const int64_t slots = max_slots(B, T, N, varlen);
+    return meta_bytes(N) + (size_t)slots * H * kda::record_bytes(K) + bound_bytes(slots, H) +
+           split_bytes(sp, N, H, K, V);
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -42,6 +92,7 @@ struct Common {
     void* ws;
     size_t ws_bytes;
     float scale;
+    int32_t split;      // sequence-splitting request (see plan_split)
 };
 
 // Checks shared by both entry points; sets N.
@@ -62,7 +113,9 @@ int check_common(const Common& c, int32_t& N) {
     if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.o, 8))
         return KDA_ERR_INVALID_ARG;
     if (!c.ws || !aligned(c.ws, ALIGN)) return KDA_ERR_WORKSPACE;
-    if (c.ws_bytes < workspace_bytes_for(c.B, c.T, c.H, c.K, N, c.varlen))
+    const SplitPlan sp = plan_split(c.B, c.T, c.H, c.V, N, c.varlen, c.split);
+    if (sp.n_virt > INT32_MAX / 4) return KDA_ERR_INVALID_ARG;
+    if (c.ws_bytes < workspace_bytes_for(c.B, c.T, c.H, c.K, c.V, N, c.varlen, sp))
         return KDA_ERR_WORKSPACE;
     return KDA_OK;
 }
@@ -71,15 +124,41 @@ struct WsLayout {
     int32_t* seq_start;
     int32_t* chunk_off;
     unsigned char* rec;
+    float* bound;
     int64_t slots;
+    SplitPlan sp;
+    // splitting only
+    int32_t *vseq_start, *vchunk_off, *final_map, *vfirst, *trans_flag;
+    float *nstate, *trans, *s_in;
 };
 
 WsLayout layout(const Common& c, int32_t N) {
-    WsLayout w;
-    w.seq_start = static_cast<int32_t*>(c.ws);
+    WsLayout w{};
+    unsigned char* base = static_cast<unsigned char*>(c.ws);
+    w.seq_start = reinterpret_cast<int32_t*>(base);
     w.chunk_off = w.seq_start + (N + 1);
-    w.rec = static_cast<unsigned char*>(c.ws) + meta_bytes(N);
     w.slots = max_slots(c.B, c.T, N, c.varlen);
+    size_t off = meta_bytes(N);
+    w.rec = base + off;
+    off += (size_t)w.slots * c.H * kda::record_bytes(c.K);
+    w.bound = reinterpret_cast<float*>(base + off);
+    off += bound_bytes(w.slots, c.H);
+    w.sp = plan_split(c.B, c.T, c.H, c.V, N, c.varlen, c.split);
+    if (w.sp.L > 0) {
+        const size_t nv = (size_t)w.sp.n_virt;
+        w.vseq_start = reinterpret_cast<int32_t*>(base + off);
+        w.vchunk_off = w.vseq_start + (nv + 1);
+        w.final_map = w.vchunk_off + (nv + 1);
+        w.vfirst = w.final_map + nv;
+        off += align_up(sizeof(int32_t) * (2 * (nv + 1) + nv + ((size_t)N + 1)));
+        w.trans_flag = reinterpret_cast<int32_t*>(base + off);
+        off += align_up(sizeof(int32_t) * nv * c.H);
+        w.nstate = reinterpret_cast<float*>(base + off);
+        off += align_up(sizeof(float) * nv * c.H * c.K * c.V);
+        w.s_in = reinterpret_cast<float*>(base + off);
+        off += align_up(sizeof(float) * nv * c.H * c.K * c.V);
+        w.trans = reinterpret_cast<float*>(base + off);
+    }
     return w;
 }
 
@@ -88,9 +167,9 @@ int run_prep(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t 
     const WsLayout w = layout(c, N);
     if (w.slots > INT32_MAX || (int64_t)N * c.H * 2 > INT32_MAX) return KDA_ERR_INVALID_ARG;
     (void)hipGetLastError();  // clear a stale error from unrelated work
-    if (c.varlen)
-        kda::launch_seq_table(c.cu, N, c.T, (int64_t)c.B * c.T, w.seq_start, w.chunk_off,
-                              stream);
+    if (c.varlen || w.sp.L > 0)  // splitting reads the table for fixed lengths too
+        kda::launch_seq_table(c.varlen ? c.cu : nullptr, N, c.T, (int64_t)c.B * c.T,
+                              w.seq_start, w.chunk_off, stream);
     p.q = c.q;
     p.k = c.k;
     p.beta = c.beta;
@@ -101,16 +180,19 @@ int run_prep(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t 
     p.seq_start = w.seq_start;
     p.chunk_off = w.chunk_off;
     p.rec = w.rec;
+    p.bound = w.bound;
     if (w.slots > 0) kda::launch_prep(p, c.K, gdn, (int)w.slots, stream);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-// kda_recur: consumes the workspace.
+// kda_recur: consumes the workspace.  With splitting: the segment table, the
+// first pass over all segments (results from a zero start and, where not
+// negligible, transitions), the scan over segments and the second pass.
 int run_recur(const Common& c, int32_t N, hipStream_t stream) {
     const WsLayout w = layout(c, N);
-    if ((int64_t)N * c.H * 2 > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)N * c.H * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;
     (void)hipGetLastError();
-    kda::RecurArgs r;
+    kda::RecurArgs r{};
     r.v = c.v;
     r.rec = w.rec;
     r.initial_state = c.initial_state;
@@ -124,7 +206,48 @@ int run_recur(const Common& c, int32_t N, hipStream_t stream) {
     r.T = c.T;
     r.seq_start = w.seq_start;
     r.chunk_off = w.chunk_off;
-    kda::launch_recur(r, c.K, stream);
+    if (w.sp.L == 0) {
+        kda::launch_recur(r, c.K, stream);
+        return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    }
+    const int32_t nv = (int32_t)w.sp.n_virt;
+    if ((int64_t)nv * c.H * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    kda::launch_seg_table(w.seq_start, w.chunk_off, N, w.sp.L, nv, w.vseq_start, w.vchunk_off,
+                          w.final_map, w.vfirst, stream);
+    // first pass: every segment from a zero start, no outputs
+    kda::RecurArgs p1 = r;
+    p1.packed = 1;
+    p1.n_seqs = nv;
+    p1.seq_start = w.vseq_start;
+    p1.chunk_off = w.vchunk_off;
+    p1.initial_state = nullptr;
+    p1.final_state = w.nstate;
+    p1.o = nullptr;
+    p1.trans_out = w.trans;
+    p1.trans_flag = w.trans_flag;
+    p1.bound = w.bound;
+    p1.bound_limit = SPLIT_BOUND_LIMIT;
+    kda::launch_recur(p1, c.K, stream);
+    kda::SplitScanArgs sa{};
+    sa.initial_state = c.initial_state;
+    sa.nstate = w.nstate;
+    sa.trans = w.trans;
+    sa.trans_flag = w.trans_flag;
+    sa.vfirst = w.vfirst;
+    sa.s_in = w.s_in;
+    sa.H = c.H;
+    sa.V = c.V;
+    sa.n_seqs = N;
+    kda::launch_split_scan(sa, c.K, stream);
+    // second pass: every segment from its true entering state, with outputs
+    kda::RecurArgs p2 = r;
+    p2.packed = 1;
+    p2.n_seqs = nv;
+    p2.seq_start = w.vseq_start;
+    p2.chunk_off = w.vchunk_off;
+    p2.initial_state = w.s_in;
+    p2.final_map = w.final_map;
+    kda::launch_recur(p2, c.K, stream);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -172,12 +295,22 @@ int run_decode(kda::DecodeArgs& d, int32_t N, int32_t H, int32_t K, int32_t V, b
 
 extern "C" {
 
-size_t kda_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
-                              int32_t num_seqs) {
+size_t kda_fwd_split_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                    int32_t num_seqs, int32_t segment_chunks) {
     if (B < 1 || T < 0 || H < 1 || num_seqs < 1 || !supported_dim(K) || !supported_dim(V))
         return 0;
-    // the bound for packed sequences also covers the fixed-length layout (N = B)
-    return workspace_bytes_for(B, T, H, K, num_seqs, true);
+    // covers both layouts: packed sequences (num_seqs of them) and fixed length
+    size_t need = 0;
+    for (int varlen = 0; varlen < 2; ++varlen) {
+        const SplitPlan sp = plan_split(B, T, H, V, num_seqs, varlen != 0, segment_chunks);
+        need = std::max(need, workspace_bytes_for(B, T, H, K, V, num_seqs, varlen != 0, sp));
+    }
+    return need;
+}
+
+size_t kda_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                              int32_t num_seqs) {
+    return kda_fwd_split_workspace_size(B, T, H, K, V, num_seqs, 0);
 }
 
 size_t gdn_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
@@ -185,14 +318,14 @@ size_t gdn_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_
     return kda_fwd_workspace_size(B, T, H, K, V, num_seqs);
 }
 
-int kda_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
-            const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
-            float scale, const float* initial_state, float* final_state,
-            const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
-            int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
-            void* stream) {
+int kda_fwd_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                  const uint16_t* beta, const float* A_log, const float* dt_bias,
+                  float lower_bound, float scale, const float* initial_state,
+                  float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                  int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                  size_t workspace_bytes, int32_t segment_chunks, void* stream) {
     Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, cu_seqlens != nullptr,
-             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale};
+             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale, segment_chunks};
     int st = check_kda_gate(T, g, A_log, dt_bias, lower_bound);
     if (st != KDA_OK) return st;
     int32_t N = 0;
@@ -206,13 +339,24 @@ int kda_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
     return run(c, N, p, false, static_cast<hipStream_t>(stream));
 }
 
-int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
-            const uint16_t* beta, float scale, const float* initial_state, float* final_state,
+int kda_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+            const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
+            float scale, const float* initial_state, float* final_state,
             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
             int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
             void* stream) {
+    return kda_fwd_split(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
+                         final_state, cu_seqlens, num_seqs, B, T, H, K, V, o, workspace,
+                         workspace_bytes, 0, stream);
+}
+
+int gdn_fwd_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                  const uint16_t* beta, float scale, const float* initial_state,
+                  float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                  int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                  size_t workspace_bytes, int32_t segment_chunks, void* stream) {
     Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, cu_seqlens != nullptr,
-             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale};
+             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale, segment_chunks};
     if (T > 0 && !g) return KDA_ERR_INVALID_ARG;
     int32_t N = 0;
     int st = check_common(c, N);
@@ -222,13 +366,22 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
     return run(c, N, p, true, static_cast<hipStream_t>(stream));
 }
 
+int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+            const uint16_t* beta, float scale, const float* initial_state, float* final_state,
+            const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+            int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
+            void* stream) {
+    return gdn_fwd_split(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens,
+                         num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, 0, stream);
+}
+
 int kda_prep(const uint16_t* q, const uint16_t* k, const uint16_t* g, const uint16_t* beta,
              const float* A_log, const float* dt_bias, float lower_bound,
              const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
              int32_t K, int32_t V, void* workspace, size_t workspace_bytes, void* stream) {
     // v and o are not touched by this stage; stand-ins satisfy the shared checks
     Common c{q, k, q, beta, nullptr, nullptr, cu_seqlens, cu_seqlens != nullptr, num_seqs, B,
-             T, H, K, V, const_cast<uint16_t*>(q), workspace, workspace_bytes, 1.f};
+             T, H, K, V, const_cast<uint16_t*>(q), workspace, workspace_bytes, 1.f, -1};
     int st = check_kda_gate(T, g, A_log, dt_bias, lower_bound);
     if (st != KDA_OK) return st;
     int32_t N = 0;
@@ -246,7 +399,7 @@ int gdn_prep(const uint16_t* q, const uint16_t* k, const float* g, const uint16_
              const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
              int32_t K, int32_t V, void* workspace, size_t workspace_bytes, void* stream) {
     Common c{q, k, q, beta, nullptr, nullptr, cu_seqlens, cu_seqlens != nullptr, num_seqs, B,
-             T, H, K, V, const_cast<uint16_t*>(q), workspace, workspace_bytes, 1.f};
+             T, H, K, V, const_cast<uint16_t*>(q), workspace, workspace_bytes, 1.f, -1};
     if (T > 0 && !g) return KDA_ERR_INVALID_ARG;
     int32_t N = 0;
     int st = check_common(c, N);
@@ -261,7 +414,7 @@ int kda_recur(const uint16_t* v, float scale, const float* initial_state, float*
               int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes, void* stream) {
     // q, k, beta are not read by this stage; v stands in for them in the shared checks
     Common c{v, v, v, v, initial_state, final_state, nullptr, varlen != 0, num_seqs, B, T, H,
-             K, V, o, workspace, workspace_bytes, scale};
+             K, V, o, workspace, workspace_bytes, scale, -1};
     int32_t N = 0;
     int st = check_common(c, N);
     if (st != KDA_OK) return st;

@@ -24,6 +24,7 @@ struct PrepArgs {
     const int32_t* seq_start;  // packed: [n_seqs + 1] flattened token offsets
     const int32_t* chunk_off;  // packed: [n_seqs + 1] first chunk slot of each sequence
     unsigned char* rec;        // [slots, H, record bytes]
+    float* bound;              // [slots, H]: sum over the chunk of max_c log2 a (<= 0)
 };
 
 struct RecurArgs {
@@ -40,6 +41,15 @@ struct RecurArgs {
     int32_t T;
     const int32_t* seq_start;
     const int32_t* chunk_off;
+    // Sequence splitting (all null / 0 for the plain forward pass):
+    const int32_t* final_map;  // [n_seqs] or null: final state of sequence n goes to
+                               // final_state[final_map[n]] (skipped when < 0)
+    float* trans_out;          // [n_seqs, H, K, K] or null: also run K transition
+                               // columns (identity start, zero values) and store them
+    int32_t* trans_flag;       // [n_seqs, H]: 1 when trans_out was computed, 0 when the
+                               // bound showed the transition negligible (not computed)
+    const float* bound;        // [slots, H] chunk bounds from kda_prep (log2)
+    float bound_limit;         // a transition with a summed bound below this is negligible
 };
 
 struct DecodeArgs {
@@ -61,6 +71,22 @@ struct DecodeArgs {
     int32_t n_pairs;
 };
 
+struct SplitScanArgs {
+    const float* initial_state;  // [n_seqs, H, K, V] or null (zeros)
+    const float* nstate;         // [virtual, H, K, V]: segment results from a zero start
+    const float* trans;          // [virtual, H, K, K]: segment transitions
+    const int32_t* trans_flag;   // [virtual, H]: transition computed (else negligible)
+    const int32_t* vfirst;       // [n_seqs + 1]: first segment of each sequence
+    float* s_in;                 // [virtual, H, K, V]: state entering each segment
+    int32_t H;
+    int32_t V;
+    int32_t n_seqs;
+};
+
+void launch_seg_table(const int32_t* seq_start, const int32_t* chunk_off, int32_t n_seqs,
+                      int32_t L, int32_t n_virt_max, int32_t* vseq_start, int32_t* vchunk_off,
+                      int32_t* final_map, int32_t* vfirst, hipStream_t stream);
+void launch_split_scan(const SplitScanArgs& a, int K, hipStream_t stream);
 void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t total_tokens,
                       int32_t* seq_start, int32_t* chunk_off, hipStream_t stream);
 void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream);

@@ -118,6 +118,7 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) bf16x8 kd0_s[NB == 2 ? KS * 64 : 1];  // block 0
     __shared__ __attribute__((aligned(16))) floatx4 t00_s[64];       // block 0's T, D layout
     __shared__ float beta0_s[16];
+    __shared__ float dmax_s[NB];  // per block: sum over rows of the row's largest log2 decay
 
     const int slot = blockIdx.x;
     const int h = blockIdx.y;
@@ -193,10 +194,18 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
 
     // ---- in-block inclusive prefix sums of the log2 decay (padding rows add 0)
     float G[KS][8];  // KDA: per channel; GDN uses G[0][0] as the row's value
+    // Also the chunk's bound on its state transition: for one token,
+    // ||(I - b k^ k^T) Diag(a)||_2 <= max_c a_c (k^ is a unit vector and b is in
+    // [0, 1]), so the sum over the chunk's tokens of max_c log2 a_c bounds the
+    // log2 norm of the chunk's transition.  Sequence splitting uses it to skip
+    // propagating a state through a segment that provably forgets it.
+    float rowmax;
     if constexpr (GDN) {
-        G[0][0] = row_scan16(valid ? graw * LOG2E : 0.f);
+        rowmax = valid ? graw * LOG2E : 0.f;
+        G[0][0] = row_scan16(rowmax);
         if (m == 15 && g == 0) gend_s[blk][0] = G[0][0];
     } else {
+        rowmax = -INFINITY;
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             float x[8];
@@ -207,6 +216,7 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
             for (int e = 0; e < 8; ++e) {
                 const float la =
                     valid ? fmaxf(a.lower_bound, -rate * softplus_f(x[e] + dv[e])) * LOG2E : 0.f;
+                rowmax = fmaxf(rowmax, la);
                 G[j][e] = row_scan16(la);
             }
             if (m == 15) {  // the block total of these channels
@@ -216,8 +226,20 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
                 *reinterpret_cast<floatx4*>(&gend_s[blk][32 * j + 8 * g + 4]) = hi;
             }
         }
+        rowmax = fmaxf(rowmax, __shfl_xor(rowmax, 16, 64));
+        rowmax = fmaxf(rowmax, __shfl_xor(rowmax, 32, 64));
+    }
+    {
+        const float dsum = row_scan16(rowmax);  // rows 0..m of the block
+        if (m == 15 && g == 0) dmax_s[blk] = dsum;
     }
     __syncthreads();
+    if (threadIdx.x == 0) {
+        float d = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) d += dmax_s[bb];
+        a.bound[(int64_t)slot * a.H + h] = d;
+    }
 
     // ---- decay factors, record fragments, in-block (and cross-block) products.
     // mfma32(X, Y) gives D = X Y^T: lane (n, g) holds element i of D at row

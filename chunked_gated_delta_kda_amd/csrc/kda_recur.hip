@@ -27,7 +27,7 @@
 // waves (one compute and one loader wave per SIMD at NW = NL = 4):
 //   loader waves: each lane keeps 16-byte slices of the record and of the V
 //     tile of DEPTH chunks in flight in registers and writes chunk c + 2 to
-//     one of three LDS buffers during iteration c;
+//     one of two LDS buffers during iteration c;
 //   compute waves: during iteration c they compute chunk c and read the
 //     critical-path operands of chunk c + 1 (nKG, Tb, V) into registers.
 // One barrier per chunk separates the iterations.
@@ -51,30 +51,52 @@ struct StageLayout {
     static constexpr int PADDED = PPL * LTHREADS * 16;  // LDS bytes per buffer
 };
 
-template <int K, int NW, int CT, int NL, int DEPTH>
-__global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) {
+// OCC: workgroups per CU the register allocation must allow (1 or 2).
+template <int K, int NW, int CT, int NL, int DEPTH, int OCC>
+__global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
+    OCC * (NW + NL) / 4))) void kda_recur_kernel(RecurArgs a) {
     static_assert(DEPTH % 2 == 0 && DEPTH >= 2, "the loop is unrolled by DEPTH and by 2");
     using R = Rec<K>;
     using L = StageLayout<K, NW, CT, NL>;
     constexpr int KS = K / 32, KT = K / 16;
-    __shared__ __attribute__((aligned(16))) unsigned char stage[3][L::PADDED];
+    // Two buffers: during iteration c the compute waves read chunk c + 1's
+    // buffer while the loaders overwrite chunk c's, whose operands have been
+    // in registers since the previous barrier.
+    __shared__ __attribute__((aligned(16))) unsigned char stage[2][L::PADDED];
 
     // XCD-aware placement: workgroups are dealt to the 8 XCDs round robin, so
     // blocks b and b + 8 share an XCD (and its L2).  The VS column blocks of
     // one (sequence, head) read the same records; give them indices that
     // differ by multiples of 8.
-    const int VS = a.V / L::VCOLS;
+    const int TC = a.trans_out ? K : 0;  // transition columns after the V value columns
+    const int VS = (a.V + TC) / L::VCOLS;
     const int b = blockIdx.x;
     const int pair = (b / (8 * VS)) * 8 + (b & 7);
     const int vs = (b >> 3) % VS;
     if (pair >= a.n_seqs * a.H) return;  // grid padded to a multiple of 8 * VS
     const int h = pair % a.H, n = pair / a.H;
-    const int cb = vs * L::VCOLS;  // the block's first value column
+    const int cb = vs * L::VCOLS;  // the block's first column (value, then transition)
+    // A transition block runs the recurrence on columns of the identity with
+    // zero values: its final "state" is the sequence's K x K transition M, so
+    // that S_end = M S_start + (the result from a zero start).
+    const bool trans = cb >= a.V;
 
     int64_t t0, t1;
     int s0, s1;
     seq_span(a, n, t0, t1, s0, s1);
     const int nch = s1 - s0;
+    if (trans) {
+        // ||M||_2 <= 2^(sum of the chunk bounds): when that is negligible the
+        // transition is not needed (and not computed).  Every wave reaches the
+        // same decision before any barrier.
+        float sum = 0.f;
+        for (int c = threadIdx.x & 63; c < nch; c += 64) sum += a.bound[(int64_t)(s0 + c) * a.H + h];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+        const bool needed = !(sum < a.bound_limit);
+        if (cb == a.V && threadIdx.x == 0) a.trans_flag[(int64_t)n * a.H + h] = needed ? 1 : 0;
+        if (!needed) return;
+    }
     // Both roles run the same number of iterations (one barrier each), rounded
     // up to the unroll factor; iterations past the last chunk only synchronise.
     const int nround = (nch + DEPTH - 1) / DEPTH * DEPTH;
@@ -90,7 +112,8 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
         const int ltid = tid - 64 * NW;
         const unsigned char* rec_h = a.rec + (int64_t)h * R::BYTES;
         const int64_t rec_stride = (int64_t)a.H * R::BYTES;
-        const uint16_t* vcol = a.v + (int64_t)h * a.V + cb;
+        // transition blocks load a value block too (in bounds, never used)
+        const uint16_t* vcol = a.v + (int64_t)h * a.V + (trans ? 0 : cb);
         // Register ring: slice j of chunk c lives in ring[c % DEPTH][j].
         u32x4 ring[DEPTH][L::PPL];
         // Every lane issues exactly PPL loads per chunk with no branch: slice
@@ -126,18 +149,24 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
             }
         };
         // slices past the end land in the buffer's padding
-        auto commit = [&](const u32x4 (&src)[L::PPL], unsigned char* buf) {
+        // V rows of padding tokens (and the whole V tile of a transition block)
+        // are written as zeros, so the compute waves read V without masking
+        auto commit = [&](const u32x4 (&src)[L::PPL], unsigned char* buf, int c) {
+            const int nvalid = trans ? 0 : (int)min((int64_t)C, t1 - (t0 + (int64_t)C * c));
+            const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int j = 0; j < L::PPL; ++j)
-                *reinterpret_cast<u32x4*>(buf + (j * L::LTHREADS + ltid) * 16) = src[j];
+                *reinterpret_cast<u32x4*>(buf + (j * L::LTHREADS + ltid) * 16) =
+                    lane_rec[j] || lane_tok[j] < nvalid ? src[j] : zero;
         };
         static_for<0, DEPTH>([&](auto d) { issue(ring[d], d); });
-        commit(ring[0], stage[0]);
-        commit(ring[1], stage[1]);
+        commit(ring[0], stage[0], 0);
         issue(ring[0], DEPTH);
+        __syncthreads();  // chunk 0 is in buffer 0
+        commit(ring[1], stage[1], 1);
         issue(ring[1], DEPTH + 1);
-        __syncthreads();
-        int s2b = 2;  // buffer of chunk c + 2
+        __syncthreads();  // chunk 1 is in buffer 1; chunk 0's operands are in registers
+        int s2b = 0;  // buffer of chunk c + 2: c % 2
         for (int base = 0; base < nround; base += DEPTH) {
             static_for<0, DEPTH>([&](auto u) {
                 constexpr int nx2 = (u + 2) % DEPTH;  // ring slot of chunk c + 2
@@ -145,10 +174,10 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
                 // unconditional (past the end: clamped re-reads into buffers no
                 // one reads), so the compiler sees a fixed order of loads and
                 // waits only for the oldest chunk in flight
-                commit(ring[nx2], stage[s2b]);
+                commit(ring[nx2], stage[s2b], c + 2);
                 issue(ring[nx2], c + 2 + DEPTH);
                 __syncthreads();
-                s2b = s2b == 2 ? 0 : s2b + 1;
+                s2b ^= 1;
             });
         }
         return;
@@ -167,10 +196,15 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
 #pragma unroll
         for (int t = 0; t < KT; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[ct][t][i] = a.initial_state ? a.initial_state[st + 16 * ct +
-                                                                (int64_t)tile_channel(t, 4 * lg + i) * a.V]
-                                              : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int row = tile_channel(t, 4 * lg + i);
+                if (trans)  // identity column cb + cw + 16 ct + lr - V
+                    S[ct][t][i] = row == cb + cw + 16 * ct + lr - a.V ? 1.f : 0.f;
+                else
+                    S[ct][t][i] =
+                        a.initial_state ? a.initial_state[st + 16 * ct + (int64_t)row * a.V] : 0.f;
+            }
+    const bool store_o = a.o != nullptr && !trans;
 
     // Every operand of a chunk sits in registers when its iteration starts:
     // each fragment of chunk c + 1 is read from its LDS buffer right after
@@ -186,8 +220,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
         floatx4 gc[KT];
         floatx4 v[CT][NB];
     };
-    auto read_nkg_v = [&](Frags& f, const unsigned char* buf, int c) {
-        const int nvalid = (int)min((int64_t)C, t1 - (t0 + (int64_t)C * c));
+    auto read_nkg_v = [&](Frags& f, const unsigned char* buf) {
         const uint16_t* vt = reinterpret_cast<const uint16_t*>(buf + L::V_OFF);
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) {
@@ -199,9 +232,8 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int tok = 16 * bb + 4 * lg + i;  // padding tokens read 0
-                    const float v = bf2f(vt[tok * L::VCOLS + cw + 16 * ct + lr]);
-                    f.v[ct][bb][i] = tok < nvalid ? v : 0.f;
+                    const int tok = 16 * bb + 4 * lg + i;  // padding rows hold zeros
+                    f.v[ct][bb][i] = bf2f(vt[tok * L::VCOLS + cw + 16 * ct + lr]);
                 }
         }
     };
@@ -266,7 +298,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
                     Y[ct][bb] = mfma32(f.nkg[bb][j], sb[ct][j], Y[ct][bb]);
-        read_nkg_v(f, next, c + 1);
+        read_nkg_v(f, next);
         // O_ob^T = S^T QG_ob^T for each 16-token output block ob
         floatx4 OT[CT][NB];
 #pragma unroll
@@ -336,7 +368,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 // OT[ct][ob][i] = O[token 16 ob + lr][column cb + cw + 16 ct + 4 lg + i]
-                if (16 * ob + lr < nvalid) {
+                if (store_o && 16 * ob + lr < nvalid) {
                     bf16x4 ov;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) ov[i] = (bf16)(a.scale * OT[ct][ob][i]);
@@ -347,31 +379,45 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
     };
 
     if (nch > 0) {
-        __syncthreads();  // chunks 0 and 1 are in buffers 0 and 1
+        __syncthreads();  // chunk 0 is in buffer 0
         Frags fr;
-        read_nkg_v(fr, stage[0], 0);
+        read_nkg_v(fr, stage[0]);
         read_qg(fr, stage[0]);
         read_gc(fr, stage[0]);
         read_tb(fr, stage[0]);
         read_kdt(fr, stage[0]);
         read_aqk(fr, stage[0]);
-        int s1b = 1;  // buffer of chunk c + 1: (c + 1) % 3
+        __syncthreads();  // chunk 1 is in buffer 1; buffer 0 may be overwritten
+        int s1b = 1;  // buffer of chunk c + 1: (c + 1) % 2
         for (int c = 0; c < nround; ++c) {
             if (c < nch) compute(fr, stage[s1b], c);  // uniform over the workgroup
             __syncthreads();
-            s1b = s1b == 2 ? 0 : s1b + 1;
+            s1b ^= 1;
         }
     }
 
-    if (a.final_state) {
+    if (trans) {
+        float* mo = a.trans_out + ((int64_t)n * a.H + h) * K * K + (cb - a.V) + cw + lr;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int t = 0; t < KT; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    a.final_state[st + 16 * ct + (int64_t)tile_channel(t, 4 * lg + i) * a.V] =
-                        S[ct][t][i];
+                    mo[16 * ct + (int64_t)tile_channel(t, 4 * lg + i) * K] = S[ct][t][i];
+    } else if (a.final_state) {
+        const int nf = a.final_map ? a.final_map[n] : n;
+        if (nf >= 0) {
+            const int64_t sf = ((int64_t)nf * a.H + h) * K * a.V + cb + cw + lr;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int t = 0; t < KT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a.final_state[sf + 16 * ct + (int64_t)tile_channel(t, 4 * lg + i) * a.V] =
+                            S[ct][t][i];
+        }
     }
 }
 
@@ -393,21 +439,51 @@ __global__ __launch_bounds__(64 * (NW + NL)) void kda_recur_kernel(RecurArgs a) 
 #define KDA_RECUR_LOADERS 2
 #endif
 #ifndef KDA_RECUR_DEPTH
-#define KDA_RECUR_DEPTH 4
+#define KDA_RECUR_DEPTH 4  // one workgroup per CU
+#endif
+#ifndef KDA_RECUR_DEPTH2
+#define KDA_RECUR_DEPTH2 2  // two workgroups per CU (fewer registers)
 #endif
 constexpr int RECUR_WAVES = KDA_RECUR_WAVES;
 constexpr int RECUR_TILES = KDA_RECUR_TILES;
 constexpr int RECUR_LOADERS = KDA_RECUR_LOADERS;
 constexpr int RECUR_DEPTH = KDA_RECUR_DEPTH;
+constexpr int RECUR_DEPTH2 = KDA_RECUR_DEPTH2;
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// A grid with more workgroups than CUs runs the variant whose registers
+// allow two workgroups per CU (the chain of each is latency-bound, so two
+// interleave well); up to one per CU, the variant with the larger register
+// budget.
 template <int K>
 void launch_recur_t(const RecurArgs& a, hipStream_t stream) {
-    const int vs = a.V / (16 * RECUR_TILES * RECUR_WAVES);
+    const int vs = (a.V + (a.trans_out ? K : 0)) / (16 * RECUR_TILES * RECUR_WAVES);
     const int64_t pairs = (int64_t)a.n_seqs * a.H;
     const int64_t groups = (pairs + 7) / 8;  // the grid covers whole groups of 8 pairs
-    hipLaunchKernelGGL(
-        (kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS, RECUR_DEPTH>),
-        dim3((unsigned)(groups * 8 * vs)), dim3(64 * (RECUR_WAVES + RECUR_LOADERS)), 0, stream, a);
+    const int64_t blocks = groups * 8 * vs;
+    const dim3 grid((unsigned)blocks), block(64 * (RECUR_WAVES + RECUR_LOADERS));
+    if (pairs * vs > device_cus())
+        hipLaunchKernelGGL(
+            (kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS, RECUR_DEPTH2, 2>), grid,
+            block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(
+            (kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS, RECUR_DEPTH, 1>), grid,
+            block, 0, stream, a);
 }
 
 void launch_recur(const RecurArgs& a, int K, hipStream_t stream) {

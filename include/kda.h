@@ -77,7 +77,8 @@ enum kda_status {
     KDA_ERR_LAUNCH = 4       /* a kernel launch failed */
 };
 
-/* Bytes of device workspace that kda_fwd needs.  num_seqs: the number of
+/* Bytes of device workspace that kda_fwd needs (including what its automatic
+ * sequence splitting needs, see kda_fwd_split).  num_seqs: the number of
  * packed sequences when cu_seqlens will be passed, else B.  Pure host
  * function; returns 0 for invalid sizes. */
 size_t kda_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
@@ -105,6 +106,41 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
             int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
             void* stream);
+
+/* kda_fwd / gdn_fwd with explicit control of sequence splitting.
+ *
+ * A sequence is one chain of dependent chunk steps, so a batch of few long
+ * sequences leaves most of the GPU idle.  Splitting cuts every sequence into
+ * segments of segment_chunks chunks that run in parallel: a first pass runs
+ * each segment from a zero state (and, when its bound says the entering
+ * state is not forgotten, its K x K transition from an identity start), a
+ * scan over the segments gives each segment its true entering state, and a
+ * second pass recomputes the segments with outputs.  The result equals the
+ * unsplit pass up to rounding.  This is context parallelism inside one
+ * card: the cuLA README (section "Benchmarks") reports it for FlashKDA on
+ * long sequences, the FlashQLA summary (section "핵심 기능") switches it on
+ * from the gate's decay.
+ *
+ * segment_chunks: < 0 never split; 0 automatic (what kda_fwd / gdn_fwd do:
+ * only when the sequences are long and (sequence, head) pairs too few to
+ * fill the GPU); > 0 segments of that many 32-token chunks.  The workspace
+ * must hold kda_fwd_split_workspace_size(..., segment_chunks) bytes; the
+ * other arguments, layouts and errors are those of kda_fwd / gdn_fwd. */
+size_t kda_fwd_split_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                    int32_t num_seqs, int32_t segment_chunks);
+
+int kda_fwd_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                  const uint16_t* beta, const float* A_log, const float* dt_bias,
+                  float lower_bound, float scale, const float* initial_state,
+                  float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                  int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                  size_t workspace_bytes, int32_t segment_chunks, void* stream);
+
+int gdn_fwd_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                  const uint16_t* beta, float scale, const float* initial_state,
+                  float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                  int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                  size_t workspace_bytes, int32_t segment_chunks, void* stream);
 
 /* The two stages of kda_fwd / gdn_fwd, callable on their own (same
  * conventions; kda_fwd is exactly kda_prep followed by kda_recur).

@@ -42,8 +42,11 @@ def test_workspace_size_formula(lib):
     rec = 3 * C * 128 * 2 + 2 * C * C * 2 + 128 * 4  # bytes per (chunk, head) at K=128
     B, T, H, N = 2, 2048, 32, 2
     meta = 256
-    want = meta + ((B * T + C - 1) // C + N) * H * rec
-    assert kda.workspace_size(B, T, H, 128, 128) == want
+    slots = (B * T + C - 1) // C + N  # the packed-sequence bound covers both layouts
+    bound = (slots * H * 4 + 255) // 256 * 256  # one fp32 transition bound per (chunk, head)
+    want = meta + slots * H * rec + bound
+    assert kda.workspace_size(B, T, H, 128, 128) == want  # 64 pairs x 4 blocks: no splitting
+    assert kda.workspace_size(B, T, H, 128, 128, segment_chunks=-1) == want
     assert kda.workspace_size(1, 100, 1, 96, 128) == 0  # unsupported K
     assert kda.workspace_size(0, 100, 1, 128, 128) == 0
 
@@ -120,3 +123,19 @@ def test_gdn_decode_rejects_on_host(lib):
     args[10] = 128
     args[7] = None
     assert lib.gdn_decode(*args) == 1  # null state_out
+
+
+def test_split_workspace_grows_with_segments(lib):
+    """Explicit splitting adds the segment tables, flags, two [segments, H, K, V]
+    state buffers and the [segments, H, K, K] transitions."""
+    B, T, H, K, V = 1, 8192, 2, 128, 128
+    plain = kda.workspace_size(B, T, H, K, V, segment_chunks=-1)
+    slots = (B * T + 31) // 32 + 1
+    for L in (16, 64):
+        nv = 1 + (slots + L - 1) // L
+        extra = kda.workspace_size(B, T, H, K, V, segment_chunks=L) - plain
+        states = nv * H * K * V * 4
+        assert extra >= 2 * states + nv * H * K * K * 4
+        assert extra < 2 * states + nv * H * K * K * 4 + 4096
+    # automatic: 2 heads x 4 column blocks is far too few workgroups, so it splits
+    assert kda.workspace_size(B, T, H, K, V) > plain
