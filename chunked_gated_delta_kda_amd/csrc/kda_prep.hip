@@ -56,6 +56,20 @@ __device__ __forceinline__ float row_scan16(float x) {
     return x;
 }
 
+// Many independent scans at once, one DPP step across all of them at a time,
+// so no step waits on the one before it in the same scan.
+template <int N>
+__device__ __forceinline__ void row_scan16_n(float* x) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR1, 0xf, 0xf, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR2, 0xf, 0xf, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR4, 0xf, 0xf, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR8, 0xf, 0xf, false);
+}
+
 __device__ __forceinline__ float lane_val(float x, int src) { return __shfl(x, src, 64); }
 
 __device__ __forceinline__ halfx4 to_h4(floatx4 x) {
@@ -119,6 +133,7 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) floatx4 t00_s[64];       // block 0's T, D layout
     __shared__ float beta0_s[16];
     __shared__ float dmax_s[NB];  // per block: sum over rows of the row's largest log2 decay
+    __shared__ __attribute__((aligned(16))) float eg_s[NB][K];  // KDA: 2^(block total) per channel
 
     const int slot = blockIdx.x;
     const int h = blockIdx.y;
@@ -217,8 +232,12 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
                 const float la =
                     valid ? fmaxf(a.lower_bound, -rate * softplus_f(x[e] + dv[e])) * LOG2E : 0.f;
                 rowmax = fmaxf(rowmax, la);
-                G[j][e] = row_scan16(la);
+                G[j][e] = la;
             }
+        }
+        row_scan16_n<KS * 8>(&G[0][0]);
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
             if (m == 15) {  // the block total of these channels
                 const floatx4 lo = {G[j][0], G[j][1], G[j][2], G[j][3]};
                 const floatx4 hi = {G[j][4], G[j][5], G[j][6], G[j][7]};
@@ -234,12 +253,17 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         if (m == 15 && g == 0) dmax_s[blk] = dsum;
     }
     __syncthreads();
+    if constexpr (!GDN) {
+        // 2^(block total) per channel, once per workgroup rather than per row
+        for (int c = threadIdx.x; c < NB * K; c += 64 * NB) eg_s[c / K][c % K] = exp2_hw(gend_s[c / K][c % K]);
+    }
     if (threadIdx.x == 0) {
         float d = 0.f;
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) d += dmax_s[bb];
         a.bound[(int64_t)slot * a.H + h] = d;
     }
+    if constexpr (!GDN) __syncthreads();
 
     // ---- decay factors, record fragments, in-block (and cross-block) products.
     // mfma32(X, Y) gives D = X Y^T: lane (n, g) holds element i of D at row
@@ -254,29 +278,55 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         unpack8(kr[j], kn);
 #pragma unroll
         for (int e = 0; e < 8; ++e) { qn[e] *= iq; kn[e] *= ik; }
-        float gown[8], goth[8];  // this block's and the other block's totals
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = GDN ? 0 : 32 * j + 8 * g + e;
-            gown[e] = gend_s[blk][c];
-            goth[e] = NB == 2 ? gend_s[1 - blk][c] : 0.f;
-        }
         float kg[8], qg[8], kgl[8], qgl[8], kil[8], kdl[8], kd[8];
+        if constexpr (GDN) {
+            // any log decay <= 0: only exponents <= 0 are formed
+            float gown[8], goth[8];  // this block's and the other block's totals
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float Gl = GDN ? G[0][0] : G[j][e];
-            const float gl = exp2_hw(Gl);
-            kgl[e] = kn[e] * gl;                       // block-local Gam
-            qgl[e] = qn[e] * gl;
-            kil[e] = GDN ? kn[e] : kn[e] * exp2_hw(-Gl);
-            kdl[e] = kn[e] * exp2_hw(gown[e] - Gl);   // decay to the block's end
-            // global factors: block 1 carries block 0's total decay, block 0's Kd
-            // carries block 1's
-            const float before = (NB == 2 && blk == 1) ? exp2_hw(goth[e]) : 1.f;
-            const float after = (NB == 2 && blk == 0) ? exp2_hw(goth[e]) : 1.f;
-            kg[e] = kgl[e] * before;
-            qg[e] = qgl[e] * before;
-            kd[e] = kdl[e] * after;
+            for (int e = 0; e < 8; ++e) {
+                gown[e] = gend_s[blk][0];
+                goth[e] = NB == 2 ? gend_s[1 - blk][0] : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float Gl = G[0][0];
+                const float gl = exp2_hw(Gl);
+                kgl[e] = kn[e] * gl;
+                qgl[e] = qn[e] * gl;
+                kil[e] = kn[e];
+                kdl[e] = kn[e] * exp2_hw(gown[e] - Gl);
+                const float before = (NB == 2 && blk == 1) ? exp2_hw(goth[e]) : 1.f;
+                const float after = (NB == 2 && blk == 0) ? exp2_hw(goth[e]) : 1.f;
+                kg[e] = kgl[e] * before;
+                qg[e] = qgl[e] * before;
+                kd[e] = kdl[e] * after;
+            }
+        } else {
+            // the floor bounds every block's |G| by 80 nats, so 2^-G and the
+            // per-channel 2^(total) are finite: Kd = (k^ 2^-G) 2^(own total)
+            float eown[8], eoth[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = 32 * j + 8 * g + e;
+                eown[e] = eg_s[blk][c];
+                eoth[e] = NB == 2 ? eg_s[NB - 1 - blk][c] : 1.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float Gl = G[j][e];
+                const float gl = exp2_hw(Gl);
+                kgl[e] = kn[e] * gl;                       // block-local Gam
+                qgl[e] = qn[e] * gl;
+                kil[e] = kn[e] * exp2_hw(-Gl);
+                kdl[e] = kil[e] * eown[e];                 // decay to the block's end
+                // global factors: block 1 carries block 0's total decay, block
+                // 0's Kd carries block 1's
+                const float before = (NB == 2 && blk == 1) ? eoth[e] : 1.f;
+                const float after = (NB == 2 && blk == 0) ? eoth[e] : 1.f;
+                kg[e] = kgl[e] * before;
+                qg[e] = qgl[e] * before;
+                kd[e] = kdl[e] * after;
+            }
         }
         *reinterpret_cast<bf16x8*>(rec + R::NKG + ((blk * KS + j) * 64 + L) * 16) = pack8(kg, -1.f);
         *reinterpret_cast<bf16x8*>(rec + R::QG + ((blk * KS + j) * 64 + L) * 16) = pack8(qg);
@@ -315,8 +365,12 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
             float gcv[8];  // the chunk's total decay of this lane's channels
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int c = GDN ? 0 : 32 * j + 8 * g + e;
-                gcv[e] = exp2_hw(gend_s[0][c] + (NB == 2 ? gend_s[NB - 1][c] : 0.f));
+                if constexpr (GDN) {
+                    gcv[e] = exp2_hw(gend_s[0][0] + (NB == 2 ? gend_s[NB - 1][0] : 0.f));
+                } else {
+                    const int c = 32 * j + 8 * g + e;
+                    gcv[e] = eg_s[0][c] * (NB == 2 ? eg_s[NB - 1][c] : 1.f);
+                }
             }
             const floatx4 lo = {gcv[0], gcv[1], gcv[2], gcv[3]};
             const floatx4 hi = {gcv[4], gcv[5], gcv[6], gcv[7]};
