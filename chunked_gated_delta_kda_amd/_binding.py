@@ -19,7 +19,8 @@ _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED"
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_fwd", "gdn_fwd", "kda_fwd_workspace_size", "gdn_fwd_workspace_size",
            "kda_fwd_split_workspace_size", "kda_fwd_split", "gdn_fwd_split", "kda_prep",
-           "gdn_prep", "kda_recur", "kda_decode", "gdn_decode", "kda_status_str", "kda_version")
+           "gdn_prep", "kda_recur", "kda_decode", "gdn_decode", "kda_bwd_workspace_size",
+           "kda_bwd", "gdn_bwd", "kda_status_str", "kda_version")
 
 
 class LibKdaError(RuntimeError):
@@ -72,7 +73,14 @@ def load(path: Path | str | None = None):
     lib.gdn_decode.restype = ctypes.c_int
     lib.gdn_decode.argtypes = [u16p, u16p, u16p, f32p, u16p, f32, f32p, f32p, i32, i32, i32, i32,
                                u16p, vp]
-    for name in ("kda_fwd_workspace_size", "gdn_fwd_workspace_size"):
+    lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_bwd.argtypes = [u16p, u16p, u16p, u16p, u16p, f32p, f32p, f32, f32, f32p, i32p,
+                            i32, i32, i32, i32, i32, i32, u16p, f32p, u16p, u16p, u16p, u16p,
+                            u16p, f32p, f32p, f32p, vp, sz, vp]
+    lib.gdn_bwd.restype = ctypes.c_int
+    lib.gdn_bwd.argtypes = [u16p, u16p, u16p, f32p, u16p, f32, f32p, i32p, i32, i32, i32, i32,
+                            i32, i32, u16p, f32p, u16p, u16p, u16p, f32p, u16p, f32p, vp, sz, vp]
+    for name in ("kda_fwd_workspace_size", "gdn_fwd_workspace_size", "kda_bwd_workspace_size"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_size_t
         fn.argtypes = [i32] * 6
@@ -128,8 +136,8 @@ def _need(t, name, dtype, shape=None, device=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens, workspace,
-             kind, out=None, final_out=None, segment_chunks=None):
+def _shapes(q, k, v, beta, scale, initial_state, cu_seqlens):
+    """Checks of the forward inputs; returns (B, T, H, K, V, N, scale)."""
     torch = _torch()
     _need(q, "q", torch.bfloat16)
     if q.dim() != 4:
@@ -154,6 +162,14 @@ def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens
         _need(initial_state, "initial_state", torch.float32, (N, H, K, V), dev)
     if scale is None:
         scale = K ** -0.5
+    return B, T, H, K, V, N, float(scale)
+
+
+def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens, workspace,
+             kind, out=None, final_out=None, segment_chunks=None):
+    torch = _torch()
+    B, T, H, K, V, N, scale = _shapes(q, k, v, beta, scale, initial_state, cu_seqlens)
+    dev = q.device
     if out is None:
         out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
     else:
@@ -318,3 +334,82 @@ def gdn_decode(q, k, v, g, beta, scale=None, state=None, state_out=None, out=Non
     _check(load().gdn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), sc, _ptr(state),
                              _ptr(so), N, H, K, V, _ptr(o), stream))
     return o, so
+
+
+# ---------------------------------------------------------------- backward
+def bwd_workspace_size(B, T, H, K, V, num_seqs=None) -> int:
+    return int(load().kda_bwd_workspace_size(B, T, H, K, V, B if num_seqs is None else num_seqs))
+
+
+def _bwd_prepare(q, k, v, beta, do, scale, initial_state, dfinal, cu_seqlens, workspace,
+                 need_dh0):
+    torch = _torch()
+    B, T, H, K, V, N, scale = _shapes(q, k, v, beta, scale, initial_state, cu_seqlens)
+    a = dict(B=B, T=T, H=H, K=K, V=V, N=N, scale=scale,
+             stream=ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream))
+    dev = q.device
+    _need(do, "do", torch.bfloat16, (B, T, H, V), dev)
+    if dfinal is not None:
+        _need(dfinal, "dfinal", torch.float32, (N, H, K, V), dev)
+    need = bwd_workspace_size(B, T, H, K, V, N)
+    if need == 0:
+        raise LibKdaError(2, status_str(2))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif _nbytes(workspace) < need or workspace.device != dev:
+        raise LibKdaError(3, status_str(3))
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dbeta": torch.empty_like(beta),
+           "dh0": torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if need_dh0 else None}
+    a.update(workspace=workspace, out=out)
+    return a
+
+
+def kda_bwd(q, k, v, g, beta, A_log, dt_bias, do, lower_bound=-5.0, scale=None,
+            initial_state=None, dfinal=None, cu_seqlens=None, workspace=None, need_dh0=True):
+    """Gradients of kda_fwd for dL/do = ``do`` [B,T,H,V] bf16 and dL/d(final state) =
+    ``dfinal`` [N,H,K,V] fp32 (None: zero).  Returns a dict with dq, dk [B,T,H,K],
+    dv [B,T,H,V], dg [B,T,H,K], dbeta [B,T,H] (bf16), dA_log [H], ddt_bias [H,K]
+    and dh0 [N,H,K,V] (fp32; None unless ``need_dh0``)."""
+    torch = _torch()
+    a = _bwd_prepare(q, k, v, beta, do, scale, initial_state, dfinal, cu_seqlens, workspace,
+                     need_dh0)
+    B, T, H, K, V, N = (a[x] for x in "BTHKVN")
+    dev = q.device
+    _need(g, "g", torch.bfloat16, (B, T, H, K), dev)
+    _need(A_log, "A_log", torch.float32, (H,), dev)
+    _need(dt_bias, "dt_bias", torch.float32, None, dev)
+    if dt_bias.numel() != H * K:
+        raise ValueError("dt_bias must hold H * K values ([H, K] or [H * K])")
+    o = a["out"]
+    o["dg"] = torch.empty_like(g)
+    o["dA_log"] = torch.empty((H,), dtype=torch.float32, device=dev)
+    o["ddt_bias"] = torch.empty((H, K), dtype=torch.float32, device=dev)
+    ws = a["workspace"]
+    _check(load().kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                          _ptr(dt_bias), float(lower_bound), a["scale"], _ptr(initial_state),
+                          _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(do), _ptr(dfinal),
+                          _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o["dg"]),
+                          _ptr(o["dbeta"]), _ptr(o["dA_log"]), _ptr(o["ddt_bias"]),
+                          _ptr(o["dh0"]), _ptr(ws), _nbytes(ws), a["stream"]))
+    return o
+
+
+def gdn_bwd(q, k, v, g, beta, do, scale=None, initial_state=None, dfinal=None, cu_seqlens=None,
+            workspace=None, need_dh0=True):
+    """Gradients of gdn_fwd: dict with dq, dk, dv, dbeta (bf16), dg [B,T,H] and dh0
+    (fp32).  Arguments as kda_bwd."""
+    torch = _torch()
+    a = _bwd_prepare(q, k, v, beta, do, scale, initial_state, dfinal, cu_seqlens, workspace,
+                     need_dh0)
+    B, T, H, K, V, N = (a[x] for x in "BTHKVN")
+    _need(g, "g", torch.float32, (B, T, H), q.device)
+    o = a["out"]
+    o["dg"] = torch.empty_like(g)
+    ws = a["workspace"]
+    _check(load().gdn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), a["scale"],
+                          _ptr(initial_state), _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(do),
+                          _ptr(dfinal), _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]),
+                          _ptr(o["dg"]), _ptr(o["dbeta"]), _ptr(o["dh0"]), _ptr(ws),
+                          _nbytes(ws), a["stream"]))
+    return o

@@ -16,7 +16,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libkda.so"
-SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_decode.hip", "kda_split.hip"]
+SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_decode.hip", "kda_split.hip",
+           "kda_bwd.hip"]
 ARCH = "gfx950"
 
 
@@ -27,26 +28,49 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libkda)")
 
 
-def build(verbose: bool = False, extra_flags=()) -> Path:
-    """Compile every HIP source for gfx950 into PKG/libkda.so (atomic replace)."""
-    fd, tmp = tempfile.mkstemp(suffix=".so", dir=str(PKG))
-    os.close(fd)
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+# Sources whose kernels keep MFMA results in VGPRs (see FLAGS_VGPR_FORM).  The
+# backward gradient kernel is left to the compiler's default: its register
+# demand exceeds the VGPR file, and the VGPR-form rewrite crashes on it.
+VGPR_FORM = {"kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_decode.hip", "kda_split.hip"}
+
+
+def _compile(src: str, obj: Path, extra_flags) -> subprocess.CompletedProcess:
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
            "-Wall", "-Wno-unused-function",
            # no packed fp32 VALU ops anywhere: plain float code only
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # MFMA results in VGPRs: the kernels convert and rescale their
-           # accumulators on the VALU every chunk, so AGPR round trips would cost
-           "-mllvm", "-amdgpu-mfma-vgpr-form",
-           f"-I{INCLUDE}", f"-I{CSRC}", *extra_flags,
-           *[str(CSRC / s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        os.unlink(tmp)
-        raise RuntimeError(f"libkda build failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+           f"-I{INCLUDE}", f"-I{CSRC}", *extra_flags]
+    if src in VGPR_FORM:
+        # MFMA results in VGPRs: the kernels convert and rescale their
+        # accumulators on the VALU every chunk, so AGPR round trips would cost
+        cmd += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    cmd += [str(CSRC / src), "-o", str(obj)]
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(verbose: bool = False, extra_flags=()) -> Path:
+    """Compile every HIP source for gfx950 (in parallel) and link PKG/libkda.so
+    (atomic replace)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    with tempfile.TemporaryDirectory(dir=str(PKG)) as td:
+        objs = [Path(td) / (Path(s).stem + ".o") for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+            results = list(ex.map(lambda so: _compile(so[0], so[1], extra_flags),
+                                  zip(SOURCES, objs)))
+        for src, res in zip(SOURCES, results):
+            if verbose:
+                print(" ".join(res.args), flush=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"libkda build failed ({src}):\n{res.stderr}")
+        fd, tmp = tempfile.mkstemp(suffix=".so", dir=str(PKG))
+        os.close(fd)
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            os.unlink(tmp)
+            raise RuntimeError(f"libkda link failed:\n{res.stderr}")
+        os.replace(tmp, LIB)
     return LIB
 
 

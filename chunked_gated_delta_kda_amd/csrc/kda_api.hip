@@ -81,6 +81,41 @@ size_t workspace_bytes_for(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Backward pass, after the forward layout (tables, records, bounds): the
+// reverse-pass records, the chunk states and V - KG S of the forward sweep,
+// the state gradients and dL/dU' of the reverse sweep (bf16), and the
+// per-chunk sums of the gate-parameter gradients.
+struct BwdLayout {
+    unsigned char* brec;
+    uint16_t *hs, *zt, *dss, *dut;
+    float *part_dt, *part_alog;
+};
+
+size_t bwd_extra_bytes(int64_t slots, int32_t H, int32_t K, int32_t V) {
+    const size_t ch = (size_t)slots * H;
+    return align_up(ch * kda::record_bytes(K)) + 2 * align_up(ch * K * V * 2) +
+           2 * align_up(ch * V * kda::C * 2) + align_up(ch * K * 4) + align_up(ch * 4);
+}
+
+BwdLayout bwd_layout(unsigned char* p, int64_t slots, int32_t H, int32_t K, int32_t V) {
+    const size_t ch = (size_t)slots * H;
+    BwdLayout b{};
+    b.brec = p;
+    p += align_up(ch * kda::record_bytes(K));
+    b.hs = reinterpret_cast<uint16_t*>(p);
+    p += align_up(ch * K * V * 2);
+    b.dss = reinterpret_cast<uint16_t*>(p);
+    p += align_up(ch * K * V * 2);
+    b.zt = reinterpret_cast<uint16_t*>(p);
+    p += align_up(ch * V * kda::C * 2);
+    b.dut = reinterpret_cast<uint16_t*>(p);
+    p += align_up(ch * V * kda::C * 2);
+    b.part_dt = reinterpret_cast<float*>(p);
+    p += align_up(ch * K * 4);
+    b.part_alog = reinterpret_cast<float*>(p);
+    return b;
+}
+
 struct Common {
     const uint16_t *q, *k, *v, *beta;
     const float* initial_state;
@@ -254,6 +289,114 @@ int run_recur(const Common& c, int32_t N, hipStream_t stream) {
 int run(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t stream) {
     int st = run_prep(c, N, p, gdn, stream);
     return st != KDA_OK ? st : run_recur(c, N, stream);
+}
+
+size_t bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t N,
+                           bool varlen) {
+    const SplitPlan none{0, 0};
+    return align_up(workspace_bytes_for(B, T, H, K, V, N, varlen, none)) +
+           bwd_extra_bytes(max_slots(B, T, N, varlen), H, K, V);
+}
+
+struct BwdIO {
+    const uint16_t* d_o;
+    const float* d_final;
+    uint16_t *dq, *dk, *dv;
+    uint16_t* dg_kda;
+    float* dg_gdn;
+    uint16_t* dbeta;
+    float *dA_log, *ddt_bias, *dh0;
+};
+
+// The backward pass: kda_prep (forward records), the reverse-pass records,
+// the forward sweep that keeps every chunk's entering state, the reverse
+// sweep (state gradients, dv, dh0), the chunk gradient kernel and the
+// gate-parameter sums.
+int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& io,
+            hipStream_t stream) {
+    if (c.ws_bytes < bwd_workspace_bytes(c.B, c.T, c.H, c.K, c.V, N, c.varlen))
+        return KDA_ERR_WORKSPACE;
+    int st = run_prep(c, N, p, gdn, stream);
+    if (st != KDA_OK) return st;
+    const WsLayout w = layout(c, N);
+    const SplitPlan none{0, 0};
+    unsigned char* extra = static_cast<unsigned char*>(c.ws) +
+                           align_up(workspace_bytes_for(c.B, c.T, c.H, c.K, c.V, N, c.varlen, none));
+    const BwdLayout bl = bwd_layout(extra, w.slots, c.H, c.K, c.V);
+    (void)hipGetLastError();
+    kda::launch_bwd_rec(w.rec, bl.brec, c.K, w.slots * c.H, stream);
+    kda::RecurArgs r{};
+    r.v = c.v;
+    r.rec = w.rec;
+    r.initial_state = c.initial_state;
+    r.scale = c.scale;
+    r.H = c.H;
+    r.V = c.V;
+    r.n_seqs = N;
+    r.packed = c.varlen;
+    r.T = c.T;
+    r.seq_start = w.seq_start;
+    r.chunk_off = w.chunk_off;
+    r.chunk_state = bl.hs;
+    r.chunk_u = bl.zt;
+    kda::launch_recur(r, c.K, stream, kda::RECUR_STORE);
+    kda::RecurArgs rb = r;
+    rb.v = io.d_o;
+    rb.rec = bl.brec;
+    rb.initial_state = io.d_final;
+    rb.final_state = io.dh0;
+    rb.o = io.dv;
+    rb.chunk_state = bl.dss;
+    rb.chunk_u = bl.dut;
+    kda::launch_recur(rb, c.K, stream, kda::RECUR_BWD);
+    kda::BwdArgs ba{};
+    ba.q = c.q;
+    ba.k = c.k;
+    ba.g_kda = p.g_kda;
+    ba.g_gdn = p.g_gdn;
+    ba.beta = c.beta;
+    ba.A_log = p.A_log;
+    ba.dt_bias = p.dt_bias;
+    ba.lower_bound = p.lower_bound;
+    ba.scale = c.scale;
+    ba.d_o = io.d_o;
+    ba.dv = io.dv;
+    ba.rec = w.rec;
+    ba.hs = bl.hs;
+    ba.zt = bl.zt;
+    ba.dss = bl.dss;
+    ba.dut = bl.dut;
+    ba.dq = io.dq;
+    ba.dk = io.dk;
+    ba.dg_kda = io.dg_kda;
+    ba.dg_gdn = io.dg_gdn;
+    ba.dbeta = io.dbeta;
+    ba.part_dt = bl.part_dt;
+    ba.part_alog = bl.part_alog;
+    ba.H = c.H;
+    ba.n_seqs = N;
+    ba.packed = c.varlen;
+    ba.T = c.T;
+    ba.seq_start = w.seq_start;
+    ba.chunk_off = w.chunk_off;
+    kda::launch_bwd_chunk(ba, c.K, c.V, gdn, (int)w.slots, stream);
+    if (!gdn)
+        kda::launch_bwd_reduce(bl.part_dt, bl.part_alog, (int32_t)w.slots, c.H, c.K, io.ddt_bias,
+                               io.dA_log, stream);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+// Pointer checks of the backward outputs (and the output gradient).
+int check_bwd_io(const Common& c, const BwdIO& io, bool gdn) {
+    const bool tokens = c.T > 0;
+    if (tokens && (!io.d_o || !io.dq || !io.dk || !io.dv || !io.dbeta)) return KDA_ERR_INVALID_ARG;
+    if (tokens && (gdn ? !io.dg_gdn : !io.dg_kda)) return KDA_ERR_INVALID_ARG;
+    if (!gdn && (!io.dA_log || !io.ddt_bias)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(io.d_o, 16) || !aligned(io.dq, 16) || !aligned(io.dk, 16) ||
+        !aligned(io.dv, 16) || !aligned(io.dg_kda, 16) || !aligned(io.dh0, 16) ||
+        !aligned(io.d_final, 16))
+        return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
 }
 
 // Checks of the KDA gate arguments.
@@ -462,6 +605,60 @@ int gdn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const fl
     d.state_out = state_out;
     d.o = o;
     return run_decode(d, N, H, K, V, true, static_cast<hipStream_t>(stream));
+}
+
+size_t kda_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                              int32_t num_seqs) {
+    if (B < 1 || T < 0 || H < 1 || num_seqs < 1 || !supported_dim(K) || !supported_dim(V))
+        return 0;
+    return std::max(bwd_workspace_bytes(B, T, H, K, V, num_seqs, false),
+                    bwd_workspace_bytes(B, T, H, K, V, num_seqs, true));
+}
+
+int kda_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+            const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
+            float scale, const float* initial_state, const int32_t* cu_seqlens,
+            int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+            const uint16_t* d_o, const float* d_final, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+            uint16_t* dg, uint16_t* dbeta, float* dA_log, float* ddt_bias, float* dh0,
+            void* workspace, size_t workspace_bytes, void* stream) {
+    // dv stands in for the forward output in the shared checks
+    Common c{q, k, v, beta, initial_state, nullptr, cu_seqlens, cu_seqlens != nullptr,
+             num_seqs, B, T, H, K, V, dv, workspace, workspace_bytes, scale, -1};
+    const BwdIO io{d_o, d_final, dq, dk, dv, dg, nullptr, dbeta, dA_log, ddt_bias, dh0};
+    int st = check_kda_gate(T, g, A_log, dt_bias, lower_bound);
+    if (st != KDA_OK) return st;
+    int32_t N = 0;
+    st = check_common(c, N);
+    if (st != KDA_OK) return st;
+    st = check_bwd_io(c, io, false);
+    if (st != KDA_OK) return st;
+    kda::PrepArgs p{};
+    p.g_kda = g;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.lower_bound = lower_bound;
+    return run_bwd(c, N, p, false, io, static_cast<hipStream_t>(stream));
+}
+
+int gdn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+            const uint16_t* beta, float scale, const float* initial_state,
+            const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+            int32_t K, int32_t V, const uint16_t* d_o, const float* d_final, uint16_t* dq,
+            uint16_t* dk, uint16_t* dv, float* dg, uint16_t* dbeta, float* dh0, void* workspace,
+            size_t workspace_bytes, void* stream) {
+    Common c{q, k, v, beta, initial_state, nullptr, cu_seqlens, cu_seqlens != nullptr,
+             num_seqs, B, T, H, K, V, dv, workspace, workspace_bytes, scale, -1};
+    const BwdIO io{d_o, d_final, dq, dk, dv, nullptr, dg, dbeta, nullptr, nullptr, dh0};
+    if (T > 0 && !g) return KDA_ERR_INVALID_ARG;
+    int32_t N = 0;
+    int st = check_common(c, N);
+    if (st != KDA_OK) return st;
+    st = check_bwd_io(c, io, true);
+    if (st != KDA_OK) return st;
+    kda::PrepArgs p{};
+    p.g_gdn = g;
+    return run_bwd(c, N, p, true, io, static_cast<hipStream_t>(stream));
 }
 
 const char* kda_status_str(int status) {

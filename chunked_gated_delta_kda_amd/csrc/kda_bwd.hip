@@ -1,0 +1,705 @@
+// kda_bwd.hip -- the backward pass (gfx950): the reverse-pass record, the
+// chunk-parallel gradient kernel and the reduction of the gate-parameter
+// gradients.
+//
+// The pages show the backward only as autograd over the forward call (cuLA
+// README mirror, section "Usage": o.backward(do) with q, k, v requiring
+// grad; the cuLA roadmap lists backward kernels for training, and the
+// FlashQLA summary (section "핵심 기능") a backward path beside the forward
+// one).  This is the reverse-mode derivative of the chunkwise forward pass
+// (kda_recur.hip), chunk by chunk.  Per chunk, with h the state entering it,
+// S' = Diag(Gam_C) h + Kd^T U' the state leaving it, U' = Tb Z,
+// Z = V - KG h, Tb = T diag(b), T = (I + diag(b) P)^-1,
+// P = tril_strict(KG Kinv^T), Kinv = k^ / Gam, O = scale (QG h + Aqk U'),
+// Aqk = tril(QG Kinv^T), and dS' the gradient reaching S':
+//   dU  = Kd dS' + scale Aqk^T dO          dV  = Tb^T dU
+//   dh  = Diag(Gam_C) dS' + scale QG^T dO - KG^T dV
+// (the reverse recurrence, kda_recur in its reverse mode), and locally
+//   W1 = T^T dU,  dM = scale tril(dO U'^T),  dP = -diag(b) tril_strict(W1 U'^T)
+//   db = rowdot(W1, Z) - rowsum(P * (W1 U'^T))
+//   dq^ = Gam * (scale dO h^T) + sum_j dM[r,j] k^_j Gam_r / Gam_j
+//   dk^ = -Gam * (dV h^T) + sum_j dP[r,j] k^_j Gam_r / Gam_j        (via KG)
+//       + sum_r (dM[r,j] q^_r + dP[r,j] k^_r) Gam_r / Gam_j         (via Kinv)
+//       + (Gam_C / Gam) * (U' dS'^T)                                (via Kd)
+//   dG  = q^ dq^ + k^ (dk^_KG - dk^_Kinv - dk^_Kd), plus, on the chunk's
+//         last token, sum_j k^_j dk^_Kd,j + Gam_C * rowsum(h * dS')
+//   d log a_t = sum over the chunk's tokens s >= t of dG_s
+// followed by the chain rule through the L2 norms, the gate and the sigmoid.
+// Every ratio Gam_r / Gam_j (r >= j) is formed from two factors of the same
+// 16-token block, or from factors that are both <= 1 across the two blocks,
+// as in the forward pass.
+#include "kda_common.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+// ------------------------------------------------------------ reverse record
+// BRec from Rec: the same matrices, transposed.  One workgroup per record; the
+// forward record is staged in LDS and every 16-byte slice of the backward one
+// gathers its 8 elements there.
+namespace {
+
+// Element (token s, channel c) of a [C x K] matrix in the Rec::NKG / QG layout.
+template <int K>
+__device__ __forceinline__ int rowop_index(int s, int c) {
+    constexpr int KS = K / 32;
+    const int bb = s >> 4, m = s & 15, j = c >> 5, g = (c & 31) >> 3, e = c & 7;
+    return ((bb * KS + j) * 64 + m + 16 * g) * 8 + e;
+}
+// Element (token s, channel c) of a [K x C] transposed matrix in the Rec::KDT layout.
+__device__ __forceinline__ int tileop_index(int s, int c) {
+    const int t = 2 * (c >> 5) + ((c & 7) >> 2), mm = 4 * ((c & 31) >> 3) + (c & 3);
+    const int p = tok_pos(s), g = p / EL, e = p % EL;
+    return ((t * 4 + g) * 16 + mm) * EL + e;
+}
+// Element (row r, token s) of a [C x C] matrix in the Rec::AQK / TB layout.
+__device__ __forceinline__ int tokop_index(int r, int s) {
+    const int p = tok_pos(s), g = p / EL, e = p % EL;
+    return (((r >> 4) * 4 + g) * 16 + (r & 15)) * EL + e;
+}
+
+}  // namespace
+
+template <int K>
+__global__ __launch_bounds__(256) void kda_bwd_rec_kernel(const unsigned char* rec,
+                                                          unsigned char* brec) {
+    using R = Rec<K>;
+    using BR = BRec<K>;
+    __shared__ __attribute__((aligned(16))) unsigned char src[R::BYTES];
+    const int64_t r0 = (int64_t)blockIdx.x * R::BYTES;
+    for (int p = threadIdx.x; p < R::BYTES / 16; p += 256)
+        reinterpret_cast<u32x4*>(src)[p] = reinterpret_cast<const u32x4*>(rec + r0)[p];
+    __syncthreads();
+    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+    constexpr int NBF = BR::GAMC / 2;  // bf16 elements before Gam_C
+    for (int p = threadIdx.x; p < BR::BYTES / 16; p += 256) {
+        u32x4 out;
+        if (p * 8 >= NBF) {  // Gam_C: same layout
+            out = reinterpret_cast<const u32x4*>(src)[p];
+        } else {
+            uint16_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int o = p * 8 + u;  // bf16 index in BRec
+                int si;
+                if (o < BR::QGT / 2) {
+                    // KD[s][c] (NKG layout) = Kd, read from KDT
+                    const int q = o;
+                    const int e = q & 7, lane = (q >> 3) & 63, bj = q >> 9;
+                    const int s = 16 * (bj / (K / 32)) + (lane & 15);
+                    const int c = 32 * (bj % (K / 32)) + 8 * (lane >> 4) + e;
+                    si = R::KDT / 2 + tileop_index(s, c);
+                } else if (o < BR::AQKT / 2) {
+                    // QGT / NKGT [t][g][m][e] = X[tok(g,e)][rho(t,m)], X from QG / NKG
+                    const bool qg = o < BR::NKGT / 2;
+                    const int q = o - (qg ? BR::QGT : BR::NKGT) / 2;
+                    const int e = q % EL, mm = (q / EL) & 15, g = (q / (EL * 16)) & 3,
+                              t = q / (EL * 64);
+                    const int s = 16 * (e >> 2) + 4 * g + (e & 3);
+                    si = (qg ? R::QG : R::NKG) / 2 + rowop_index<K>(s, tile_channel(t, mm));
+                } else {
+                    // AQKT / TBT [a][g][n][e] = X[tok(g,e)][16a+n], X from AQK / TB
+                    const bool aq = o < BR::TBT / 2;
+                    const int q = o - (aq ? BR::AQKT : BR::TBT) / 2;
+                    const int e = q % EL, n = (q / EL) & 15, g = (q / (EL * 16)) & 3,
+                              blk = q / (EL * 64);
+                    const int s = 16 * (e >> 2) + 4 * g + (e & 3);
+                    si = (aq ? R::AQK : R::TB) / 2 + tokop_index(s, 16 * blk + n);
+                }
+                v[u] = s16[si];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) out[u] = (uint32_t)v[2 * u] | ((uint32_t)v[2 * u + 1] << 16);
+        }
+        reinterpret_cast<u32x4*>(brec + r0)[p] = out;
+    }
+}
+
+void launch_bwd_rec(const unsigned char* rec, unsigned char* brec, int K, int64_t n_recs,
+                    hipStream_t stream) {
+    if (n_recs <= 0) return;
+    if (K == 128)
+        hipLaunchKernelGGL(kda_bwd_rec_kernel<128>, dim3((unsigned)n_recs), dim3(256), 0, stream,
+                           rec, brec);
+    else
+        hipLaunchKernelGGL(kda_bwd_rec_kernel<64>, dim3((unsigned)n_recs), dim3(256), 0, stream,
+                           rec, brec);
+}
+
+// ------------------------------------------------------------ gradient kernel
+namespace {
+
+constexpr int ROW_SHR1 = 0x111, ROW_SHR2 = 0x112, ROW_SHR4 = 0x114, ROW_SHR8 = 0x118;
+
+__device__ __forceinline__ float row_scan16(float x) {
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR1, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR2, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR4, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR8, 0xf, 0xf, false);
+    return x;
+}
+// sum over the 16 lanes of a row (every lane gets it)
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 v, float* f) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f[2 * u] = bf2f(v[u] & 0xffff);
+        f[2 * u + 1] = bf2f(v[u] >> 16);
+    }
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* f) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)f[e];
+    return r;
+}
+
+__device__ __forceinline__ uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, (bf16)x); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): about 16 significant bits
+template <class A>
+__device__ __forceinline__ void put_split(A& arr, int part, int c, int p, float x) {
+    const bf16 hi = (bf16)x;
+    arr[0][part][c][p] = __builtin_bit_cast(uint16_t, hi);
+    arr[1][part][c][p] = bits(x - (float)hi);
+}
+
+}  // namespace
+
+// One workgroup per (chunk slot, head) with one wave per 16-token block; lane
+// l = m + 16 g of wave b owns token 16 b + m and the channels 32 j + 8 g + e
+// (the row layout of kda_prep).  Products that contract over channels read
+// their operands from registers; products that contract over tokens read
+// token-ordered copies from LDS; products that contract over value columns
+// read the stored states and [C, V] rows.  Every result that is a function
+// of (token, channel) is produced transposed (channels as MFMA rows in the
+// tile_channel order), which lands it in the owner lane's registers.
+template <int K, int V, bool GDN>
+__global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
+    static_assert(NB == 2, "the gradient kernel assumes 32-token chunks");
+    constexpr int KS = K / 32, KT = K / 16, VS = V / 32, VT = V / 16;
+    constexpr int UP = V + 8;  // padded row of the U' / W1 copies (bf16)
+    using R = Rec<K>;
+    __shared__ float gend_s[2][K];                                    // block totals (log2)
+    __shared__ float beta_s[C];
+    __shared__ float P_s[C][C + 1];                                   // tril_strict(KG Kinv^T)
+    __shared__ __attribute__((aligned(16))) uint16_t tt_s[C][C];      // [r][pos(s)] = T[s][r]
+    __shared__ __attribute__((aligned(16))) uint16_t u_s[C][UP];      // U' rows
+    __shared__ __attribute__((aligned(16))) uint16_t w_s[C][UP];      // W1 rows
+    __shared__ __attribute__((aligned(16))) bf16x8 kbc0_s[KS * 64];   // block 0: k^ 2^(G_end0 - G)
+    // channel-major token operands [part][c][pos(s)]: 0: k^ 2^-Gl, 1: k^ 2^(G_end0 - Gl)
+    // (block 0), 2: q^ 2^Gl, 3: k^ 2^Gl (Gl: log2 decay within the token's block),
+    // each as a bf16 pair hi + lo.  A token pair (r, j) enters dG_r through one
+    // operand and dG_j, with the opposite sign, through another; in the reverse
+    // cumulative sum over the chunk the two cancel exactly unless their
+    // roundings differ, so these operands carry ~16 significant bits.
+    __shared__ __attribute__((aligned(16))) uint16_t xt_s[2][4][K][C];
+    __shared__ __attribute__((aligned(16))) uint16_t dmr_s[C][C];     // [r][pos(j)] = dM[r][j]
+    __shared__ __attribute__((aligned(16))) uint16_t dmc_s[C][C];     // [j][pos(r)] = dM[r][j]
+    __shared__ __attribute__((aligned(16))) uint16_t dpr_s[C][C];
+    __shared__ __attribute__((aligned(16))) uint16_t dpc_s[C][C];
+    __shared__ float dbeta_s[C];
+    __shared__ float kd_s[2][K];   // per block: sum over tokens of k^ dk^_Kd
+    __shared__ float hs_s[K];      // rowsum(h * dS')
+    __shared__ float tot_s[K];     // block 1's total of dG per channel
+    __shared__ float red_s[2][K];  // per block: sum over tokens of dL/d(dt_bias)
+    __shared__ float alog_s[2];
+
+    const int slot = blockIdx.x;
+    const int h = blockIdx.y;
+    const int blk = threadIdx.x >> 6;
+    const int L = threadIdx.x & 63, m = L & 15, g = L >> 4;
+
+    int n;
+    if (!a.packed) {
+        n = slot / ((a.T + C - 1) / C);
+        if (n >= a.n_seqs) return;
+    } else {
+        if (slot >= a.chunk_off[a.n_seqs]) {
+            // a slot past the packed chunks (the grid covers their upper bound):
+            // its share of the gate-parameter sums is zero
+            if constexpr (!GDN) {
+                const int64_t chb = (int64_t)slot * a.H + h;
+                for (int c = threadIdx.x; c < K; c += 128) a.part_dt[chb * K + c] = 0.f;
+                if (threadIdx.x == 0) a.part_alog[chb] = 0.f;
+            }
+            return;
+        }
+        int lo = 0, hi = a.n_seqs;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.chunk_off[mid] <= slot) lo = mid; else hi = mid;
+        }
+        n = lo;
+    }
+    int64_t t0, t1;
+    int s0, s1;
+    seq_span(a, n, t0, t1, s0, s1);
+    const int64_t start = t0 + (int64_t)C * (slot - s0);
+    const int nvalid = (int)min((int64_t)C, t1 - start);
+    const int row = 16 * blk + m;
+    const bool valid = row < nvalid;
+    const int64_t lrow = (start + (valid ? row : 0)) * a.H + h;
+    const int64_t ch_base = (int64_t)slot * a.H + h;  // chunk-head index of the stored tensors
+
+    // ---- this lane's row: q^, k^, log2 decay, beta
+    float qh[KS][8], kh[KS][8], G[KS][8];
+    float iq, ik;
+    {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const int c = 32 * j + 8 * g;
+            const u32x4 qv = *reinterpret_cast<const u32x4*>(a.q + lrow * K + c);
+            const u32x4 kv = *reinterpret_cast<const u32x4*>(a.k + lrow * K + c);
+            unpack8(qv, qh[j]);
+            unpack8(kv, kh[j]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (!valid) { qh[j][e] = 0.f; kh[j][e] = 0.f; }
+                sq += qh[j][e] * qh[j][e];
+                sk += kh[j][e] * kh[j][e];
+            }
+        }
+        sq += __shfl_xor(sq, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        sk += __shfl_xor(sk, 16, 64);
+        sk += __shfl_xor(sk, 32, 64);
+        iq = rsq_hw(sq + NORM_EPS);
+        ik = rsq_hw(sk + NORM_EPS);
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { qh[j][e] *= iq; kh[j][e] *= ik; }
+    }
+    const float braw = bf2f(a.beta[lrow]);
+    const float b = valid ? (GDN ? braw : sigmoid_f(braw)) : 0.f;
+    const float rate = GDN ? 0.f : exp2_hw(a.A_log[h] * LOG2E);
+    if constexpr (GDN) {
+        const float la = valid ? a.g_gdn[lrow] * LOG2E : 0.f;
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) G[j][e] = la;
+    } else {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const int c = 32 * j + 8 * g;
+            float x[8];
+            unpack8(*reinterpret_cast<const u32x4*>(a.g_kda + lrow * K + c), x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                G[j][e] = valid ? fmaxf(a.lower_bound, -rate * softplus_f(x[e] + a.dt_bias[(int64_t)h * K + c + e])) * LOG2E
+                                : 0.f;
+        }
+    }
+    // in-block inclusive prefix (log2), block totals to LDS
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            G[j][e] = row_scan16(G[j][e]);
+            if (m == 15) gend_s[blk][32 * j + 8 * g + e] = G[j][e];
+        }
+    if (g == 0) beta_s[row] = b;
+    __syncthreads();
+
+    // ---- decay-weighted operands; in-block P; transposed copies for token products
+    floatx4 Pacc = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 ka_f[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+        float ka[8], kbs[8], kbc[8], qa[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = 32 * j + 8 * g + e;
+            const float ga = exp2_hw(G[j][e]);
+            ka[e] = kh[j][e] * ga;
+            qa[e] = qh[j][e] * ga;
+            kbs[e] = kh[j][e] * exp2_hw(-G[j][e]);
+            kbc[e] = kh[j][e] * exp2_hw(gend_s[0][c] - G[j][e]);  // used for block 0 only
+            const int p = tok_pos(row);
+            put_split(xt_s, 0, c, p, kbs[e]);
+            if (blk == 0) put_split(xt_s, 1, c, p, kbc[e]);
+            put_split(xt_s, 2, c, p, qa[e]);
+            put_split(xt_s, 3, c, p, ka[e]);
+        }
+        ka_f[j] = pack8(ka);
+        Pacc = mfma32(ka_f[j], pack8(kbs), Pacc);  // P[16b + 4g' + i][16b + n]
+        if (blk == 0) kbc0_s[j * 64 + L] = pack8(kbc);
+    }
+    __syncthreads();
+    {
+        // lane (n, g') of the D layout: rows 4 g' + i, column n (= m here)
+        floatx4 Pc = {0.f, 0.f, 0.f, 0.f};
+        if (blk == 1) {
+#pragma unroll
+            for (int j = 0; j < KS; ++j) Pc = mfma32(ka_f[j], kbc0_s[j * 64 + L], Pc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * blk + 4 * g + i;
+            P_s[r][16 * blk + m] = (m < 4 * g + i) ? Pacc[i] : 0.f;
+            P_s[r][16 * (1 - blk) + m] = blk == 1 ? Pc[i] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- T = (I + diag(b) P)^-1 by forward substitution: lane j of wave 0 owns column j
+    if (blk == 0 && L < C) {
+        float Tc[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < r; ++s) acc += P_s[r][s] * Tc[s];
+            Tc[r] = (r == L ? 1.f : 0.f) - beta_s[r] * acc;
+        }
+#pragma unroll
+        for (int r = 0; r < C; ++r) tt_s[L][tok_pos(r)] = bits(Tc[r]);
+    }
+    __syncthreads();
+
+    // ---- U' = Tb Z and W1 = T^T dU for this block's rows (D layout, V/16 tiles);
+    // rowdot(W1, Z) on the way
+    float zw[4] = {0.f, 0.f, 0.f, 0.f};
+    {
+        const bf16xEL tb = *reinterpret_cast<const bf16xEL*>(
+            a.rec + ch_base * R::BYTES + R::TB + (blk * 64 + L) * (2 * EL));
+        const bf16xEL tt = *reinterpret_cast<const bf16xEL*>(&tt_s[16 * blk + m][EL * g]);
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) {
+            const int col = 16 * vt + m;
+            const u32x4 wz = *reinterpret_cast<const u32x4*>(a.zt + (ch_base * V + col) * C + EL * g);
+            const bf16xEL bz = __builtin_bit_cast(bf16xEL, wz);
+            const bf16xEL bu = *reinterpret_cast<const bf16xEL*>(a.dut + (ch_base * V + col) * C + EL * g);
+            const floatx4 U = mfma_tok(tb, bz, zero);
+            const floatx4 W = mfma_tok(tt, bu, zero);
+            float zf[8];
+            unpack8(wz, zf);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                zw[i] += W[i] * zf[4 * blk + i];  // Z[16b + 4g + i][col]
+                u_s[16 * blk + 4 * g + i][col] = bits(U[i]);
+                w_s[16 * blk + 4 * g + i][col] = bits(W[i]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- dM = scale tril(dO U'^T), E1 = W1 U'^T, dP, db (this block's rows)
+    bf16x8 dof[VS];
+#pragma unroll
+    for (int jv = 0; jv < VS; ++jv) {
+        const u32x4 zero4 = {0u, 0u, 0u, 0u};
+        const u32x4 x = *reinterpret_cast<const u32x4*>(a.d_o + lrow * V + 32 * jv + 8 * g);
+        dof[jv] = __builtin_bit_cast(bf16x8, valid ? x : zero4);
+    }
+    {
+        float dbp[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dbp[i] = zw[i];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            floatx4 dm = {0.f, 0.f, 0.f, 0.f}, e1 = dm;
+#pragma unroll
+            for (int jv = 0; jv < VS; ++jv) {
+                const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&u_s[16 * cb + m][32 * jv + 8 * g]);
+                const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_s[16 * blk + m][32 * jv + 8 * g]);
+                dm = mfma32(dof[jv], bu, dm);
+                e1 = mfma32(aw, bu, e1);
+            }
+            const int j = 16 * cb + m;  // this lane's column
+            bf16x4 dmv, dpv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * blk + 4 * g + i;
+                const float dmx = j <= r ? a.scale * dm[i] : 0.f;
+                const float dpx = j < r ? -beta_s[r] * e1[i] : 0.f;
+                if (j < r) dbp[i] -= P_s[r][j] * e1[i];
+                dmr_s[r][tok_pos(j)] = bits(dmx);
+                dpr_s[r][tok_pos(j)] = bits(dpx);
+                dmv[i] = (bf16)dmx;
+                dpv[i] = (bf16)dpx;
+            }
+            // [j][pos(r)]: rows 16 b + 4 g + i sit at positions EL g + 4 b + i
+            *reinterpret_cast<bf16x4*>(&dmc_s[j][EL * g + 4 * blk]) = dmv;
+            *reinterpret_cast<bf16x4*>(&dpc_s[j][EL * g + 4 * blk]) = dpv;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s = row_sum16(dbp[i]);
+            if (m == 0) dbeta_s[16 * blk + 4 * g + i] = s;
+        }
+    }
+    __syncthreads();
+
+    // ---- per-channel accumulators of this lane's row
+    float dqh[KS][8], dkh[KS][8], dks[KS][8];  // dq^, dk^, dk^_KG - dk^_Kinv - dk^_Kd
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { dqh[j][e] = 0.f; dkh[j][e] = 0.f; dks[j][e] = 0.f; }
+
+    // intra-chunk products over tokens; result tile t holds channels
+    // rho(t, 4 g + i) = 32 (t / 2) + 8 g + 4 (t % 2) + i of row 16 b + m
+    {
+        const bf16xEL bmr = *reinterpret_cast<const bf16xEL*>(&dmr_s[16 * blk + m][EL * g]);
+        const bf16xEL bpr = *reinterpret_cast<const bf16xEL*>(&dpr_s[16 * blk + m][EL * g]);
+        // (operands are split and joined as 32-bit words: element-wise moves
+        // inside bf16 vectors are avoided, see kda_recur.hip)
+        u32x4 wmc = *reinterpret_cast<const u32x4*>(&dmc_s[16 * blk + m][EL * g]);
+        u32x4 wpc = *reinterpret_cast<const u32x4*>(&dpc_s[16 * blk + m][EL * g]);
+        // block 0's columns split by the row block r of dM[r][j] (different factors):
+        // slots 0..3 hold rows of block 0, slots 4..7 rows of block 1
+        u32x4 wmc1 = wmc, wpc1 = wpc;
+        if (blk == 0) {
+            wmc[2] = wmc[3] = wpc[2] = wpc[3] = 0u;
+            wmc1[0] = wmc1[1] = wpc1[0] = wpc1[1] = 0u;
+        }
+        const bf16xEL bmc = __builtin_bit_cast(bf16xEL, wmc), bpc = __builtin_bit_cast(bf16xEL, wpc);
+        const bf16xEL bmc1 = __builtin_bit_cast(bf16xEL, wmc1),
+                      bpc1 = __builtin_bit_cast(bf16xEL, wpc1);
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int ch = tile_channel(t, m);  // this lane's A-operand row
+            floatx4 iq4 = zero, ik4 = zero, ki0 = zero, ki1 = zero;
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {  // hi and lo parts of the operands
+                u32x4 wkb = *reinterpret_cast<const u32x4*>(&xt_s[hl][0][ch][EL * g]);
+                if (blk == 1) {  // block 0's slots with the cross-block factor
+                    const uint2 lo = *reinterpret_cast<const uint2*>(&xt_s[hl][1][ch][EL * g]);
+                    wkb[0] = lo.x;
+                    wkb[1] = lo.y;
+                }
+                const bf16xEL akb = __builtin_bit_cast(bf16xEL, wkb);
+                const bf16xEL aqa = *reinterpret_cast<const bf16xEL*>(&xt_s[hl][2][ch][EL * g]);
+                const bf16xEL aka = *reinterpret_cast<const bf16xEL*>(&xt_s[hl][3][ch][EL * g]);
+                iq4 = mfma_tok(akb, bmr, iq4);
+                ik4 = mfma_tok(akb, bpr, ik4);
+                ki0 = mfma_tok(aka, bpc, mfma_tok(aqa, bmc, ki0));
+                if (blk == 0) ki1 = mfma_tok(aka, bpc1, mfma_tok(aqa, bmc1, ki1));
+            }
+            const int j = t >> 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * (t & 1) + i;
+                const int c = 32 * j + 8 * g + e;
+                const float Gl = G[j][e];
+                const float ga = exp2_hw(Gl);
+                const float kinv = blk == 0 ? exp2_hw(-Gl) * ki0[i] + exp2_hw(gend_s[0][c] - Gl) * ki1[i]
+                                            : exp2_hw(-Gl) * ki0[i];
+                dqh[j][e] += ga * iq4[i];
+                const float dkg = ga * ik4[i];
+                dkh[j][e] += dkg + kinv;
+                dks[j][e] += dkg - kinv;
+            }
+        }
+    }
+
+    // ---- products over value columns with the stored states: dO h^T, dV h^T,
+    // U' dS'^T (transposed), and rowsum(h * dS')
+    {
+        bf16x8 dvf[VS], uf[VS];
+#pragma unroll
+        for (int jv = 0; jv < VS; ++jv) {
+            const u32x4 zero4 = {0u, 0u, 0u, 0u};
+            const u32x4 x = *reinterpret_cast<const u32x4*>(a.dv + lrow * V + 32 * jv + 8 * g);
+            dvf[jv] = __builtin_bit_cast(bf16x8, valid ? x : zero4);
+            uf[jv] = *reinterpret_cast<const bf16x8*>(&u_s[16 * blk + m][32 * jv + 8 * g]);
+        }
+        const uint16_t* hbase = a.hs + ch_base * K * V;
+        const uint16_t* dbase = a.dss + ch_base * K * V;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int ch = tile_channel(t, m);
+            floatx4 hq = {0.f, 0.f, 0.f, 0.f}, hk = hq, hd = hq;
+            float hsp = 0.f;
+#pragma unroll
+            for (int jv = 0; jv < VS; ++jv) {
+                const u32x4 wh = *reinterpret_cast<const u32x4*>(hbase + (int64_t)ch * V + 32 * jv + 8 * g);
+                const u32x4 wd = *reinterpret_cast<const u32x4*>(dbase + (int64_t)ch * V + 32 * jv + 8 * g);
+                const bf16x8 ah = __builtin_bit_cast(bf16x8, wh), ad = __builtin_bit_cast(bf16x8, wd);
+                hq = mfma32(ah, dof[jv], hq);
+                hk = mfma32(ah, dvf[jv], hk);
+                hd = mfma32(ad, uf[jv], hd);
+                float fh[8], fd[8];
+                unpack8(wh, fh);
+                unpack8(wd, fd);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) hsp += fh[e] * fd[e];
+            }
+            hsp += __shfl_xor(hsp, 16, 64);
+            hsp += __shfl_xor(hsp, 32, 64);
+            if (blk == 0 && g == 0) hs_s[ch] = hsp;
+            const int j = t >> 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * (t & 1) + i;
+                const int c = 32 * j + 8 * g + e;
+                const float gg = G[j][e] + (blk == 1 ? gend_s[0][c] : 0.f);  // chunk-global log2
+                const float gam = exp2_hw(gg);
+                const float gcr = exp2_hw(gend_s[0][c] + gend_s[1][c] - gg);  // Gam_C / Gam
+                dqh[j][e] += a.scale * gam * hq[i];
+                const float dkg = -gam * hk[i];
+                const float dkd = gcr * hd[i];
+                dkh[j][e] += dkg + dkd;
+                dks[j][e] += dkg - dkd;
+                // sum over this block's tokens of k^ dk^_Kd for channel c
+                const float kdr = row_sum16(kh[j][e] * dkd);
+                if (m == 0) kd_s[blk][c] = kdr;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- dG, its reverse cumulative sum over the chunk, and the chain rule
+    float dla[KS][8];
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float dG = qh[j][e] * dqh[j][e] + kh[j][e] * dks[j][e];
+            const float inc = row_scan16(dG);
+            const float tot = __shfl(inc, (L & 48) | 15, 64);
+            dla[j][e] = tot - inc + dG;  // sum over this block's tokens s >= row
+            if (blk == 1 && m == 15) tot_s[32 * j + 8 * g + e] = tot;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = 32 * j + 8 * g + e;
+            const float gc = exp2_hw(gend_s[0][c] + gend_s[1][c]);
+            dla[j][e] += (blk == 0 ? tot_s[c] : 0.f) + kd_s[0][c] + kd_s[1][c] + gc * hs_s[c];
+        }
+
+    // dq, dk through the norms
+    {
+        float pq = 0.f, pk = 0.f;
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { pq += qh[j][e] * dqh[j][e]; pk += kh[j][e] * dkh[j][e]; }
+        pq += __shfl_xor(pq, 16, 64);
+        pq += __shfl_xor(pq, 32, 64);
+        pk += __shfl_xor(pk, 16, 64);
+        pk += __shfl_xor(pk, 32, 64);
+        if (valid) {
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                float xq[8], xk[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xq[e] = (dqh[j][e] - qh[j][e] * pq) * iq;
+                    xk[e] = (dkh[j][e] - kh[j][e] * pk) * ik;
+                }
+                *reinterpret_cast<bf16x8*>(a.dq + lrow * K + 32 * j + 8 * g) = pack8(xq);
+                *reinterpret_cast<bf16x8*>(a.dk + lrow * K + 32 * j + 8 * g) = pack8(xk);
+            }
+        }
+    }
+    // beta
+    if (valid && g == 0) {
+        const float db = dbeta_s[row];
+        a.dbeta[lrow] = bits(GDN ? db : db * b * (1.f - b));
+    }
+    // the gate
+    if constexpr (GDN) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += dla[j][e];
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        if (valid && g == 0) a.dg_gdn[lrow] = s;
+    } else {
+        float alog = 0.f;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const int c0 = 32 * j + 8 * g;
+            float x[8], dx[8];
+            unpack8(*reinterpret_cast<const u32x4*>(a.g_kda + lrow * K + c0), x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xx = x[e] + a.dt_bias[(int64_t)h * K + c0 + e];
+                const float pre = -rate * softplus_f(xx);
+                const float da = (valid && pre >= a.lower_bound) ? dla[j][e] : 0.f;
+                dx[e] = -rate * sigmoid_f(xx) * da;
+                alog += da * pre;
+                const float colsum = row_sum16(dx[e]);
+                if (m == 0) red_s[blk][c0 + e] = colsum;
+            }
+            if (valid) *reinterpret_cast<bf16x8*>(a.dg_kda + lrow * K + c0) = pack8(dx);
+        }
+        alog += __shfl_xor(alog, 16, 64);
+        alog += __shfl_xor(alog, 32, 64);
+        alog = row_sum16(alog);
+        if (L == 0) alog_s[blk] = alog;
+        __syncthreads();
+        for (int c = threadIdx.x; c < K; c += 128)
+            a.part_dt[ch_base * K + c] = red_s[0][c] + red_s[1][c];
+        if (threadIdx.x == 0) a.part_alog[ch_base] = alog_s[0] + alog_s[1];
+    }
+}
+
+template <int K, int V>
+void launch_bwd_chunk_kv(const BwdArgs& a, bool gdn, int n_slots, hipStream_t stream) {
+    const dim3 grid(n_slots, a.H), block(128);
+    if (gdn) hipLaunchKernelGGL((kda_bwd_chunk_kernel<K, V, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((kda_bwd_chunk_kernel<K, V, false>), grid, block, 0, stream, a);
+}
+
+void launch_bwd_chunk(const BwdArgs& a, int K, int V, bool gdn, int n_slots, hipStream_t stream) {
+    if (n_slots <= 0) return;
+    if (K == 128) {
+        if (V == 128) launch_bwd_chunk_kv<128, 128>(a, gdn, n_slots, stream);
+        else launch_bwd_chunk_kv<128, 64>(a, gdn, n_slots, stream);
+    } else {
+        if (V == 128) launch_bwd_chunk_kv<64, 128>(a, gdn, n_slots, stream);
+        else launch_bwd_chunk_kv<64, 64>(a, gdn, n_slots, stream);
+    }
+}
+
+// ------------------------------------------------------------ gate reductions
+// dL/d(dt_bias)[h][c] and dL/dA_log[h]: sums over every chunk slot of the
+// per-chunk sums, in a fixed order (no atomics: the result is reproducible).
+__global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(const float* part_dt,
+                                                             const float* part_alog,
+                                                             int32_t n_slots, int32_t H,
+                                                             int32_t K, float* ddt_bias,
+                                                             float* dA_log) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < H * K) {
+        const int h = i / K, c = i % K;
+        float s = 0.f;
+        for (int sl = 0; sl < n_slots; ++sl) s += part_dt[((int64_t)sl * H + h) * K + c];
+        ddt_bias[i] = s;
+    } else if (i < H * K + H) {
+        const int h = i - H * K;
+        float s = 0.f;
+        for (int sl = 0; sl < n_slots; ++sl) s += part_alog[(int64_t)sl * H + h];
+        dA_log[h] = s;
+    }
+}
+
+void launch_bwd_reduce(const float* part_dt, const float* part_alog, int32_t n_slots,
+                       int32_t H, int32_t K, float* ddt_bias, float* dA_log, hipStream_t stream) {
+    const int total = H * K + H;
+    hipLaunchKernelGGL(kda_bwd_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, stream,
+                       part_dt, part_alog, n_slots, H, K, ddt_bias, dA_log);
+}
+
+}  // namespace kda

@@ -157,6 +157,38 @@ struct Rec {
     static constexpr int BYTES = GAMC + K * 4;
 };
 
+// Per (chunk slot, head) record of the reverse pass: the same matrices as Rec,
+// transposed for the adjoint recurrence (kda_bwd_rec writes it from Rec).
+// With dS' the gradient of the state leaving the chunk and dO its output
+// gradient, the reverse step is
+//   dU = Kd dS' + scale Aqk^T dO,  dV = Tb^T dU,
+//   dS = Diag(Gam_C) dS' + scale QG^T dO + nKG^T dV,
+// so Kd is needed row-major (A operand over channels, layout of Rec::NKG) and
+// QG, nKG, Aqk, Tb transposed (A operands over tokens).
+template <int K>
+struct BRec {
+    static constexpr int KSTEPS = K / 32;
+    static constexpr int KTILES = K / 16;
+    static constexpr int KD = 0;                  // bf16 [NB][KSTEPS][4][16][8]
+    static constexpr int QGT = KD + C * K * 2;    // bf16 [KTILES][4][16][EL]:
+                                                  //   [t][g][m][e] = QG[tok(g,e)][rho(t,m)]
+    static constexpr int NKGT = QGT + C * K * 2;  // same layout, nKG
+    static constexpr int AQKT = NKGT + C * K * 2; // bf16 [NB][4][16][EL]:
+                                                  //   [a][g][n][e] = Aqk[tok(g,e)][16a+n]
+    static constexpr int TBT = AQKT + C * C * 2;  // bf16 [NB][4][16][EL]:
+                                                  //   [b][g][m][e] = Tb[tok(g,e)][16b+m]
+    static constexpr int GAMC = TBT + C * C * 2;  // fp32 [K], as in Rec
+    static constexpr int BYTES = GAMC + K * 4;
+    static_assert(BYTES == Rec<K>::BYTES, "the stage layout of kda_recur assumes equal sizes");
+};
+
+// Position of chunk token s among the EL k-slots of a token operand: the slot
+// (g, e) with tok(g, e) = 16 (e / 4) + 4 g + e % 4 = s sits at index 8 g + e
+// (two blocks; with one block, 4 g + e).
+__host__ __device__ constexpr int tok_pos(int s) {
+    return EL * ((s & 15) >> 2) + 4 * (s >> 4) + (s & 3);
+}
+
 // channel of element e of lane group g in k-step j of a 16x16x32 fragment
 __host__ __device__ constexpr int frag_channel(int j, int g, int e) { return 32 * j + 8 * g + e; }
 // channel of row r of state tile t

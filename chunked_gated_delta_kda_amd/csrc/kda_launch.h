@@ -50,7 +50,17 @@ struct RecurArgs {
                                // bound showed the transition negligible (not computed)
     const float* bound;        // [slots, H] chunk bounds from kda_prep (log2)
     float bound_limit;         // a transition with a summed bound below this is negligible
+    // Backward pass (null for the forward pass):
+    uint16_t* chunk_state;     // [slots, H, K, V] bf16: the state entering each chunk
+                               // (reverse pass: the state gradient leaving each chunk)
+    uint16_t* chunk_u;         // [slots, H, V, C] bf16, tokens in k-slot order: the
+                               // chunk's V - KG S (reverse pass: dL/dU')
 };
+
+// kda_recur variants: the forward pass; the forward pass that stores every
+// chunk's entering state and V - KG S instead of outputs; the reverse pass
+// over the backward record (state gradient, dL/dU' and dv).
+enum RecurMode { RECUR_FWD = 0, RECUR_STORE = 1, RECUR_BWD = 2 };
 
 struct DecodeArgs {
     const uint16_t* q;         // [pairs, K] bf16 (pairs = N * H, head fastest)
@@ -83,6 +93,45 @@ struct SplitScanArgs {
     int32_t n_seqs;
 };
 
+// Backward pass: the chunk-parallel gradient kernel (kda_bwd.hip).
+struct BwdArgs {
+    const uint16_t* q;         // [tokens, H, K] bf16
+    const uint16_t* k;         // [tokens, H, K] bf16
+    const uint16_t* g_kda;     // KDA: pre-activation gate [tokens, H, K] bf16
+    const float* g_gdn;        // GDN: log decay [tokens, H] fp32
+    const uint16_t* beta;      // [tokens, H] bf16
+    const float* A_log;        // [H] (KDA)
+    const float* dt_bias;      // [H, K] (KDA)
+    float lower_bound;
+    float scale;
+    const uint16_t* d_o;       // [tokens, H, V] bf16: dL/do
+    const uint16_t* dv;        // [tokens, H, V] bf16: dL/dv (from the reverse pass)
+    const unsigned char* rec;  // forward records (for Tb)
+    const uint16_t* hs;        // [slots, H, K, V] bf16: state entering each chunk
+    const uint16_t* zt;        // [slots, H, V, C] bf16: V - KG S of each chunk
+    const uint16_t* dss;       // [slots, H, K, V] bf16: gradient of the state leaving it
+    const uint16_t* dut;       // [slots, H, V, C] bf16: dL/dU'
+    uint16_t* dq;              // [tokens, H, K] bf16
+    uint16_t* dk;              // [tokens, H, K] bf16
+    uint16_t* dg_kda;          // KDA: [tokens, H, K] bf16
+    float* dg_gdn;             // GDN: [tokens, H] fp32
+    uint16_t* dbeta;           // [tokens, H] bf16
+    float* part_dt;            // KDA: [slots, H, K] per-chunk sums of dL/d(dt_bias)
+    float* part_alog;          // KDA: [slots, H] per-chunk sums of dL/dA_log
+    int32_t H;
+    int32_t n_seqs;
+    int32_t packed;
+    int32_t T;
+    const int32_t* seq_start;
+    const int32_t* chunk_off;
+};
+
+void launch_bwd_rec(const unsigned char* rec, unsigned char* brec, int K, int64_t n_recs,
+                    hipStream_t stream);
+void launch_bwd_chunk(const BwdArgs& a, int K, int V, bool gdn, int n_slots, hipStream_t stream);
+void launch_bwd_reduce(const float* part_dt, const float* part_alog, int32_t n_slots,
+                       int32_t H, int32_t K, float* ddt_bias, float* dA_log, hipStream_t stream);
+
 void launch_seg_table(const int32_t* seq_start, const int32_t* chunk_off, int32_t n_seqs,
                       int32_t L, int32_t n_virt_max, int32_t* vseq_start, int32_t* vchunk_off,
                       int32_t* final_map, int32_t* vfirst, hipStream_t stream);
@@ -90,7 +139,7 @@ void launch_split_scan(const SplitScanArgs& a, int K, hipStream_t stream);
 void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t total_tokens,
                       int32_t* seq_start, int32_t* chunk_off, hipStream_t stream);
 void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream);
-void launch_recur(const RecurArgs& a, int K, hipStream_t stream);
+void launch_recur(const RecurArgs& a, int K, hipStream_t stream, RecurMode mode = RECUR_FWD);
 void launch_decode(const DecodeArgs& a, int K, bool gdn, hipStream_t stream);
 int record_bytes(int K);
 

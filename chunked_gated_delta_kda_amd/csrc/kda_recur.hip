@@ -52,11 +52,17 @@ struct StageLayout {
 };
 
 // OCC: workgroups per CU the register allocation must allow (1 or 2).
-template <int K, int NW, int CT, int NL, int DEPTH, int OCC>
+// MODE (RecurMode): the forward pass; the forward pass that stores, for the
+// backward pass, each chunk's entering state and V - KG S (no outputs); the
+// reverse pass, which walks the chunks backwards over BRec records with the
+// output gradient in place of V (see kda_bwd.hip).
+template <int K, int NW, int CT, int NL, int DEPTH, int OCC, int MODE>
 __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
     OCC * (NW + NL) / 4))) void kda_recur_kernel(RecurArgs a) {
     static_assert(DEPTH % 2 == 0 && DEPTH >= 2, "the loop is unrolled by DEPTH and by 2");
+    constexpr bool STORE = MODE == RECUR_STORE, BWD = MODE == RECUR_BWD;
     using R = Rec<K>;
+    using BR = BRec<K>;
     using L = StageLayout<K, NW, CT, NL>;
     constexpr int KS = K / 32, KT = K / 16;
     // Two buffers: during iteration c the compute waves read chunk c + 1's
@@ -135,6 +141,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
         // loads chunk c (clamped to the last chunk: harmless re-reads at the end)
         auto issue = [&](u32x4 (&dst)[L::PPL], int c) {
             c = min(c, nch - 1);
+            if constexpr (BWD) c = nch - 1 - c;  // the reverse pass walks backwards
             const unsigned char* rec = rec_h + (int64_t)(s0 + c) * rec_stride;
             const int64_t start = t0 + (int64_t)C * c;
             const int nvalid = (int)min((int64_t)C, t1 - start);
@@ -152,6 +159,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
         // V rows of padding tokens (and the whole V tile of a transition block)
         // are written as zeros, so the compute waves read V without masking
         auto commit = [&](const u32x4 (&src)[L::PPL], unsigned char* buf, int c) {
+            if constexpr (BWD) c = nch - 1 - min(c, nch - 1);
             const int nvalid = trans ? 0 : (int)min((int64_t)C, t1 - (t0 + (int64_t)C * c));
             const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -269,6 +277,37 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
                 *reinterpret_cast<const bf16xEL*>(buf + R::AQK + (bb * 64 + lane) * (2 * EL));
     };
 
+    // Backward-pass stores.  store_state: the bf16 state copy (k-step j of
+    // column tile ct holds channels 32 j + 8 lg + e of column lr) into
+    // chunk_state [slots, H, K, V].  store_tok: a [C, columns] result in D
+    // layout (block bb, rows 4 lg + i) into chunk_u [slots, H, V, C] with the
+    // tokens in k-slot order, 8 bytes per block.
+    // (single bf16 elements are taken from the packed 32-bit words with
+    // integer shifts: storing vector elements of a bf16 vector directly was
+    // compiled into stores of one element repeated)
+    auto store_state = [&](const bf16x8 (&sb)[CT][KS], int64_t slot) {
+        uint16_t* hp = a.chunk_state + (slot * a.H + h) * K * a.V + cb + cw + lr;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                const u32x4 w = __builtin_bit_cast(u32x4, sb[ct][j]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    hp[16 * ct + (int64_t)(32 * j + 8 * lg + e) * a.V] =
+                        (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            }
+    };
+    auto store_tok = [&](const floatx4 (&X)[CT][NB], int64_t slot) {
+        uint16_t* up = a.chunk_u + ((slot * a.H + h) * a.V + cb + cw + lr) * C;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+                *reinterpret_cast<bf16x4*>(up + 16 * ct * C + EL * lg + 4 * bb) =
+                    to_bf16x4(X[ct][bb]);
+    };
+
     // One chunk from registers; `next` is chunk c + 1's buffer.  Each operand
     // fragment serves the wave's CT column tiles.
     auto compute = [&](Frags& f, const unsigned char* next, int c) {
@@ -285,6 +324,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
                     sb[ct][j][e] = (bf16)S[ct][2 * j][e];
                     sb[ct][j][4 + e] = (bf16)S[ct][2 * j + 1][e];
                 }
+        if constexpr (STORE) store_state(sb, s0 + c);
         // Y_b = V_b - KG_b S for each 16-token block b
         floatx4 Y[CT][NB];
 #pragma unroll
@@ -299,17 +339,21 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
                 for (int ct = 0; ct < CT; ++ct)
                     Y[ct][bb] = mfma32(f.nkg[bb][j], sb[ct][j], Y[ct][bb]);
         read_nkg_v(f, next);
+        if constexpr (STORE) store_tok(Y, s0 + c);
         // O_ob^T = S^T QG_ob^T for each 16-token output block ob
         floatx4 OT[CT][NB];
+        if constexpr (!STORE) {
 #pragma unroll
-        for (int ob = 0; ob < NB; ++ob)
+            for (int ob = 0; ob < NB; ++ob)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                OT[ct][ob] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int ct = 0; ct < CT; ++ct) {
+                    OT[ct][ob] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < KS; ++j) OT[ct][ob] = mfma32(sb[ct][j], f.qg[ob][j], OT[ct][ob]);
-            }
-        read_qg(f, next);
+                    for (int j = 0; j < KS; ++j)
+                        OT[ct][ob] = mfma32(sb[ct][j], f.qg[ob][j], OT[ct][ob]);
+                }
+            read_qg(f, next);
+        }
         // decay the state; the rank-C update accumulates onto it
 #pragma unroll
         for (int t = 0; t < KT; ++t)
@@ -346,6 +390,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) S[ct][t] = mfma_tok(f.kdt[t], uc[ct], S[ct][t]);
         read_kdt(f, next);
+        if constexpr (STORE) return;  // no outputs
         // + U'^T Aqk^T.  With one block the 16x16x16 product is accumulated apart
         // and added on the VALU: a 16x16x16 MFMA must not take the result of a
         // 16x16x32 MFMA as its accumulator input (that dependent pair gave wrong
@@ -378,21 +423,193 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
             }
     };
 
+    // ---- the reverse pass (BWD): BRec operands, the output gradient in the V tile
+    struct BFrags {
+        bf16x8 kd[NB][KS];
+        bf16xEL qgt[KT];
+        bf16xEL nkgt[KT];
+        bf16xEL tbt[NB];
+        bf16xEL aqkt[NB];
+        floatx4 gc[KT];
+        floatx4 dov[CT][NB];
+    };
+    auto read_kd_do = [&](BFrags& f, const unsigned char* buf) {
+        const uint16_t* vt = reinterpret_cast<const uint16_t*>(buf + L::V_OFF);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+            for (int j = 0; j < KS; ++j)
+                f.kd[bb][j] = *reinterpret_cast<const bf16x8*>(
+                    buf + BR::KD + ((bb * KS + j) * 64 + lane) * 16);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    f.dov[ct][bb][i] = bf2f(vt[(16 * bb + 4 * lg + i) * L::VCOLS + cw + 16 * ct + lr]);
+        }
+    };
+    auto read_tiles = [&](bf16xEL (&dst)[KT], const unsigned char* buf, int off) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            dst[t] = *reinterpret_cast<const bf16xEL*>(buf + off + (t * 64 + lane) * (2 * EL));
+    };
+    auto read_blocks = [&](bf16xEL (&dst)[NB], const unsigned char* buf, int off) {
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+            dst[bb] = *reinterpret_cast<const bf16xEL*>(buf + off + (bb * 64 + lane) * (2 * EL));
+    };
+    auto read_bgc = [&](BFrags& f, const unsigned char* buf) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            f.gc[t] = *reinterpret_cast<const floatx4*>(buf + BR::GAMC + (16 * t + 4 * lg) * 4);
+    };
+    // One reverse step: S holds dS', the gradient of the state leaving chunk
+    // cc = nch - 1 - c, and leaves with the gradient of the state entering it.
+    auto compute_bwd = [&](BFrags& f, const unsigned char* next, int c) {
+        const int cc = nch - 1 - c;
+        const int64_t start = t0 + (int64_t)C * cc;
+        const int nvalid = (int)min((int64_t)C, t1 - start);
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 sb[CT][KS];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int j = 0; j < KS; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sb[ct][j][e] = (bf16)S[ct][2 * j][e];
+                    sb[ct][j][4 + e] = (bf16)S[ct][2 * j + 1][e];
+                }
+        if (a.chunk_state) store_state(sb, s0 + cc);
+        // the output gradient as a token operand (scale applied to the products)
+        bf16xEL dob[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dob[ct][i] = (bf16)f.dov[ct][0][i];
+                if constexpr (NB == 2) dob[ct][4 + i] = (bf16)f.dov[ct][NB - 1][i];
+            }
+        // dU = Kd dS' + scale Aqk^T dO
+        floatx4 dU[CT][NB], aux[CT][NB];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                dU[ct][bb] = zero;
+                aux[ct][bb] = mfma_tok(f.aqkt[bb], dob[ct], zero);
+            }
+        read_blocks(f.aqkt, next, BR::AQKT);
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    dU[ct][bb] = mfma32(f.kd[bb][j], sb[ct][j], dU[ct][bb]);
+        read_kd_do(f, next);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dU[ct][bb][i] += a.scale * aux[ct][bb][i];
+        if (a.chunk_u) store_tok(dU, s0 + cc);
+        bf16xEL duc[CT], yc[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                duc[ct][i] = (bf16)dU[ct][0][i];
+                if constexpr (NB == 2) duc[ct][4 + i] = (bf16)dU[ct][NB - 1][i];
+            }
+        // dV = Tb^T dU: the value gradient of the chunk's tokens
+        floatx4 dV[CT][NB];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) dV[ct][bb] = mfma_tok(f.tbt[bb], duc[ct], zero);
+        read_blocks(f.tbt, next, BR::TBT);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                yc[ct][i] = (bf16)dV[ct][0][i];
+                if constexpr (NB == 2) yc[ct][4 + i] = (bf16)dV[ct][NB - 1][i];
+            }
+        if (a.o) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const u32x4 w = __builtin_bit_cast(u32x4, yc[ct]);
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * bb + 4 * lg + i, e = 4 * bb + i;
+                        if (row < nvalid)
+                            a.o[(start + row) * vstride + (int64_t)h * a.V + cb + cw + 16 * ct + lr] =
+                                (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                    }
+            }
+        }
+        // dS = Diag(Gam_C) dS' + nKG^T dV + scale QG^T dO
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[ct][t][i] *= f.gc[t][i];
+        read_bgc(f, next);
+        floatx4 QD[CT][KT];
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) QD[ct][t] = mfma_tok(f.qgt[t], dob[ct], zero);
+        read_tiles(f.qgt, next, BR::QGT);
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) S[ct][t] = mfma_tok(f.nkgt[t], yc[ct], S[ct][t]);
+        read_tiles(f.nkgt, next, BR::NKGT);
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[ct][t][i] += a.scale * QD[ct][t][i];
+    };
+
     if (nch > 0) {
         __syncthreads();  // chunk 0 is in buffer 0
-        Frags fr;
-        read_nkg_v(fr, stage[0]);
-        read_qg(fr, stage[0]);
-        read_gc(fr, stage[0]);
-        read_tb(fr, stage[0]);
-        read_kdt(fr, stage[0]);
-        read_aqk(fr, stage[0]);
-        __syncthreads();  // chunk 1 is in buffer 1; buffer 0 may be overwritten
-        int s1b = 1;  // buffer of chunk c + 1: (c + 1) % 2
-        for (int c = 0; c < nround; ++c) {
-            if (c < nch) compute(fr, stage[s1b], c);  // uniform over the workgroup
-            __syncthreads();
-            s1b ^= 1;
+        int s1b = 1;      // buffer of chunk c + 1: (c + 1) % 2
+        if constexpr (BWD) {
+            BFrags fr;
+            read_kd_do(fr, stage[0]);
+            read_tiles(fr.qgt, stage[0], BR::QGT);
+            read_tiles(fr.nkgt, stage[0], BR::NKGT);
+            read_blocks(fr.tbt, stage[0], BR::TBT);
+            read_blocks(fr.aqkt, stage[0], BR::AQKT);
+            read_bgc(fr, stage[0]);
+            __syncthreads();  // chunk 1 is in buffer 1; buffer 0 may be overwritten
+            for (int c = 0; c < nround; ++c) {
+                if (c < nch) compute_bwd(fr, stage[s1b], c);  // uniform over the workgroup
+                __syncthreads();
+                s1b ^= 1;
+            }
+        } else {
+            Frags fr;
+            read_nkg_v(fr, stage[0]);
+            read_qg(fr, stage[0]);
+            read_gc(fr, stage[0]);
+            read_tb(fr, stage[0]);
+            read_kdt(fr, stage[0]);
+            read_aqk(fr, stage[0]);
+            __syncthreads();  // chunk 1 is in buffer 1; buffer 0 may be overwritten
+            for (int c = 0; c < nround; ++c) {
+                if (c < nch) compute(fr, stage[s1b], c);  // uniform over the workgroup
+                __syncthreads();
+                s1b ^= 1;
+            }
         }
     }
 
@@ -469,26 +686,34 @@ int device_cus() {
 // allow two workgroups per CU (the chain of each is latency-bound, so two
 // interleave well); up to one per CU, the variant with the larger register
 // budget.
-template <int K>
+template <int K, int MODE>
 void launch_recur_t(const RecurArgs& a, hipStream_t stream) {
     const int vs = (a.V + (a.trans_out ? K : 0)) / (16 * RECUR_TILES * RECUR_WAVES);
     const int64_t pairs = (int64_t)a.n_seqs * a.H;
     const int64_t groups = (pairs + 7) / 8;  // the grid covers whole groups of 8 pairs
     const int64_t blocks = groups * 8 * vs;
     const dim3 grid((unsigned)blocks), block(64 * (RECUR_WAVES + RECUR_LOADERS));
-    if (pairs * vs > device_cus())
-        hipLaunchKernelGGL(
-            (kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS, RECUR_DEPTH2, 2>), grid,
-            block, 0, stream, a);
+    // (the reverse pass needs the larger register budget in any case)
+    if (MODE != RECUR_BWD && pairs * vs > device_cus())
+        hipLaunchKernelGGL((kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS,
+                                             RECUR_DEPTH2, 2, MODE>),
+                           grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL(
-            (kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS, RECUR_DEPTH, 1>), grid,
-            block, 0, stream, a);
+        hipLaunchKernelGGL((kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS,
+                                             RECUR_DEPTH, 1, MODE>),
+                           grid, block, 0, stream, a);
 }
 
-void launch_recur(const RecurArgs& a, int K, hipStream_t stream) {
-    if (K == 128) launch_recur_t<128>(a, stream);
-    else launch_recur_t<64>(a, stream);
+template <int K>
+void launch_recur_k(const RecurArgs& a, hipStream_t stream, RecurMode mode) {
+    if (mode == RECUR_STORE) launch_recur_t<K, RECUR_STORE>(a, stream);
+    else if (mode == RECUR_BWD) launch_recur_t<K, RECUR_BWD>(a, stream);
+    else launch_recur_t<K, RECUR_FWD>(a, stream);
+}
+
+void launch_recur(const RecurArgs& a, int K, hipStream_t stream, RecurMode mode) {
+    if (K == 128) launch_recur_k<128>(a, stream, mode);
+    else launch_recur_k<64>(a, stream, mode);
 }
 
 }  // namespace kda

@@ -148,6 +148,18 @@ def gdn_workload(B, T, H, K, V, seed, *, init_std=None, lengths=None, decay_shif
     return Workload("gdn", name, q, k, v, g, beta, None, None, -5.0, K ** -0.5, h0, cu)
 
 
+def output_grads(w: Workload, seed, *, do_std=1.0, dfinal_std=None):
+    """Seeded gradients for the backward pass: dL/do ~N(0, do_std) bf16 [B,T,H,V]
+    and, when ``dfinal_std`` is given, dL/d(final state) ~N(0, dfinal_std) fp32
+    [N,H,K,V] (else None)."""
+    gen = torch.Generator().manual_seed(seed)
+    do = _normal(gen, (w.B, w.T, w.H, w.V), do_std).to(torch.bfloat16)
+    dfin = None
+    if dfinal_std is not None:
+        dfin = _normal(gen, (w.n_seqs, w.H, w.K, w.V), dfinal_std)
+    return do, dfin
+
+
 # The five workloads the benchmark and the parity suite are built around.
 CONFIG_NAMES = {
     0: "kda_tiny_B1_T256_H4_K64",

@@ -172,7 +172,6 @@ int kda_recur(const uint16_t* v, float scale, const float* initial_state, float*
               int32_t varlen, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
               int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Static description of a status code (never NULL). */
 /* One recurrent step per sequence: the single-token form of the same
  * recurrence, for decoding after a prefill (the cuLA pages list decode
  * kernels on their inference roadmap: cuLA blog, section "Status &
@@ -202,6 +201,52 @@ int gdn_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const fl
                const uint16_t* beta, float scale, const float* state_in, float* state_out,
                int32_t N, int32_t H, int32_t K, int32_t V, uint16_t* o, void* stream);
 
+/* Backward pass: the gradients of a scalar loss L with respect to every input
+ * of kda_fwd / gdn_fwd, given dL/do and, optionally, dL/d(final state).  The
+ * pages show the backward only as autograd over the forward call (cuLA
+ * README mirror, section "Usage": q, k, v with requires_grad and
+ * o.backward(do)); the cuLA roadmap lists backward kernels for training and
+ * the FlashQLA summary (section "핵심 기능") a backward path beside the forward
+ * one.  The result is the exact derivative of the forward recurrence above,
+ * computed chunkwise (recomputing the forward states; no state of a forward
+ * call is needed).  The floor max(lower_bound, x) passes the gradient where
+ * x >= lower_bound and blocks it where the floor is active.
+ *
+ * Inputs: the forward inputs (same layouts and conventions as kda_fwd /
+ * gdn_fwd), d_o [B, T, H, V] bf16 (dL/do), d_final [N, H, K, V] fp32 or NULL
+ * (dL/d final state; NULL = zero).
+ * Outputs (caller-allocated, every element written):
+ *   dq, dk [B, T, H, K] bf16;  dv [B, T, H, V] bf16;
+ *   KDA: dg [B, T, H, K] bf16 (w.r.t. the pre-activation gate), dbeta
+ *        [B, T, H] bf16 (w.r.t. the logits), dA_log [H] fp32, ddt_bias [H, K]
+ *        fp32 (sums over all tokens, in a fixed order: reproducible);
+ *   GDN: dg [B, T, H] fp32 (w.r.t. the log decay), dbeta [B, T, H] bf16
+ *        (w.r.t. the probabilities);
+ *   dh0 [N, H, K, V] fp32 or NULL (dL/d initial state; not written if NULL).
+ * Workspace: at least *_bwd_workspace_size() bytes, 256-byte aligned (it holds
+ * bf16 copies of the state entering every chunk and of its gradient, about
+ * 4 (K + C) V bytes per chunk and head, C = 32).  Alignment: d_o, dq, dk, dv,
+ * dg (KDA), d_final, dh0 16 bytes.  Errors and stream semantics as for the
+ * forward pass.  There is no sequence splitting in the backward pass. */
+size_t kda_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                              int32_t num_seqs);
+
+int kda_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+            const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
+            float scale, const float* initial_state, const int32_t* cu_seqlens,
+            int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+            const uint16_t* d_o, const float* d_final, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+            uint16_t* dg, uint16_t* dbeta, float* dA_log, float* ddt_bias, float* dh0,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+int gdn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+            const uint16_t* beta, float scale, const float* initial_state,
+            const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+            int32_t K, int32_t V, const uint16_t* d_o, const float* d_final, uint16_t* dq,
+            uint16_t* dk, uint16_t* dv, float* dg, uint16_t* dbeta, float* dh0, void* workspace,
+            size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
 const char* kda_status_str(int status);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

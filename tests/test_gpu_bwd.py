@@ -1,0 +1,214 @@
+"""GPU parity of the backward pass (kda_bwd / gdn_bwd through the C ABI)
+against the fp64 backward oracle (``oracle/backward.py``, itself pinned by
+finite differences and autograd), on the same seeded inputs.
+
+Acceptance per gradient tensor: relative Frobenius error <= 1e-2 and
+max |gpu - ref| <= 5e-2 * max(1, max |ref|).  The relative bound is the
+forward pass's; the absolute one is scaled to the tensor because gradients
+summed over many tokens (dA_log, ddt_bias, dh0) are far larger than 1 while
+their inputs carry the same bf16 rounding (2^-9 relative) as the forward
+operands.  Gate gradients are compared away from the floor of the log decay
+(|pre-activation decay - lower_bound| > 1e-3): there the floor's on/off
+decision, taken in fp32 on the GPU and in fp64 in the oracle, may differ.
+dA_log[h] and ddt_bias[h, c] are sums over tokens (and channels) of terms of
+both signs that largely cancel, so their error is bounded by the terms it
+sums: |gpu - ref| <= 2e-2 * sum |terms|, with the terms taken from the
+oracle's per-token dg.  The per-token errors are correlated (the bf16
+operands of the recurrence round the same state for every token of a
+chunk): an fp64 emulation of this algorithm with the same bf16 roundings
+reaches 0.97% of sum |terms| on the slow-decay case, hence 2%.  A sum with
+few surviving terms (most entries at the floor) is at the absolute noise of
+its head's gate gradients instead; there the bound is the one the dg
+acceptance implies (Cauchy-Schwarz: a sum of N errors whose Frobenius norm
+is at most 1e-2 * ||terms||_F is at most 1e-2 * sqrt(N) * ||terms||_F), and
+the larger of the two bounds applies.  The reduction itself is checked
+tighter: the GPU's sums must equal the sums of its own per-token dg to bf16
+rounding (2^-8 * sum |terms|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_kda_amd as kda
+from chunked_gated_delta_kda_amd import inputs
+from oracle import backward as obwd
+from parity_util import say, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+REL = 1e-2
+ABS = 5e-2
+SUM_REL = 2e-2
+
+
+def close(name, got, want, mask=None):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, f"{name}: shape {got.shape} vs {want.shape}"
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    if mask is not None:
+        got = np.where(mask, got, 0.0)
+        want = np.where(mask, want, 0.0)
+    n = np.linalg.norm(want)
+    rel = np.linalg.norm(got - want) / n if n > 0 else np.linalg.norm(got - want)
+    mx = float(np.max(np.abs(got - want))) if got.size else 0.0
+    lim = ABS * max(1.0, float(np.max(np.abs(want))) if want.size else 1.0)
+    say(f"  {name}: rel {rel:.3e} max {mx:.3e} (limit {lim:.3e})")
+    assert rel <= REL, f"{name}: relative Frobenius error {rel:.3e} > {REL}"
+    assert mx <= lim, f"{name}: max abs error {mx:.3e} > {lim:.3e}"
+
+
+def close_sum(name, got, want, scale, tol=REL, floor=0.0):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - want)
+    lim = np.maximum(tol * scale, floor) + 1e-12
+    say(f"  {name}: max err/limit {float(np.max(err / lim)):.3f}")
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    assert np.all(err <= lim), f"{name}: error {err.max():.3e} above {tol} x the terms' scale"
+
+
+def gate_sum_terms(w, dg, heads):
+    """Per-token terms of ddt_bias (dg itself) and of dA_log (da * pre-activation
+    decay, da = dg / (-rate sigmoid(x))) for the selected heads."""
+    hh = list(range(w.H)) if heads is None else list(heads)
+    x = w.g.double().numpy()[:, :, hh] + w.dt_bias.double().numpy().reshape(w.H, w.K)[hh][None, None]
+    rate = np.exp(w.A_log.double().numpy()[hh])[None, None, :, None]
+    da = dg / (-rate / (1.0 + np.exp(-x)))
+    return dg, da * (-rate * np.logaddexp(0.0, x))
+
+
+def gpu_bwd(w, do, dfin):
+    d = w.to(DEV)
+    dod = do.to(DEV)
+    dfd = None if dfin is None else dfin.to(DEV)
+    if w.kind == "kda":
+        r = kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], dod,
+                        w.lower_bound, w.scale, d["initial_state"], dfd, d["cu_seqlens"])
+    else:
+        r = kda.gdn_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], dod, w.scale,
+                        d["initial_state"], dfd, d["cu_seqlens"])
+    torch.cuda.synchronize()
+    return r
+
+
+def ref_bwd(w, do, dfin, heads=None):
+    if w.kind == "kda":
+        return obwd.kda_bwd(w.q, w.k, w.v, w.g, w.beta, w.A_log, w.dt_bias, w.lower_bound,
+                            w.scale, w.initial_state, do, dfin, w.cu_seqlens, heads=heads)
+    return obwd.gdn_bwd(w.q, w.k, w.v, w.g, w.beta, w.scale, w.initial_state, do, dfin,
+                        w.cu_seqlens, heads=heads)
+
+
+def floor_mask(w, heads=None):
+    """Entries whose pre-activation log decay is not within 1e-3 of the floor."""
+    g = w.g.double().numpy()
+    dt = w.dt_bias.double().numpy().reshape(w.H, w.K)
+    rate = np.exp(w.A_log.double().numpy())
+    x = g + dt[None, None]
+    pre = -rate[None, None, :, None] * np.logaddexp(0.0, x)
+    m = np.abs(pre - w.lower_bound) > 1e-3
+    return m if heads is None else m[:, :, heads]
+
+
+def check_bwd(w, do, dfin, heads=None):
+    say(f"[bwd] {w.name}: B={w.B} T={w.T} H={w.H} K={w.K} V={w.V} N={w.n_seqs} "
+        f"heads={'all' if heads is None else heads} dfinal={dfin is not None}")
+    r = gpu_bwd(w, do, dfin)
+    ref = ref_bwd(w, do, dfin, heads)
+    hsel = (lambda t, ax: to64(t, heads, ax)) if heads is not None else (lambda t, ax: to64(t))
+    close("dq", hsel(r["dq"], 2), ref["dq"])
+    close("dk", hsel(r["dk"], 2), ref["dk"])
+    close("dv", hsel(r["dv"], 2), ref["dv"])
+    close("dbeta", hsel(r["dbeta"], 2), ref["dbeta"])
+    close("dh0", hsel(r["dh0"], 1), ref["dh0"])
+    if w.kind == "kda":
+        mask = floor_mask(w, heads)
+        close("dg", hsel(r["dg"], 2), ref["dg"], mask)
+        if mask.all():
+            tdt, tal = gate_sum_terms(w, ref["dg"], heads)
+            gdt, gal = gate_sum_terms(w, hsel(r["dg"], 2), heads)
+            ddt, dal = hsel(r["ddt_bias"], 0), hsel(r["dA_log"], 0)
+            ntok = tdt.shape[0] * tdt.shape[1]
+            fro_dt = np.sqrt((tdt ** 2).sum(axis=(0, 1, 3)))[:, None]  # per head
+            fro_al = np.sqrt((tal ** 2).sum(axis=(0, 1, 3)))
+            close_sum("ddt_bias", ddt, ref["ddt_bias"], np.abs(tdt).sum(axis=(0, 1)), SUM_REL,
+                      REL * np.sqrt(ntok) * fro_dt)
+            close_sum("dA_log", dal, ref["dA_log"], np.abs(tal).sum(axis=(0, 1, 3)), SUM_REL,
+                      REL * np.sqrt(ntok * w.K) * fro_al)
+            close_sum("ddt_bias = sum of dg", ddt, gdt.sum(axis=(0, 1)),
+                      np.abs(gdt).sum(axis=(0, 1)), 2.0 ** -8)
+            close_sum("dA_log = sum of its terms", dal, gal.sum(axis=(0, 1, 3)),
+                      np.abs(gal).sum(axis=(0, 1, 3)), 2.0 ** -8)
+    else:
+        close("dg", hsel(r["dg"], 2), ref["dg"])
+    return r
+
+
+CASES = [
+    ("tiny K=V=64 default decay",
+     lambda: inputs.kda_workload(1, 256, 4, 64, 64, seed=7000, name="bwd_tiny"), None),
+    ("slow decay T=300 ragged tail, state gradient",
+     lambda: inputs.kda_workload(1, 300, 2, 128, 128, seed=7100, dt_bias_value=-6.0,
+                                 init_std=0.05, name="bwd_slow"), 0.05),
+    ("default decay B2 T=200",
+     lambda: inputs.kda_workload(2, 200, 3, 128, 128, seed=7200, init_std=0.05,
+                                 name="bwd_default"), 0.05),
+    ("K=128 V=64",
+     lambda: inputs.kda_workload(1, 150, 2, 128, 64, seed=7300, dt_bias_value=-6.0,
+                                 init_std=0.05, name="bwd_k128v64"), 0.05),
+    ("K=64 V=128",
+     lambda: inputs.kda_workload(1, 150, 2, 64, 128, seed=7400, dt_bias_value=-6.0,
+                                 init_std=0.05, name="bwd_k64v128"), 0.05),
+    ("varlen with empty and short sequences",
+     lambda: inputs.kda_workload(1, 0, 2, 128, 128, seed=7500, dt_bias_value=-6.0,
+                                 init_std=0.05, lengths=[0, 70, 5, 200, 33], name="bwd_varlen"),
+     0.05),
+    ("GDN slow decay",
+     lambda: inputs.gdn_workload(2, 180, 2, 128, 128, seed=7600, init_std=0.05, decay_shift=-6.0,
+                                 name="bwd_gdn"), 0.05),
+    ("GDN default decay, no state",
+     lambda: inputs.gdn_workload(1, 100, 3, 128, 128, seed=7700, name="bwd_gdn_default"), None),
+]
+
+
+@pytest.mark.parametrize("name,make,dfs", CASES, ids=[c[0] for c in CASES])
+def test_bwd_matches_oracle(name, make, dfs):
+    w = make()
+    do, dfin = inputs.output_grads(w, seed=sum(map(ord, name)), dfinal_std=dfs)
+    check_bwd(w, do, dfin)
+
+
+def test_bwd_clamp_active():
+    """The floor binds on most entries (g ~ N(8, 1)): those get zero gate gradient."""
+    w = inputs.kda_workload(1, 120, 2, 128, 128, seed=7800, g_mean=8.0, g_std=1.0,
+                            init_std=0.05, name="bwd_clamp")
+    do, dfin = inputs.output_grads(w, seed=7801, dfinal_std=0.05)
+    r = check_bwd(w, do, dfin)
+    clamped = ~floor_mask(w) & (w.g.double().numpy() > 2)
+    assert np.all(to64(r["dg"])[clamped] == 0.0)
+
+
+def test_bwd_config1_sampled_heads():
+    """The benchmark workload (B2 T2048 H32 K=V=128) on its full launch; the oracle
+    on three heads."""
+    w = inputs.config(1)
+    do, dfin = inputs.output_grads(w, seed=7900, dfinal_std=0.05)
+    check_bwd(w, do, dfin, heads=[0, 13, 31])
+
+
+def test_bwd_deterministic():
+    w = inputs.kda_workload(1, 400, 2, 128, 128, seed=8000, dt_bias_value=-6.0, init_std=0.05)
+    do, dfin = inputs.output_grads(w, seed=8001, dfinal_std=0.05)
+    r1 = gpu_bwd(w, do, dfin)
+    r2 = gpu_bwd(w, do, dfin)
+    for key in r1:
+        assert torch.equal(r1[key], r2[key]), key
+
+
+def test_bwd_empty_sequence_batch():
+    """T = 0: dh0 equals dL/d(final state); the gate-parameter gradients are zero."""
+    w = inputs.kda_workload(2, 0, 2, 64, 64, seed=8100, init_std=0.05)
+    do, dfin = inputs.output_grads(w, seed=8101, dfinal_std=0.05)
+    r = gpu_bwd(w, do, dfin)
+    assert torch.equal(r["dh0"].cpu(), dfin)
+    assert torch.count_nonzero(r["dA_log"]) == 0 and torch.count_nonzero(r["ddt_bias"]) == 0
