@@ -153,6 +153,62 @@ def bench_decode(args, torch, kda, inputs, dev):
     }), flush=True)
 
 
+def bench_bwd(args, torch, kda, inputs, dev):
+    """The backward pass (kda_bwd: every gradient, from dL/do and dL/d final state)
+    on the benchmark workload, input sets rotated as for the forward pass.  Its
+    algorithmic bytes per token-head are the reads of q, k, g, v, beta, do and the
+    writes of dq, dk, dg, dv, dbeta (12 K + 6 V + 4 bytes), plus per (sequence,
+    head) the initial state and the final-state gradient read and dh0 written."""
+    base = inputs.config(1)
+    B, T, H, K, V, N = base.B, base.T, base.H, base.K, base.V, base.n_seqs
+    sets = []
+    for r in range(args.sets):
+        w = base if r == 0 else inputs.kda_workload(B, T, H, K, V, seed=1001 + 1000 * r,
+                                                    init_std=0.05)
+        do, dfin = inputs.output_grads(w, seed=5000 + r, dfinal_std=0.05)
+        d = w.to(dev)
+        d["do"], d["dfin"] = do.to(dev), dfin.to(dev)
+        sets.append(d)
+    ws = torch.empty(kda.bwd_workspace_size(B, T, H, K, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = sets[i % len(sets)]
+        kda.kda_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
+                    d["do"], base.lower_bound, base.scale, d["initial_state"], d["dfin"],
+                    workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    nbytes = B * T * H * (12 * K + 6 * V + 4) + N * H * 3 * K * V * 4 + 2 * H * (K + 1) * 4
+    achieved = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "kda backward tokens/sec (all gradients), B2 T2048 H32 K=V=128",
+        "value": round(B * T / (elapsed / args.steps), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": inputs.CONFIG_NAMES[1] + "_bwd", "B": B, "T": T, "H": H, "K": K,
+                   "V": V, "chunk": C, "input_sets_rotated": len(sets)},
+        "roofline": {"bound": "hbm", "kernel": "kda_bwd (whole call, six launches)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(nbytes),
+                     "avg_launch_us": round(us, 2)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +221,9 @@ def main():
                     help="instead of the forward pass, time the single-token decode step "
                          "(kda_decode) for --decode-seqs sequences x 32 heads, K=V=128")
     ap.add_argument("--decode-seqs", type=int, default=64)
+    ap.add_argument("--bwd", action="store_true",
+                    help="instead of the forward pass, time the backward pass (kda_bwd) on "
+                         "the same workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, copy BYTES bytes device-to-device "
                          "--steps times (the known-size reference for HBM byte counters)")
@@ -201,6 +260,9 @@ def main():
 
     if args.decode:
         bench_decode(args, torch, kda, inputs, dev)
+        return
+    if args.bwd:
+        bench_bwd(args, torch, kda, inputs, dev)
         return
 
     base = inputs.config(1)

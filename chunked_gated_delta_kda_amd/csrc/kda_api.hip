@@ -83,18 +83,18 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Backward pass, after the forward layout (tables, records, bounds): the
 // reverse-pass records, the chunk states and V - KG S of the forward sweep,
-// the state gradients and dL/dU' of the reverse sweep (bf16), and the
+// the state gradients, dL/dU' and dL/dV of the reverse sweep (bf16), and the
 // per-chunk sums of the gate-parameter gradients.
 struct BwdLayout {
     unsigned char* brec;
-    uint16_t *hs, *zt, *dss, *dut;
+    uint16_t *hs, *zt, *dss, *dut, *yt;
     float *part_dt, *part_alog;
 };
 
 size_t bwd_extra_bytes(int64_t slots, int32_t H, int32_t K, int32_t V) {
     const size_t ch = (size_t)slots * H;
     return align_up(ch * kda::record_bytes(K)) + 2 * align_up(ch * K * V * 2) +
-           2 * align_up(ch * V * kda::C * 2) + align_up(ch * K * 4) + align_up(ch * 4);
+           3 * align_up(ch * V * kda::C * 2) + align_up(ch * K * 4) + align_up(ch * 4);
 }
 
 BwdLayout bwd_layout(unsigned char* p, int64_t slots, int32_t H, int32_t K, int32_t V) {
@@ -109,6 +109,8 @@ BwdLayout bwd_layout(unsigned char* p, int64_t slots, int32_t H, int32_t K, int3
     b.zt = reinterpret_cast<uint16_t*>(p);
     p += align_up(ch * V * kda::C * 2);
     b.dut = reinterpret_cast<uint16_t*>(p);
+    p += align_up(ch * V * kda::C * 2);
+    b.yt = reinterpret_cast<uint16_t*>(p);
     p += align_up(ch * V * kda::C * 2);
     b.part_dt = reinterpret_cast<float*>(p);
     p += align_up(ch * K * 4);
@@ -348,6 +350,7 @@ int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& 
     rb.o = io.dv;
     rb.chunk_state = bl.dss;
     rb.chunk_u = bl.dut;
+    rb.chunk_y = bl.yt;
     kda::launch_recur(rb, c.K, stream, kda::RECUR_BWD);
     kda::BwdArgs ba{};
     ba.q = c.q;
@@ -366,6 +369,7 @@ int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& 
     ba.zt = bl.zt;
     ba.dss = bl.dss;
     ba.dut = bl.dut;
+    ba.yt = bl.yt;
     ba.dq = io.dq;
     ba.dk = io.dk;
     ba.dg_kda = io.dg_kda;

@@ -174,49 +174,73 @@ __device__ __forceinline__ void put_split(A& arr, int part, int c, int p, float 
 
 }  // namespace
 
-// One workgroup per (chunk slot, head) with one wave per 16-token block; lane
-// l = m + 16 g of wave b owns token 16 b + m and the channels 32 j + 8 g + e
-// (the row layout of kda_prep).  Products that contract over channels read
-// their operands from registers; products that contract over tokens read
-// token-ordered copies from LDS; products that contract over value columns
-// read the stored states and [C, V] rows.  Every result that is a function
-// of (token, channel) is produced transposed (channels as MFMA rows in the
-// tile_channel order), which lands it in the owner lane's registers.
+// One workgroup per (chunk slot, head) and four waves: wave w owns the
+// 16-token block b = w % 2 and the channel half hf = w / 2.  Lane
+// l = m + 16 g of a wave owns token 16 b + m and the channels 32 j + 8 g + e
+// of its half's k-steps j (the row layout of kda_prep, split in two).
+// Products that contract over channels read their operands from registers
+// (partial sums over the two halves meet in LDS); products that contract over
+// tokens read token-ordered copies from LDS; products that contract over
+// value columns read the stored states and [C, V] rows.  Every result that is
+// a function of (token, channel) is produced transposed (channels as MFMA rows
+// in the tile_channel order), which lands it in the owner lane's registers.
 template <int K, int V, bool GDN>
-__global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_bwd_chunk_kernel(
+    BwdArgs a) {
     static_assert(NB == 2, "the gradient kernel assumes 32-token chunks");
-    constexpr int KS = K / 32, KT = K / 16, VS = V / 32, VT = V / 16;
+    constexpr int KS = K / 32, KH = KS / 2, KT = K / 16, VS = V / 32, VT = V / 16;
     constexpr int UP = V + 8;  // padded row of the U' / W1 copies (bf16)
     using R = Rec<K>;
-    __shared__ float gend_s[2][K];                                    // block totals (log2)
-    __shared__ float beta_s[C];
-    __shared__ float P_s[C][C + 1];                                   // tril_strict(KG Kinv^T)
-    __shared__ __attribute__((aligned(16))) uint16_t tt_s[C][C];      // [r][pos(s)] = T[s][r]
-    __shared__ __attribute__((aligned(16))) uint16_t u_s[C][UP];      // U' rows
-    __shared__ __attribute__((aligned(16))) uint16_t w_s[C][UP];      // W1 rows
-    __shared__ __attribute__((aligned(16))) bf16x8 kbc0_s[KS * 64];   // block 0: k^ 2^(G_end0 - G)
-    // channel-major token operands [part][c][pos(s)]: 0: k^ 2^-Gl, 1: k^ 2^(G_end0 - Gl)
-    // (block 0), 2: q^ 2^Gl, 3: k^ 2^Gl (Gl: log2 decay within the token's block),
-    // each as a bf16 pair hi + lo.  A token pair (r, j) enters dG_r through one
-    // operand and dG_j, with the opposite sign, through another; in the reverse
+    // LDS, 80 KB at K = V = 128 so that two workgroups share a CU: regions
+    // whose lifetimes do not overlap share memory (the phase of each is noted).
+    constexpr int OFF_GEND = 0;                               // float [2][K], all phases
+    constexpr int OFF_BETA = OFF_GEND + 2 * K * 4;            // float [C], until dM
+    constexpr int OFF_P = OFF_BETA + C * 4;                   // float [C][C+1], P .. dM
+    constexpr int OFF_XT = OFF_P + C * (C + 1) * 4;           // bf16 [2][3][K][C], P .. intra
+    constexpr int OFF_U = OFF_XT + 2 * 3 * K * C * 2;         // bf16 [C][UP], U' .. V-products
+    constexpr int OFF_W = OFF_U + C * UP * 2;                 // bf16 [C][UP], U' .. dM;
+                                                              //   then the late sums below
+    constexpr int OFF_DM = OFF_W + C * UP * 2;                // bf16 4 x [C][C], dM .. intra;
+                                                              //   before: kbc0, norms
+    constexpr int OFF_DB = OFF_DM + 4 * C * C * 2;            // float [2][C], dM .. end
+    constexpr int LDS_BYTES = OFF_DB + 2 * C * 4;
+    static_assert(KS * 64 * 16 + C * C * 2 + 2 * C * 2 * 4 <= 4 * C * C * 2, "early region");
+    static_assert(2 * K * 4 + K * 4 * 2 + 2 * C * 2 * 4 + 4 * 4 <= C * UP * 2 + 2 * K * 4, "late region");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+    auto& gend_s = *reinterpret_cast<float(*)[2][K]>(smem + OFF_GEND);
+    auto& beta_s = *reinterpret_cast<float(*)[C]>(smem + OFF_BETA);
+    auto& P_s = *reinterpret_cast<float(*)[C][C + 1]>(smem + OFF_P);  // tril_strict(KG Kinv^T)
+    // channel-major token operands [hi/lo][part][c][pos(s)]: 0: k^ 2^-Gl,
+    // 1: q^ 2^Gl, 2: k^ 2^Gl (Gl: log2 decay within the token's block), each as
+    // a bf16 pair hi + lo.  A token pair (r, j) enters dG_r through one operand
+    // and dG_j, with the opposite sign, through another; in the reverse
     // cumulative sum over the chunk the two cancel exactly unless their
     // roundings differ, so these operands carry ~16 significant bits.
-    __shared__ __attribute__((aligned(16))) uint16_t xt_s[2][4][K][C];
-    __shared__ __attribute__((aligned(16))) uint16_t dmr_s[C][C];     // [r][pos(j)] = dM[r][j]
-    __shared__ __attribute__((aligned(16))) uint16_t dmc_s[C][C];     // [j][pos(r)] = dM[r][j]
-    __shared__ __attribute__((aligned(16))) uint16_t dpr_s[C][C];
-    __shared__ __attribute__((aligned(16))) uint16_t dpc_s[C][C];
-    __shared__ float dbeta_s[C];
-    __shared__ float kd_s[2][K];   // per block: sum over tokens of k^ dk^_Kd
-    __shared__ float hs_s[K];      // rowsum(h * dS')
-    __shared__ float tot_s[K];     // block 1's total of dG per channel
-    __shared__ float red_s[2][K];  // per block: sum over tokens of dL/d(dt_bias)
-    __shared__ float alog_s[2];
+    auto& xt_s = *reinterpret_cast<uint16_t(*)[2][3][K][C]>(smem + OFF_XT);
+    auto& u_s = *reinterpret_cast<uint16_t(*)[C][UP]>(smem + OFF_U);  // U' rows
+    auto& w_s = *reinterpret_cast<uint16_t(*)[C][UP]>(smem + OFF_W);  // W1 rows
+    auto& dmr_s = *reinterpret_cast<uint16_t(*)[C][C]>(smem + OFF_DM);              // [r][pos(j)]
+    auto& dmc_s = *reinterpret_cast<uint16_t(*)[C][C]>(smem + OFF_DM + C * C * 2);  // [j][pos(r)]
+    auto& dpr_s = *reinterpret_cast<uint16_t(*)[C][C]>(smem + OFF_DM + 2 * C * C * 2);
+    auto& dpc_s = *reinterpret_cast<uint16_t(*)[C][C]>(smem + OFF_DM + 3 * C * C * 2);
+    // early tenants of the dM region
+    auto& kbc0_s = *reinterpret_cast<bf16x8(*)[KS * 64]>(smem + OFF_DM);  // block 0: k^ 2^(G_end0 - G)
+    auto& nrm_s = *reinterpret_cast<float(*)[2][C][2]>(smem + OFF_DM + KS * 64 * 16 + C * C * 2);
+    auto& dbeta_s = *reinterpret_cast<float(*)[2][C]>(smem + OFF_DB);  // per half
+    // late tenants of the W1 region
+    auto& kd_s = *reinterpret_cast<float(*)[2][K]>(smem + OFF_W);  // per block: sum of k^ dk^_Kd
+    auto& hs_s = *reinterpret_cast<float(*)[K]>(smem + OFF_W + 2 * K * 4);  // rowsum(h * dS')
+    auto& tot_s = *reinterpret_cast<float(*)[K]>(smem + OFF_W + 3 * K * 4);  // block 1's dG totals
+    auto& dot_s = *reinterpret_cast<float(*)[2][C][2]>(smem + OFF_W + 4 * K * 4);
+    auto& red_s = *reinterpret_cast<float(*)[2][K]>(smem + OFF_W + 4 * K * 4 + 2 * C * 2 * 4);
+    auto& alog_s = *reinterpret_cast<float(*)[4]>(smem + OFF_W + 6 * K * 4 + 2 * C * 2 * 4);
 
     const int slot = blockIdx.x;
     const int h = blockIdx.y;
-    const int blk = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6;
+    const int blk = wave & 1, hf = wave >> 1;
     const int L = threadIdx.x & 63, m = L & 15, g = L >> 4;
+    const int j0 = hf * KH;  // this wave's first k-step (channels 32 j0 ..)
 
     int n;
     if (!a.packed) {
@@ -228,7 +252,7 @@ __global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
             // its share of the gate-parameter sums is zero
             if constexpr (!GDN) {
                 const int64_t chb = (int64_t)slot * a.H + h;
-                for (int c = threadIdx.x; c < K; c += 128) a.part_dt[chb * K + c] = 0.f;
+                for (int c = threadIdx.x; c < K; c += 256) a.part_dt[chb * K + c] = 0.f;
                 if (threadIdx.x == 0) a.part_alog[chb] = 0.f;
             }
             return;
@@ -250,35 +274,27 @@ __global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
     const int64_t lrow = (start + (valid ? row : 0)) * a.H + h;
     const int64_t ch_base = (int64_t)slot * a.H + h;  // chunk-head index of the stored tensors
 
-    // ---- this lane's row: q^, k^, log2 decay, beta
-    float qh[KS][8], kh[KS][8], G[KS][8];
-    float iq, ik;
+    // ---- this lane's row and channels: q^, k^, log2 decay; beta
+    float qh[KH][8], kh[KH][8], G[KH][8];
     {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            const int c = 32 * j + 8 * g;
-            const u32x4 qv = *reinterpret_cast<const u32x4*>(a.q + lrow * K + c);
-            const u32x4 kv = *reinterpret_cast<const u32x4*>(a.k + lrow * K + c);
-            unpack8(qv, qh[j]);
-            unpack8(kv, kh[j]);
+        for (int jj = 0; jj < KH; ++jj) {
+            const int c = 32 * (j0 + jj) + 8 * g;
+            unpack8(*reinterpret_cast<const u32x4*>(a.q + lrow * K + c), qh[jj]);
+            unpack8(*reinterpret_cast<const u32x4*>(a.k + lrow * K + c), kh[jj]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (!valid) { qh[j][e] = 0.f; kh[j][e] = 0.f; }
-                sq += qh[j][e] * qh[j][e];
-                sk += kh[j][e] * kh[j][e];
+                if (!valid) { qh[jj][e] = 0.f; kh[jj][e] = 0.f; }
+                sq += qh[jj][e] * qh[jj][e];
+                sk += kh[jj][e] * kh[jj][e];
             }
         }
         sq += __shfl_xor(sq, 16, 64);
         sq += __shfl_xor(sq, 32, 64);
         sk += __shfl_xor(sk, 16, 64);
         sk += __shfl_xor(sk, 32, 64);
-        iq = rsq_hw(sq + NORM_EPS);
-        ik = rsq_hw(sk + NORM_EPS);
-#pragma unroll
-        for (int j = 0; j < KS; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { qh[j][e] *= iq; kh[j][e] *= ik; }
+        if (g == 0) { nrm_s[hf][row][0] = sq; nrm_s[hf][row][1] = sk; }
     }
     const float braw = bf2f(a.beta[lrow]);
     const float b = valid ? (GDN ? braw : sigmoid_f(braw)) : 0.f;
@@ -286,55 +302,61 @@ __global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
     if constexpr (GDN) {
         const float la = valid ? a.g_gdn[lrow] * LOG2E : 0.f;
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
+        for (int jj = 0; jj < KH; ++jj)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) G[j][e] = la;
+            for (int e = 0; e < 8; ++e) G[jj][e] = la;
     } else {
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            const int c = 32 * j + 8 * g;
+        for (int jj = 0; jj < KH; ++jj) {
+            const int c = 32 * (j0 + jj) + 8 * g;
             float x[8];
             unpack8(*reinterpret_cast<const u32x4*>(a.g_kda + lrow * K + c), x);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                G[j][e] = valid ? fmaxf(a.lower_bound, -rate * softplus_f(x[e] + a.dt_bias[(int64_t)h * K + c + e])) * LOG2E
-                                : 0.f;
+                G[jj][e] = valid ? fmaxf(a.lower_bound,
+                                         -rate * softplus_f(x[e] + a.dt_bias[(int64_t)h * K + c + e])) * LOG2E
+                                 : 0.f;
         }
     }
     // in-block inclusive prefix (log2), block totals to LDS
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
+    for (int jj = 0; jj < KH; ++jj)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            G[j][e] = row_scan16(G[j][e]);
-            if (m == 15) gend_s[blk][32 * j + 8 * g + e] = G[j][e];
+            G[jj][e] = row_scan16(G[jj][e]);
+            if (m == 15) gend_s[blk][32 * (j0 + jj) + 8 * g + e] = G[jj][e];
         }
-    if (g == 0) beta_s[row] = b;
+    if (hf == 0 && g == 0) beta_s[row] = b;
     __syncthreads();
-
-    // ---- decay-weighted operands; in-block P; transposed copies for token products
-    floatx4 Pacc = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 ka_f[KS];
+    const float iq = rsq_hw(nrm_s[0][row][0] + nrm_s[1][row][0] + NORM_EPS);
+    const float ik = rsq_hw(nrm_s[0][row][1] + nrm_s[1][row][1] + NORM_EPS);
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
+    for (int jj = 0; jj < KH; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { qh[jj][e] *= iq; kh[jj][e] *= ik; }
+
+    // ---- decay-weighted operands; this half's share of P; token-ordered copies
+    floatx4 Pacc = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 ka_f[KH];
+#pragma unroll
+    for (int jj = 0; jj < KH; ++jj) {
         float ka[8], kbs[8], kbc[8], qa[8];
+        const int p = tok_pos(row);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int c = 32 * j + 8 * g + e;
-            const float ga = exp2_hw(G[j][e]);
-            ka[e] = kh[j][e] * ga;
-            qa[e] = qh[j][e] * ga;
-            kbs[e] = kh[j][e] * exp2_hw(-G[j][e]);
-            kbc[e] = kh[j][e] * exp2_hw(gend_s[0][c] - G[j][e]);  // used for block 0 only
-            const int p = tok_pos(row);
+            const int c = 32 * (j0 + jj) + 8 * g + e;
+            const float ga = exp2_hw(G[jj][e]);
+            ka[e] = kh[jj][e] * ga;
+            qa[e] = qh[jj][e] * ga;
+            kbs[e] = kh[jj][e] * exp2_hw(-G[jj][e]);
+            kbc[e] = kh[jj][e] * exp2_hw(gend_s[0][c] - G[jj][e]);  // used for block 0 only
             put_split(xt_s, 0, c, p, kbs[e]);
-            if (blk == 0) put_split(xt_s, 1, c, p, kbc[e]);
-            put_split(xt_s, 2, c, p, qa[e]);
-            put_split(xt_s, 3, c, p, ka[e]);
+            put_split(xt_s, 1, c, p, qa[e]);
+            put_split(xt_s, 2, c, p, ka[e]);
         }
-        ka_f[j] = pack8(ka);
-        Pacc = mfma32(ka_f[j], pack8(kbs), Pacc);  // P[16b + 4g' + i][16b + n]
-        if (blk == 0) kbc0_s[j * 64 + L] = pack8(kbc);
+        ka_f[jj] = pack8(ka);
+        Pacc = mfma32(ka_f[jj], pack8(kbs), Pacc);  // P[16b + 4g' + i][16b + n], this half
+        if (blk == 0) kbc0_s[(j0 + jj) * 64 + L] = pack8(kbc);
     }
     __syncthreads();
     {
@@ -342,61 +364,71 @@ __global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
         floatx4 Pc = {0.f, 0.f, 0.f, 0.f};
         if (blk == 1) {
 #pragma unroll
-            for (int j = 0; j < KS; ++j) Pc = mfma32(ka_f[j], kbc0_s[j * 64 + L], Pc);
+            for (int jj = 0; jj < KH; ++jj) Pc = mfma32(ka_f[jj], kbc0_s[(j0 + jj) * 64 + L], Pc);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * blk + 4 * g + i;
-            P_s[r][16 * blk + m] = (m < 4 * g + i) ? Pacc[i] : 0.f;
-            P_s[r][16 * (1 - blk) + m] = blk == 1 ? Pc[i] : 0.f;
-        }
-    }
-    __syncthreads();
-
-    // ---- T = (I + diag(b) P)^-1 by forward substitution: lane j of wave 0 owns column j
-    if (blk == 0 && L < C) {
-        float Tc[C];
-#pragma unroll
-        for (int r = 0; r < C; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int s = 0; s < r; ++s) acc += P_s[r][s] * Tc[s];
-            Tc[r] = (r == L ? 1.f : 0.f) - beta_s[r] * acc;
-        }
-#pragma unroll
-        for (int r = 0; r < C; ++r) tt_s[L][tok_pos(r)] = bits(Tc[r]);
-    }
-    __syncthreads();
-
-    // ---- U' = Tb Z and W1 = T^T dU for this block's rows (D layout, V/16 tiles);
-    // rowdot(W1, Z) on the way
-    float zw[4] = {0.f, 0.f, 0.f, 0.f};
-    {
-        const bf16xEL tb = *reinterpret_cast<const bf16xEL*>(
-            a.rec + ch_base * R::BYTES + R::TB + (blk * 64 + L) * (2 * EL));
-        const bf16xEL tt = *reinterpret_cast<const bf16xEL*>(&tt_s[16 * blk + m][EL * g]);
-        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt) {
-            const int col = 16 * vt + m;
-            const u32x4 wz = *reinterpret_cast<const u32x4*>(a.zt + (ch_base * V + col) * C + EL * g);
-            const bf16xEL bz = __builtin_bit_cast(bf16xEL, wz);
-            const bf16xEL bu = *reinterpret_cast<const bf16xEL*>(a.dut + (ch_base * V + col) * C + EL * g);
-            const floatx4 U = mfma_tok(tb, bz, zero);
-            const floatx4 W = mfma_tok(tt, bu, zero);
-            float zf[8];
-            unpack8(wz, zf);
+        // the two channel halves add up: half 1 writes, half 0 adds
+        if (hf == 1) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                zw[i] += W[i] * zf[4 * blk + i];  // Z[16b + 4g + i][col]
-                u_s[16 * blk + 4 * g + i][col] = bits(U[i]);
-                w_s[16 * blk + 4 * g + i][col] = bits(W[i]);
+                const int r = 16 * blk + 4 * g + i;
+                P_s[r][16 * blk + m] = (m < 4 * g + i) ? Pacc[i] : 0.f;
+                P_s[r][16 * (1 - blk) + m] = blk == 1 ? Pc[i] : 0.f;
+            }
+        }
+        __syncthreads();
+        if (hf == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * blk + 4 * g + i;
+                if (m < 4 * g + i) P_s[r][16 * blk + m] += Pacc[i];
+                if (blk == 1) P_s[r][m] += Pc[i];
             }
         }
     }
     __syncthreads();
 
-    // ---- dM = scale tril(dO U'^T), E1 = W1 U'^T, dP, db (this block's rows)
+    // ---- U' = Tb Z and W1 = T^T dU for this block's rows and this half's value
+    // tiles (D layout); rowdot(W1, Z) on the way.  W1 needs no inverse:
+    // (I + diag(b) P)^T W1 = dU and diag(b) W1 = Tb^T dU = dV give
+    // W1 = dU - P^T dV.
+    float zw[4] = {0.f, 0.f, 0.f, 0.f};
+    {
+        const bf16xEL tb = *reinterpret_cast<const bf16xEL*>(
+            a.rec + ch_base * R::BYTES + R::TB + (blk * 64 + L) * (2 * EL));
+        // P^T rows of this block as a token operand: slot (g, e) holds P[tok(g, e)][16 b + m]
+        float ptf[EL];
+#pragma unroll
+        for (int e = 0; e < EL; ++e) ptf[e] = P_s[16 * (e >> 2) + 4 * g + (e & 3)][16 * blk + m];
+        const bf16xEL apt = pack8(ptf);
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int vv = 0; vv < VT / 2; ++vv) {
+            const int col = 16 * (hf * (VT / 2) + vv) + m;
+            const int64_t cbase = (ch_base * V + col) * C;
+            const u32x4 wz = *reinterpret_cast<const u32x4*>(a.zt + cbase + EL * g);
+            const bf16xEL bz = __builtin_bit_cast(bf16xEL, wz);
+            const bf16xEL by = *reinterpret_cast<const bf16xEL*>(a.yt + cbase + EL * g);
+            // dU in D layout: rows 16 b + 4 g + i sit at positions EL g + 4 b + i
+            const uint2 wdu = *reinterpret_cast<const uint2*>(a.dut + cbase + EL * g + 4 * blk);
+            const floatx4 U = mfma_tok(tb, bz, zero);
+            const floatx4 PY = mfma_tok(apt, by, zero);
+            const float duf[4] = {bf2f(wdu.x & 0xffff), bf2f(wdu.x >> 16), bf2f(wdu.y & 0xffff),
+                                  bf2f(wdu.y >> 16)};
+            float zf[8];
+            unpack8(wz, zf);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float Wi = duf[i] - PY[i];
+                zw[i] += Wi * zf[4 * blk + i];  // Z[16b + 4g + i][col]
+                u_s[16 * blk + 4 * g + i][col] = bits(U[i]);
+                w_s[16 * blk + 4 * g + i][col] = bits(Wi);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- dM = scale tril(dO U'^T), E1 = W1 U'^T, dP for this block's rows and
+    // the 16 columns cb = hf; db's share
     bf16x8 dof[VS];
 #pragma unroll
     for (int jv = 0; jv < VS; ++jv) {
@@ -405,110 +437,119 @@ __global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
         dof[jv] = __builtin_bit_cast(bf16x8, valid ? x : zero4);
     }
     {
+        const int cb = hf;
         float dbp[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) dbp[i] = zw[i];
+        floatx4 dm = {0.f, 0.f, 0.f, 0.f}, e1 = dm;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            floatx4 dm = {0.f, 0.f, 0.f, 0.f}, e1 = dm;
-#pragma unroll
-            for (int jv = 0; jv < VS; ++jv) {
-                const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&u_s[16 * cb + m][32 * jv + 8 * g]);
-                const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_s[16 * blk + m][32 * jv + 8 * g]);
-                dm = mfma32(dof[jv], bu, dm);
-                e1 = mfma32(aw, bu, e1);
-            }
-            const int j = 16 * cb + m;  // this lane's column
-            bf16x4 dmv, dpv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * blk + 4 * g + i;
-                const float dmx = j <= r ? a.scale * dm[i] : 0.f;
-                const float dpx = j < r ? -beta_s[r] * e1[i] : 0.f;
-                if (j < r) dbp[i] -= P_s[r][j] * e1[i];
-                dmr_s[r][tok_pos(j)] = bits(dmx);
-                dpr_s[r][tok_pos(j)] = bits(dpx);
-                dmv[i] = (bf16)dmx;
-                dpv[i] = (bf16)dpx;
-            }
-            // [j][pos(r)]: rows 16 b + 4 g + i sit at positions EL g + 4 b + i
-            *reinterpret_cast<bf16x4*>(&dmc_s[j][EL * g + 4 * blk]) = dmv;
-            *reinterpret_cast<bf16x4*>(&dpc_s[j][EL * g + 4 * blk]) = dpv;
+        for (int jv = 0; jv < VS; ++jv) {
+            const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&u_s[16 * cb + m][32 * jv + 8 * g]);
+            const bf16x8 aw = *reinterpret_cast<const bf16x8*>(&w_s[16 * blk + m][32 * jv + 8 * g]);
+            dm = mfma32(dof[jv], bu, dm);
+            e1 = mfma32(aw, bu, e1);
         }
+        const int j = 16 * cb + m;  // this lane's column
+        bf16x4 dmv, dpv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * blk + 4 * g + i;
+            const float dmx = j <= r ? a.scale * dm[i] : 0.f;
+            const float dpx = j < r ? -beta_s[r] * e1[i] : 0.f;
+            if (j < r) dbp[i] -= P_s[r][j] * e1[i];
+            dmr_s[r][tok_pos(j)] = bits(dmx);
+            dpr_s[r][tok_pos(j)] = bits(dpx);
+            dmv[i] = (bf16)dmx;
+            dpv[i] = (bf16)dpx;
+        }
+        // [j][pos(r)]: rows 16 b + 4 g + i sit at positions EL g + 4 b + i
+        *reinterpret_cast<bf16x4*>(&dmc_s[j][EL * g + 4 * blk]) = dmv;
+        *reinterpret_cast<bf16x4*>(&dpc_s[j][EL * g + 4 * blk]) = dpv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float s = row_sum16(dbp[i]);
-            if (m == 0) dbeta_s[16 * blk + 4 * g + i] = s;
+            if (m == 0) dbeta_s[hf][16 * blk + 4 * g + i] = s;
         }
     }
     __syncthreads();
 
     // ---- per-channel accumulators of this lane's row
-    float dqh[KS][8], dkh[KS][8], dks[KS][8];  // dq^, dk^, dk^_KG - dk^_Kinv - dk^_Kd
+    float dqh[KH][8], dkh[KH][8], dks[KH][8];  // dq^, dk^, dk^_KG - dk^_Kinv - dk^_Kd
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
+    for (int jj = 0; jj < KH; ++jj)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { dqh[j][e] = 0.f; dkh[j][e] = 0.f; dks[j][e] = 0.f; }
+        for (int e = 0; e < 8; ++e) { dqh[jj][e] = 0.f; dkh[jj][e] = 0.f; dks[jj][e] = 0.f; }
 
     // intra-chunk products over tokens; result tile t holds channels
     // rho(t, 4 g + i) = 32 (t / 2) + 8 g + 4 (t % 2) + i of row 16 b + m
     {
-        const bf16xEL bmr = *reinterpret_cast<const bf16xEL*>(&dmr_s[16 * blk + m][EL * g]);
-        const bf16xEL bpr = *reinterpret_cast<const bf16xEL*>(&dpr_s[16 * blk + m][EL * g]);
         // (operands are split and joined as 32-bit words: element-wise moves
         // inside bf16 vectors are avoided, see kda_recur.hip)
+        const u32x4 wmr = *reinterpret_cast<const u32x4*>(&dmr_s[16 * blk + m][EL * g]);
+        const u32x4 wpr = *reinterpret_cast<const u32x4*>(&dpr_s[16 * blk + m][EL * g]);
         u32x4 wmc = *reinterpret_cast<const u32x4*>(&dmc_s[16 * blk + m][EL * g]);
         u32x4 wpc = *reinterpret_cast<const u32x4*>(&dpc_s[16 * blk + m][EL * g]);
-        // block 0's columns split by the row block r of dM[r][j] (different factors):
-        // slots 0..3 hold rows of block 0, slots 4..7 rows of block 1
+        // token slots 0..3 hold block 0, slots 4..7 block 1.  Block 1's rows r
+        // reach block 0's tokens j through 2^(G_end0 - Gl_j) = 2^G_end0 2^-Gl_j:
+        // those slots are summed apart and scaled by 2^G_end0 per channel.
+        u32x4 wmr0 = wmr, wmr1 = wmr, wpr0 = wpr, wpr1 = wpr;
+        wmr0[2] = wmr0[3] = wpr0[2] = wpr0[3] = 0u;
+        wmr1[0] = wmr1[1] = wpr1[0] = wpr1[1] = 0u;
+        // block 0's columns j: rows r of block 0 (same factor) and of block 1
+        // (cross factor) summed apart
         u32x4 wmc1 = wmc, wpc1 = wpc;
         if (blk == 0) {
             wmc[2] = wmc[3] = wpc[2] = wpc[3] = 0u;
             wmc1[0] = wmc1[1] = wpc1[0] = wpc1[1] = 0u;
         }
+        const bf16xEL bmr0 = __builtin_bit_cast(bf16xEL, wmr0), bmr1 = __builtin_bit_cast(bf16xEL, wmr1);
+        const bf16xEL bpr0 = __builtin_bit_cast(bf16xEL, wpr0), bpr1 = __builtin_bit_cast(bf16xEL, wpr1);
         const bf16xEL bmc = __builtin_bit_cast(bf16xEL, wmc), bpc = __builtin_bit_cast(bf16xEL, wpc);
         const bf16xEL bmc1 = __builtin_bit_cast(bf16xEL, wmc1),
                       bpc1 = __builtin_bit_cast(bf16xEL, wpc1);
         const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
+        for (int tt2 = 0; tt2 < 2 * KH; ++tt2) {
+            const int t = 2 * j0 + tt2;
             const int ch = tile_channel(t, m);  // this lane's A-operand row
-            floatx4 iq4 = zero, ik4 = zero, ki0 = zero, ki1 = zero;
+            floatx4 iq0 = zero, iq1 = zero, ik0 = zero, ik1 = zero, ki0 = zero, ki1 = zero;
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl) {  // hi and lo parts of the operands
-                u32x4 wkb = *reinterpret_cast<const u32x4*>(&xt_s[hl][0][ch][EL * g]);
-                if (blk == 1) {  // block 0's slots with the cross-block factor
-                    const uint2 lo = *reinterpret_cast<const uint2*>(&xt_s[hl][1][ch][EL * g]);
-                    wkb[0] = lo.x;
-                    wkb[1] = lo.y;
+                const bf16xEL akb = *reinterpret_cast<const bf16xEL*>(&xt_s[hl][0][ch][EL * g]);
+                const bf16xEL aqa = *reinterpret_cast<const bf16xEL*>(&xt_s[hl][1][ch][EL * g]);
+                const bf16xEL aka = *reinterpret_cast<const bf16xEL*>(&xt_s[hl][2][ch][EL * g]);
+                iq0 = mfma_tok(akb, bmr0, iq0);
+                ik0 = mfma_tok(akb, bpr0, ik0);
+                if (blk == 1) {
+                    iq1 = mfma_tok(akb, bmr1, iq1);
+                    ik1 = mfma_tok(akb, bpr1, ik1);
                 }
-                const bf16xEL akb = __builtin_bit_cast(bf16xEL, wkb);
-                const bf16xEL aqa = *reinterpret_cast<const bf16xEL*>(&xt_s[hl][2][ch][EL * g]);
-                const bf16xEL aka = *reinterpret_cast<const bf16xEL*>(&xt_s[hl][3][ch][EL * g]);
-                iq4 = mfma_tok(akb, bmr, iq4);
-                ik4 = mfma_tok(akb, bpr, ik4);
                 ki0 = mfma_tok(aka, bpc, mfma_tok(aqa, bmc, ki0));
                 if (blk == 0) ki1 = mfma_tok(aka, bpc1, mfma_tok(aqa, bmc1, ki1));
             }
-            const int j = t >> 1;
+            const int jj = (t >> 1) - j0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 4 * (t & 1) + i;
-                const int c = 32 * j + 8 * g + e;
-                const float Gl = G[j][e];
+                const int c = 32 * (j0 + jj) + 8 * g + e;
+                const float Gl = G[jj][e];
                 const float ga = exp2_hw(Gl);
+                // block 1: block-0 tokens carry 2^G_end0; block 0: only block-0 tokens
+                const float x0 = blk == 1 ? exp2_hw(gend_s[0][c]) : 1.f;
+                const float iq = blk == 1 ? x0 * iq0[i] + iq1[i] : iq0[i];
+                const float ik = blk == 1 ? x0 * ik0[i] + ik1[i] : ik0[i];
                 const float kinv = blk == 0 ? exp2_hw(-Gl) * ki0[i] + exp2_hw(gend_s[0][c] - Gl) * ki1[i]
                                             : exp2_hw(-Gl) * ki0[i];
-                dqh[j][e] += ga * iq4[i];
-                const float dkg = ga * ik4[i];
-                dkh[j][e] += dkg + kinv;
-                dks[j][e] += dkg - kinv;
+                dqh[jj][e] += ga * iq;
+                const float dkg = ga * ik;
+                dkh[jj][e] += dkg + kinv;
+                dks[jj][e] += dkg - kinv;
             }
         }
     }
 
     // ---- products over value columns with the stored states: dO h^T, dV h^T,
-    // U' dS'^T (transposed), and rowsum(h * dS')
+    // U' dS'^T (transposed), and rowsum(h * dS'), for this half's channels
     {
         bf16x8 dvf[VS], uf[VS];
 #pragma unroll
@@ -521,7 +562,8 @@ __global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
         const uint16_t* hbase = a.hs + ch_base * K * V;
         const uint16_t* dbase = a.dss + ch_base * K * V;
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
+        for (int tt2 = 0; tt2 < 2 * KH; ++tt2) {
+            const int t = 2 * j0 + tt2;
             const int ch = tile_channel(t, m);
             floatx4 hq = {0.f, 0.f, 0.f, 0.f}, hk = hq, hd = hq;
             float hsp = 0.f;
@@ -542,21 +584,21 @@ __global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
             hsp += __shfl_xor(hsp, 16, 64);
             hsp += __shfl_xor(hsp, 32, 64);
             if (blk == 0 && g == 0) hs_s[ch] = hsp;
-            const int j = t >> 1;
+            const int jj = (t >> 1) - j0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 4 * (t & 1) + i;
-                const int c = 32 * j + 8 * g + e;
-                const float gg = G[j][e] + (blk == 1 ? gend_s[0][c] : 0.f);  // chunk-global log2
+                const int c = 32 * (j0 + jj) + 8 * g + e;
+                const float gg = G[jj][e] + (blk == 1 ? gend_s[0][c] : 0.f);  // chunk-global log2
                 const float gam = exp2_hw(gg);
                 const float gcr = exp2_hw(gend_s[0][c] + gend_s[1][c] - gg);  // Gam_C / Gam
-                dqh[j][e] += a.scale * gam * hq[i];
+                dqh[jj][e] += a.scale * gam * hq[i];
                 const float dkg = -gam * hk[i];
                 const float dkd = gcr * hd[i];
-                dkh[j][e] += dkg + dkd;
-                dks[j][e] += dkg - dkd;
+                dkh[jj][e] += dkg + dkd;
+                dks[jj][e] += dkg - dkd;
                 // sum over this block's tokens of k^ dk^_Kd for channel c
-                const float kdr = row_sum16(kh[j][e] * dkd);
+                const float kdr = row_sum16(kh[jj][e] * dkd);
                 if (m == 0) kd_s[blk][c] = kdr;
             }
         }
@@ -564,79 +606,84 @@ __global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
     __syncthreads();
 
     // ---- dG, its reverse cumulative sum over the chunk, and the chain rule
-    float dla[KS][8];
+    float dla[KH][8];
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
+    for (int jj = 0; jj < KH; ++jj)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float dG = qh[j][e] * dqh[j][e] + kh[j][e] * dks[j][e];
+            const float dG = qh[jj][e] * dqh[jj][e] + kh[jj][e] * dks[jj][e];
             const float inc = row_scan16(dG);
             const float tot = __shfl(inc, (L & 48) | 15, 64);
-            dla[j][e] = tot - inc + dG;  // sum over this block's tokens s >= row
-            if (blk == 1 && m == 15) tot_s[32 * j + 8 * g + e] = tot;
+            dla[jj][e] = tot - inc + dG;  // sum over this block's tokens s >= row
+            if (blk == 1 && m == 15) tot_s[32 * (j0 + jj) + 8 * g + e] = tot;
         }
+    float pq = 0.f, pk = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < KH; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pq += qh[jj][e] * dqh[jj][e]; pk += kh[jj][e] * dkh[jj][e]; }
+    pq += __shfl_xor(pq, 16, 64);
+    pq += __shfl_xor(pq, 32, 64);
+    pk += __shfl_xor(pk, 16, 64);
+    pk += __shfl_xor(pk, 32, 64);
+    if (g == 0) { dot_s[hf][row][0] = pq; dot_s[hf][row][1] = pk; }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
+    for (int jj = 0; jj < KH; ++jj)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int c = 32 * j + 8 * g + e;
+            const int c = 32 * (j0 + jj) + 8 * g + e;
             const float gc = exp2_hw(gend_s[0][c] + gend_s[1][c]);
-            dla[j][e] += (blk == 0 ? tot_s[c] : 0.f) + kd_s[0][c] + kd_s[1][c] + gc * hs_s[c];
+            dla[jj][e] += (blk == 0 ? tot_s[c] : 0.f) + kd_s[0][c] + kd_s[1][c] + gc * hs_s[c];
         }
 
     // dq, dk through the norms
-    {
-        float pq = 0.f, pk = 0.f;
+    pq = dot_s[0][row][0] + dot_s[1][row][0];
+    pk = dot_s[0][row][1] + dot_s[1][row][1];
+    if (valid) {
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
+        for (int jj = 0; jj < KH; ++jj) {
+            float xq[8], xk[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { pq += qh[j][e] * dqh[j][e]; pk += kh[j][e] * dkh[j][e]; }
-        pq += __shfl_xor(pq, 16, 64);
-        pq += __shfl_xor(pq, 32, 64);
-        pk += __shfl_xor(pk, 16, 64);
-        pk += __shfl_xor(pk, 32, 64);
-        if (valid) {
-#pragma unroll
-            for (int j = 0; j < KS; ++j) {
-                float xq[8], xk[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xq[e] = (dqh[j][e] - qh[j][e] * pq) * iq;
-                    xk[e] = (dkh[j][e] - kh[j][e] * pk) * ik;
-                }
-                *reinterpret_cast<bf16x8*>(a.dq + lrow * K + 32 * j + 8 * g) = pack8(xq);
-                *reinterpret_cast<bf16x8*>(a.dk + lrow * K + 32 * j + 8 * g) = pack8(xk);
+            for (int e = 0; e < 8; ++e) {
+                xq[e] = (dqh[jj][e] - qh[jj][e] * pq) * iq;
+                xk[e] = (dkh[jj][e] - kh[jj][e] * pk) * ik;
             }
+            const int c0 = 32 * (j0 + jj) + 8 * g;
+            *reinterpret_cast<bf16x8*>(a.dq + lrow * K + c0) = pack8(xq);
+            *reinterpret_cast<bf16x8*>(a.dk + lrow * K + c0) = pack8(xk);
         }
     }
     // beta
-    if (valid && g == 0) {
-        const float db = dbeta_s[row];
+    if (valid && hf == 0 && g == 0) {
+        const float db = dbeta_s[0][row] + dbeta_s[1][row];
         a.dbeta[lrow] = bits(GDN ? db : db * b * (1.f - b));
     }
     // the gate
     if constexpr (GDN) {
         float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
+        for (int jj = 0; jj < KH; ++jj)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s += dla[j][e];
+            for (int e = 0; e < 8; ++e) s += dla[jj][e];
         s += __shfl_xor(s, 16, 64);
         s += __shfl_xor(s, 32, 64);
-        if (valid && g == 0) a.dg_gdn[lrow] = s;
+        __syncthreads();  // dot_s is reused
+        if (g == 0) dot_s[hf][row][0] = s;
+        __syncthreads();
+        if (valid && hf == 0 && g == 0) a.dg_gdn[lrow] = dot_s[0][row][0] + dot_s[1][row][0];
     } else {
         float alog = 0.f;
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            const int c0 = 32 * j + 8 * g;
+        for (int jj = 0; jj < KH; ++jj) {
+            const int c0 = 32 * (j0 + jj) + 8 * g;
             float x[8], dx[8];
             unpack8(*reinterpret_cast<const u32x4*>(a.g_kda + lrow * K + c0), x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float xx = x[e] + a.dt_bias[(int64_t)h * K + c0 + e];
                 const float pre = -rate * softplus_f(xx);
-                const float da = (valid && pre >= a.lower_bound) ? dla[j][e] : 0.f;
+                const float da = (valid && pre >= a.lower_bound) ? dla[jj][e] : 0.f;
                 dx[e] = -rate * sigmoid_f(xx) * da;
                 alog += da * pre;
                 const float colsum = row_sum16(dx[e]);
@@ -647,17 +694,17 @@ __global__ __launch_bounds__(128) void kda_bwd_chunk_kernel(BwdArgs a) {
         alog += __shfl_xor(alog, 16, 64);
         alog += __shfl_xor(alog, 32, 64);
         alog = row_sum16(alog);
-        if (L == 0) alog_s[blk] = alog;
+        if (L == 0) alog_s[wave] = alog;
         __syncthreads();
-        for (int c = threadIdx.x; c < K; c += 128)
+        for (int c = threadIdx.x; c < K; c += 256)
             a.part_dt[ch_base * K + c] = red_s[0][c] + red_s[1][c];
-        if (threadIdx.x == 0) a.part_alog[ch_base] = alog_s[0] + alog_s[1];
+        if (threadIdx.x == 0) a.part_alog[ch_base] = alog_s[0] + alog_s[1] + alog_s[2] + alog_s[3];
     }
 }
 
 template <int K, int V>
 void launch_bwd_chunk_kv(const BwdArgs& a, bool gdn, int n_slots, hipStream_t stream) {
-    const dim3 grid(n_slots, a.H), block(128);
+    const dim3 grid(n_slots, a.H), block(256);
     if (gdn) hipLaunchKernelGGL((kda_bwd_chunk_kernel<K, V, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((kda_bwd_chunk_kernel<K, V, false>), grid, block, 0, stream, a);
 }
@@ -676,29 +723,39 @@ void launch_bwd_chunk(const BwdArgs& a, int K, int V, bool gdn, int n_slots, hip
 // ------------------------------------------------------------ gate reductions
 // dL/d(dt_bias)[h][c] and dL/dA_log[h]: sums over every chunk slot of the
 // per-chunk sums, in a fixed order (no atomics: the result is reproducible).
+// Workgroup (h, 64-channel block): thread (c, q) sums slots q, q + 4, ... of
+// channel c; the four partial sums are added in LDS.  The workgroup with
+// channel block 0 also sums dA_log's slots.
 __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(const float* part_dt,
                                                              const float* part_alog,
                                                              int32_t n_slots, int32_t H,
                                                              int32_t K, float* ddt_bias,
                                                              float* dA_log) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < H * K) {
-        const int h = i / K, c = i % K;
-        float s = 0.f;
-        for (int sl = 0; sl < n_slots; ++sl) s += part_dt[((int64_t)sl * H + h) * K + c];
-        ddt_bias[i] = s;
-    } else if (i < H * K + H) {
-        const int h = i - H * K;
-        float s = 0.f;
-        for (int sl = 0; sl < n_slots; ++sl) s += part_alog[(int64_t)sl * H + h];
-        dA_log[h] = s;
+    __shared__ float acc[4][64];
+    __shared__ float al[256];
+    const int h = blockIdx.x, c = blockIdx.y * 64 + (threadIdx.x & 63), q = threadIdx.x >> 6;
+    float s = 0.f;
+    if (c < K)
+        for (int sl = q; sl < n_slots; sl += 4) s += part_dt[((int64_t)sl * H + h) * K + c];
+    acc[q][threadIdx.x & 63] = s;
+    float t = 0.f;
+    if (blockIdx.y == 0)
+        for (int sl = threadIdx.x; sl < n_slots; sl += 256) t += part_alog[(int64_t)sl * H + h];
+    al[threadIdx.x] = t;
+    __syncthreads();
+    if (q == 0 && c < K)
+        ddt_bias[(int64_t)h * K + c] = (acc[0][threadIdx.x] + acc[1][threadIdx.x]) +
+                                       (acc[2][threadIdx.x] + acc[3][threadIdx.x]);
+    for (int d = 128; d > 0; d >>= 1) {
+        if (threadIdx.x < d) al[threadIdx.x] += al[threadIdx.x + d];
+        __syncthreads();
     }
+    if (blockIdx.y == 0 && threadIdx.x == 0) dA_log[h] = al[0];
 }
 
 void launch_bwd_reduce(const float* part_dt, const float* part_alog, int32_t n_slots,
                        int32_t H, int32_t K, float* ddt_bias, float* dA_log, hipStream_t stream) {
-    const int total = H * K + H;
-    hipLaunchKernelGGL(kda_bwd_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, stream,
+    hipLaunchKernelGGL(kda_bwd_reduce_kernel, dim3(H, (K + 63) / 64), dim3(256), 0, stream,
                        part_dt, part_alog, n_slots, H, K, ddt_bias, dA_log);
 }
 

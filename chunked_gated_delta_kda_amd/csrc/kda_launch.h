@@ -55,6 +55,8 @@ struct RecurArgs {
                                // (reverse pass: the state gradient leaving each chunk)
     uint16_t* chunk_u;         // [slots, H, V, C] bf16, tokens in k-slot order: the
                                // chunk's V - KG S (reverse pass: dL/dU')
+    uint16_t* chunk_y;         // reverse pass: [slots, H, V, C] bf16, dL/dV in the same
+                               // layout (or null)
 };
 
 // kda_recur variants: the forward pass; the forward pass that stores every
@@ -111,6 +113,7 @@ struct BwdArgs {
     const uint16_t* zt;        // [slots, H, V, C] bf16: V - KG S of each chunk
     const uint16_t* dss;       // [slots, H, K, V] bf16: gradient of the state leaving it
     const uint16_t* dut;       // [slots, H, V, C] bf16: dL/dU'
+    const uint16_t* yt;        // [slots, H, V, C] bf16: dL/dV (token-ordered copy of dv)
     uint16_t* dq;              // [tokens, H, K] bf16
     uint16_t* dk;              // [tokens, H, K] bf16
     uint16_t* dg_kda;          // KDA: [tokens, H, K] bf16

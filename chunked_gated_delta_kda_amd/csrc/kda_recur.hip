@@ -280,7 +280,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
     // Backward-pass stores.  store_state: the bf16 state copy (k-step j of
     // column tile ct holds channels 32 j + 8 lg + e of column lr) into
     // chunk_state [slots, H, K, V].  store_tok: a [C, columns] result in D
-    // layout (block bb, rows 4 lg + i) into chunk_u [slots, H, V, C] with the
+    // layout (block bb, rows 4 lg + i) into a [slots, H, V, C] buffer with the
     // tokens in k-slot order, 8 bytes per block.
     // (single bf16 elements are taken from the packed 32-bit words with
     // integer shifts: storing vector elements of a bf16 vector directly was
@@ -298,8 +298,8 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
                         (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
             }
     };
-    auto store_tok = [&](const floatx4 (&X)[CT][NB], int64_t slot) {
-        uint16_t* up = a.chunk_u + ((slot * a.H + h) * a.V + cb + cw + lr) * C;
+    auto store_tok = [&](uint16_t* base, const floatx4 (&X)[CT][NB], int64_t slot) {
+        uint16_t* up = base + ((slot * a.H + h) * a.V + cb + cw + lr) * C;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
                 for (int ct = 0; ct < CT; ++ct)
                     Y[ct][bb] = mfma32(f.nkg[bb][j], sb[ct][j], Y[ct][bb]);
         read_nkg_v(f, next);
-        if constexpr (STORE) store_tok(Y, s0 + c);
+        if constexpr (STORE) store_tok(a.chunk_u, Y, s0 + c);
         // O_ob^T = S^T QG_ob^T for each 16-token output block ob
         floatx4 OT[CT][NB];
         if constexpr (!STORE) {
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dU[ct][bb][i] += a.scale * aux[ct][bb][i];
-        if (a.chunk_u) store_tok(dU, s0 + cc);
+        if (a.chunk_u) store_tok(a.chunk_u, dU, s0 + cc);
         bf16xEL duc[CT], yc[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
@@ -530,6 +530,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) dV[ct][bb] = mfma_tok(f.tbt[bb], duc[ct], zero);
         read_blocks(f.tbt, next, BR::TBT);
+        if (a.chunk_y) store_tok(a.chunk_y, dV, s0 + cc);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
