@@ -174,21 +174,23 @@ __device__ __forceinline__ void put_split(A& arr, int part, int c, int p, float 
 
 }  // namespace
 
-// One workgroup per (chunk slot, head) and four waves: wave w owns the
-// 16-token block b = w % 2 and the channel half hf = w / 2.  Lane
-// l = m + 16 g of a wave owns token 16 b + m and the channels 32 j + 8 g + e
-// of its half's k-steps j (the row layout of kda_prep, split in two).
+// One workgroup per (chunk slot, head) and 2 K / 32 waves: wave w owns the
+// 16-token block b = w % 2 and the channel group q = w / 2 of 32 channels.
+// Lane l = m + 16 g of a wave owns token 16 b + m and the channels
+// 32 q + 8 g + e, e < 8 (the row layout of kda_prep, one k-step per wave).
 // Products that contract over channels read their operands from registers
-// (partial sums over the two halves meet in LDS); products that contract over
+// (partial sums over the channel groups meet in LDS); products that contract over
 // tokens read token-ordered copies from LDS; products that contract over
 // value columns read the stored states and [C, V] rows.  Every result that is
 // a function of (token, channel) is produced transposed (channels as MFMA rows
 // in the tile_channel order), which lands it in the owner lane's registers.
 template <int K, int V, bool GDN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void kda_bwd_chunk_kernel(
-    BwdArgs a) {
+__global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
     static_assert(NB == 2, "the gradient kernel assumes 32-token chunks");
-    constexpr int KS = K / 32, KH = KS / 2, KT = K / 16, VS = V / 32, VT = V / 16;
+    constexpr int KS = K / 32, KH = 1, KT = K / 16, VS = V / 32, VT = V / 16;
+    constexpr int NQ = KS;             // channel groups (waves per token block)
+    constexpr int NT = 128 * NQ;       // threads
+    static_assert(VT % NQ == 0, "value tiles are dealt evenly to the channel groups");
     constexpr int UP = V + 8;  // padded row of the U' / W1 copies (bf16)
     using R = Rec<K>;
     // LDS, 80 KB at K = V = 128 so that two workgroups share a CU: regions
@@ -202,10 +204,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                                               //   then the late sums below
     constexpr int OFF_DM = OFF_W + C * UP * 2;                // bf16 4 x [C][C], dM .. intra;
                                                               //   before: kbc0, norms
-    constexpr int OFF_DB = OFF_DM + 4 * C * C * 2;            // float [2][C], dM .. end
-    constexpr int LDS_BYTES = OFF_DB + 2 * C * 4;
-    static_assert(KS * 64 * 16 + C * C * 2 + 2 * C * 2 * 4 <= 4 * C * C * 2, "early region");
-    static_assert(2 * K * 4 + K * 4 * 2 + 2 * C * 2 * 4 + 4 * 4 <= C * UP * 2 + 2 * K * 4, "late region");
+    constexpr int OFF_DB = OFF_DM + 4 * C * C * 2;            // float [NQ][C], dM .. end
+    constexpr int LDS_BYTES = OFF_DB + NQ * C * 4;
+    static_assert(KS * 64 * 16 + NQ * C * 2 * 4 <= 4 * C * C * 2, "early region");
+    static_assert(6 * K * 4 + NQ * C * 2 * 4 + 2 * NQ * 4 <= C * UP * 2, "late region");
     __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
     auto& gend_s = *reinterpret_cast<float(*)[2][K]>(smem + OFF_GEND);
     auto& beta_s = *reinterpret_cast<float(*)[C]>(smem + OFF_BETA);
@@ -225,22 +227,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     auto& dpc_s = *reinterpret_cast<uint16_t(*)[C][C]>(smem + OFF_DM + 3 * C * C * 2);
     // early tenants of the dM region
     auto& kbc0_s = *reinterpret_cast<bf16x8(*)[KS * 64]>(smem + OFF_DM);  // block 0: k^ 2^(G_end0 - G)
-    auto& nrm_s = *reinterpret_cast<float(*)[2][C][2]>(smem + OFF_DM + KS * 64 * 16 + C * C * 2);
-    auto& dbeta_s = *reinterpret_cast<float(*)[2][C]>(smem + OFF_DB);  // per half
+    auto& nrm_s = *reinterpret_cast<float(*)[NQ][C][2]>(smem + OFF_DM + KS * 64 * 16);
+    auto& dbeta_s = *reinterpret_cast<float(*)[NQ][C]>(smem + OFF_DB);  // per channel group
     // late tenants of the W1 region
     auto& kd_s = *reinterpret_cast<float(*)[2][K]>(smem + OFF_W);  // per block: sum of k^ dk^_Kd
     auto& hs_s = *reinterpret_cast<float(*)[K]>(smem + OFF_W + 2 * K * 4);  // rowsum(h * dS')
     auto& tot_s = *reinterpret_cast<float(*)[K]>(smem + OFF_W + 3 * K * 4);  // block 1's dG totals
-    auto& dot_s = *reinterpret_cast<float(*)[2][C][2]>(smem + OFF_W + 4 * K * 4);
-    auto& red_s = *reinterpret_cast<float(*)[2][K]>(smem + OFF_W + 4 * K * 4 + 2 * C * 2 * 4);
-    auto& alog_s = *reinterpret_cast<float(*)[4]>(smem + OFF_W + 6 * K * 4 + 2 * C * 2 * 4);
+    auto& dot_s = *reinterpret_cast<float(*)[NQ][C][2]>(smem + OFF_W + 4 * K * 4);
+    auto& red_s = *reinterpret_cast<float(*)[2][K]>(smem + OFF_W + 4 * K * 4 + NQ * C * 2 * 4);
+    auto& alog_s = *reinterpret_cast<float(*)[2 * NQ]>(smem + OFF_W + 6 * K * 4 + NQ * C * 2 * 4);
 
     const int slot = blockIdx.x;
     const int h = blockIdx.y;
     const int wave = threadIdx.x >> 6;
-    const int blk = wave & 1, hf = wave >> 1;
+    const int blk = wave & 1, hf = wave >> 1;  // token block, channel group
     const int L = threadIdx.x & 63, m = L & 15, g = L >> 4;
-    const int j0 = hf * KH;  // this wave's first k-step (channels 32 j0 ..)
+    const int j0 = hf;  // this wave's k-step (channels 32 j0 ..)
 
     int n;
     if (!a.packed) {
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             // its share of the gate-parameter sums is zero
             if constexpr (!GDN) {
                 const int64_t chb = (int64_t)slot * a.H + h;
-                for (int c = threadIdx.x; c < K; c += 256) a.part_dt[chb * K + c] = 0.f;
+                for (int c = threadIdx.x; c < K; c += NT) a.part_dt[chb * K + c] = 0.f;
                 if (threadIdx.x == 0) a.part_alog[chb] = 0.f;
             }
             return;
@@ -328,8 +330,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
     if (hf == 0 && g == 0) beta_s[row] = b;
     __syncthreads();
-    const float iq = rsq_hw(nrm_s[0][row][0] + nrm_s[1][row][0] + NORM_EPS);
-    const float ik = rsq_hw(nrm_s[0][row][1] + nrm_s[1][row][1] + NORM_EPS);
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) { sq += nrm_s[qq][row][0]; sk += nrm_s[qq][row][1]; }
+    const float iq = rsq_hw(sq + NORM_EPS), ik = rsq_hw(sk + NORM_EPS);
 #pragma unroll
     for (int jj = 0; jj < KH; ++jj)
 #pragma unroll
@@ -366,8 +370,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
             for (int jj = 0; jj < KH; ++jj) Pc = mfma32(ka_f[jj], kbc0_s[(j0 + jj) * 64 + L], Pc);
         }
-        // the two channel halves add up: half 1 writes, half 0 adds
-        if (hf == 1) {
+        // the channel groups add up in a fixed order: the last writes, the
+        // others add (one group per step, so the sum is reproducible)
+        if (hf == NQ - 1) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * blk + 4 * g + i;
@@ -375,13 +380,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 P_s[r][16 * (1 - blk) + m] = blk == 1 ? Pc[i] : 0.f;
             }
         }
-        __syncthreads();
-        if (hf == 0) {
+        for (int qq = NQ - 2; qq >= 0; --qq) {
+            __syncthreads();
+            if (hf == qq) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * blk + 4 * g + i;
-                if (m < 4 * g + i) P_s[r][16 * blk + m] += Pacc[i];
-                if (blk == 1) P_s[r][m] += Pc[i];
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * blk + 4 * g + i;
+                    if (m < 4 * g + i) P_s[r][16 * blk + m] += Pacc[i];
+                    if (blk == 1) P_s[r][m] += Pc[i];
+                }
             }
         }
     }
@@ -402,8 +409,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const bf16xEL apt = pack8(ptf);
         const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int vv = 0; vv < VT / 2; ++vv) {
-            const int col = 16 * (hf * (VT / 2) + vv) + m;
+        for (int vv = 0; vv < VT / NQ; ++vv) {
+            const int col = 16 * (hf * (VT / NQ) + vv) + m;
             const int64_t cbase = (ch_base * V + col) * C;
             const u32x4 wz = *reinterpret_cast<const u32x4*>(a.zt + cbase + EL * g);
             const bf16xEL bz = __builtin_bit_cast(bf16xEL, wz);
@@ -428,7 +435,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __syncthreads();
 
     // ---- dM = scale tril(dO U'^T), E1 = W1 U'^T, dP for this block's rows and
-    // the 16 columns cb = hf; db's share
+    // the 16 columns cb = q (channel groups 0 and 1); db's share
     bf16x8 dof[VS];
 #pragma unroll
     for (int jv = 0; jv < VS; ++jv) {
@@ -441,6 +448,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         float dbp[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) dbp[i] = zw[i];
+        if (cb < 2) {
         floatx4 dm = {0.f, 0.f, 0.f, 0.f}, e1 = dm;
 #pragma unroll
         for (int jv = 0; jv < VS; ++jv) {
@@ -465,6 +473,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // [j][pos(r)]: rows 16 b + 4 g + i sit at positions EL g + 4 b + i
         *reinterpret_cast<bf16x4*>(&dmc_s[j][EL * g + 4 * blk]) = dmv;
         *reinterpret_cast<bf16x4*>(&dpc_s[j][EL * g + 4 * blk]) = dpv;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float s = row_sum16(dbp[i]);
@@ -638,8 +647,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
 
     // dq, dk through the norms
-    pq = dot_s[0][row][0] + dot_s[1][row][0];
-    pk = dot_s[0][row][1] + dot_s[1][row][1];
+    pq = 0.f;
+    pk = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) { pq += dot_s[qq][row][0]; pk += dot_s[qq][row][1]; }
     if (valid) {
 #pragma unroll
         for (int jj = 0; jj < KH; ++jj) {
@@ -656,7 +667,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     // beta
     if (valid && hf == 0 && g == 0) {
-        const float db = dbeta_s[0][row] + dbeta_s[1][row];
+        float db = 0.f;
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) db += dbeta_s[qq][row];
         a.dbeta[lrow] = bits(GDN ? db : db * b * (1.f - b));
     }
     // the gate
@@ -671,7 +684,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         __syncthreads();  // dot_s is reused
         if (g == 0) dot_s[hf][row][0] = s;
         __syncthreads();
-        if (valid && hf == 0 && g == 0) a.dg_gdn[lrow] = dot_s[0][row][0] + dot_s[1][row][0];
+        if (valid && hf == 0 && g == 0) {
+            float d = 0.f;
+#pragma unroll
+            for (int qq = 0; qq < NQ; ++qq) d += dot_s[qq][row][0];
+            a.dg_gdn[lrow] = d;
+        }
     } else {
         float alog = 0.f;
 #pragma unroll
@@ -696,15 +714,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         alog = row_sum16(alog);
         if (L == 0) alog_s[wave] = alog;
         __syncthreads();
-        for (int c = threadIdx.x; c < K; c += 256)
+        for (int c = threadIdx.x; c < K; c += NT)
             a.part_dt[ch_base * K + c] = red_s[0][c] + red_s[1][c];
-        if (threadIdx.x == 0) a.part_alog[ch_base] = alog_s[0] + alog_s[1] + alog_s[2] + alog_s[3];
+        if (threadIdx.x == 0) {
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < 2 * NQ; ++w) t += alog_s[w];
+            a.part_alog[ch_base] = t;
+        }
     }
 }
 
 template <int K, int V>
 void launch_bwd_chunk_kv(const BwdArgs& a, bool gdn, int n_slots, hipStream_t stream) {
-    const dim3 grid(n_slots, a.H), block(256);
+    const dim3 grid(n_slots, a.H), block(4 * K);
     if (gdn) hipLaunchKernelGGL((kda_bwd_chunk_kernel<K, V, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((kda_bwd_chunk_kernel<K, V, false>), grid, block, 0, stream, a);
 }
