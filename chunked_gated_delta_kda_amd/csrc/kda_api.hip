@@ -310,23 +310,23 @@ struct BwdIO {
     float *dA_log, *ddt_bias, *dh0;
 };
 
-// The backward pass: kda_prep (forward records), the reverse-pass records,
-// the forward sweep that keeps every chunk's entering state, the reverse
-// sweep (state gradients, dv, dh0), the chunk gradient kernel and the
+// The backward pass: kda_prep (forward and reverse-pass records), the
+// forward sweep that keeps every chunk's entering state, the reverse sweep
+// (state gradients, dv, dh0), the chunk gradient kernel and the
 // gate-parameter sums.
 int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& io,
             hipStream_t stream) {
     if (c.ws_bytes < bwd_workspace_bytes(c.B, c.T, c.H, c.K, c.V, N, c.varlen))
         return KDA_ERR_WORKSPACE;
-    int st = run_prep(c, N, p, gdn, stream);
-    if (st != KDA_OK) return st;
     const WsLayout w = layout(c, N);
     const SplitPlan none{0, 0};
     unsigned char* extra = static_cast<unsigned char*>(c.ws) +
                            align_up(workspace_bytes_for(c.B, c.T, c.H, c.K, c.V, N, c.varlen, none));
     const BwdLayout bl = bwd_layout(extra, w.slots, c.H, c.K, c.V);
+    p.brec = bl.brec;  // kda_prep also writes the reverse-pass records
+    int st = run_prep(c, N, p, gdn, stream);
+    if (st != KDA_OK) return st;
     (void)hipGetLastError();
-    kda::launch_bwd_rec(w.rec, bl.brec, c.K, w.slots * c.H, stream);
     kda::RecurArgs r{};
     r.v = c.v;
     r.rec = w.rec;

@@ -1,6 +1,6 @@
-// kda_bwd.hip -- the backward pass (gfx950): the reverse-pass record, the
-// chunk-parallel gradient kernel and the reduction of the gate-parameter
-// gradients.
+// kda_bwd.hip -- the backward pass (gfx950): the chunk-parallel gradient
+// kernel and the reduction of the gate-parameter gradients (the reverse-pass
+// record comes from kda_prep, the two sweeps from kda_recur).
 //
 // The pages show the backward only as autograd over the forward call (cuLA
 // README mirror, section "Usage": o.backward(do) with q, k, v requiring
@@ -32,99 +32,6 @@
 #include "kda_launch.h"
 
 namespace kda {
-
-// ------------------------------------------------------------ reverse record
-// BRec from Rec: the same matrices, transposed.  One workgroup per record; the
-// forward record is staged in LDS and every 16-byte slice of the backward one
-// gathers its 8 elements there.
-namespace {
-
-// Element (token s, channel c) of a [C x K] matrix in the Rec::NKG / QG layout.
-template <int K>
-__device__ __forceinline__ int rowop_index(int s, int c) {
-    constexpr int KS = K / 32;
-    const int bb = s >> 4, m = s & 15, j = c >> 5, g = (c & 31) >> 3, e = c & 7;
-    return ((bb * KS + j) * 64 + m + 16 * g) * 8 + e;
-}
-// Element (token s, channel c) of a [K x C] transposed matrix in the Rec::KDT layout.
-__device__ __forceinline__ int tileop_index(int s, int c) {
-    const int t = 2 * (c >> 5) + ((c & 7) >> 2), mm = 4 * ((c & 31) >> 3) + (c & 3);
-    const int p = tok_pos(s), g = p / EL, e = p % EL;
-    return ((t * 4 + g) * 16 + mm) * EL + e;
-}
-// Element (row r, token s) of a [C x C] matrix in the Rec::AQK / TB layout.
-__device__ __forceinline__ int tokop_index(int r, int s) {
-    const int p = tok_pos(s), g = p / EL, e = p % EL;
-    return (((r >> 4) * 4 + g) * 16 + (r & 15)) * EL + e;
-}
-
-}  // namespace
-
-template <int K>
-__global__ __launch_bounds__(256) void kda_bwd_rec_kernel(const unsigned char* rec,
-                                                          unsigned char* brec) {
-    using R = Rec<K>;
-    using BR = BRec<K>;
-    __shared__ __attribute__((aligned(16))) unsigned char src[R::BYTES];
-    const int64_t r0 = (int64_t)blockIdx.x * R::BYTES;
-    for (int p = threadIdx.x; p < R::BYTES / 16; p += 256)
-        reinterpret_cast<u32x4*>(src)[p] = reinterpret_cast<const u32x4*>(rec + r0)[p];
-    __syncthreads();
-    const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
-    constexpr int NBF = BR::GAMC / 2;  // bf16 elements before Gam_C
-    for (int p = threadIdx.x; p < BR::BYTES / 16; p += 256) {
-        u32x4 out;
-        if (p * 8 >= NBF) {  // Gam_C: same layout
-            out = reinterpret_cast<const u32x4*>(src)[p];
-        } else {
-            uint16_t v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int o = p * 8 + u;  // bf16 index in BRec
-                int si;
-                if (o < BR::QGT / 2) {
-                    // KD[s][c] (NKG layout) = Kd, read from KDT
-                    const int q = o;
-                    const int e = q & 7, lane = (q >> 3) & 63, bj = q >> 9;
-                    const int s = 16 * (bj / (K / 32)) + (lane & 15);
-                    const int c = 32 * (bj % (K / 32)) + 8 * (lane >> 4) + e;
-                    si = R::KDT / 2 + tileop_index(s, c);
-                } else if (o < BR::AQKT / 2) {
-                    // QGT / NKGT [t][g][m][e] = X[tok(g,e)][rho(t,m)], X from QG / NKG
-                    const bool qg = o < BR::NKGT / 2;
-                    const int q = o - (qg ? BR::QGT : BR::NKGT) / 2;
-                    const int e = q % EL, mm = (q / EL) & 15, g = (q / (EL * 16)) & 3,
-                              t = q / (EL * 64);
-                    const int s = 16 * (e >> 2) + 4 * g + (e & 3);
-                    si = (qg ? R::QG : R::NKG) / 2 + rowop_index<K>(s, tile_channel(t, mm));
-                } else {
-                    // AQKT / TBT [a][g][n][e] = X[tok(g,e)][16a+n], X from AQK / TB
-                    const bool aq = o < BR::TBT / 2;
-                    const int q = o - (aq ? BR::AQKT : BR::TBT) / 2;
-                    const int e = q % EL, n = (q / EL) & 15, g = (q / (EL * 16)) & 3,
-                              blk = q / (EL * 64);
-                    const int s = 16 * (e >> 2) + 4 * g + (e & 3);
-                    si = (aq ? R::AQK : R::TB) / 2 + tokop_index(s, 16 * blk + n);
-                }
-                v[u] = s16[si];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) out[u] = (uint32_t)v[2 * u] | ((uint32_t)v[2 * u + 1] << 16);
-        }
-        reinterpret_cast<u32x4*>(brec + r0)[p] = out;
-    }
-}
-
-void launch_bwd_rec(const unsigned char* rec, unsigned char* brec, int K, int64_t n_recs,
-                    hipStream_t stream) {
-    if (n_recs <= 0) return;
-    if (K == 128)
-        hipLaunchKernelGGL(kda_bwd_rec_kernel<128>, dim3((unsigned)n_recs), dim3(256), 0, stream,
-                           rec, brec);
-    else
-        hipLaunchKernelGGL(kda_bwd_rec_kernel<64>, dim3((unsigned)n_recs), dim3(256), 0, stream,
-                           rec, brec);
-}
 
 // ------------------------------------------------------------ gradient kernel
 namespace {

@@ -25,6 +25,7 @@ struct PrepArgs {
     const int32_t* chunk_off;  // packed: [n_seqs + 1] first chunk slot of each sequence
     unsigned char* rec;        // [slots, H, record bytes]
     float* bound;              // [slots, H]: sum over the chunk of max_c log2 a (<= 0)
+    unsigned char* brec;       // [slots, H, BRec bytes] or null: the reverse-pass records
 };
 
 struct RecurArgs {
@@ -129,8 +130,6 @@ struct BwdArgs {
     const int32_t* chunk_off;
 };
 
-void launch_bwd_rec(const unsigned char* rec, unsigned char* brec, int K, int64_t n_recs,
-                    hipStream_t stream);
 void launch_bwd_chunk(const BwdArgs& a, int K, int V, bool gdn, int n_slots, hipStream_t stream);
 void launch_bwd_reduce(const float* part_dt, const float* part_alog, int32_t n_slots,
                        int32_t H, int32_t K, float* ddt_bias, float* dA_log, hipStream_t stream);

@@ -123,8 +123,11 @@ __device__ __forceinline__ bf16xEL pack_tok(floatx4 lo, floatx4 hi) {
 
 }  // namespace
 
-template <int K, bool GDN>
+// BREC: also write the reverse-pass record (BRec, kda_common.h) for the
+// backward pass: the same matrices, transposed through LDS.
+template <int K, bool GDN, bool BREC>
 __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
+    static_assert(!BREC || NB == 2, "the reverse-pass record is written for 32-token chunks");
     constexpr int KS = K / 32;  // 16-byte channel slices per lane
     using R = Rec<K>;
     __shared__ __attribute__((aligned(16))) uint16_t kdt_s[C * K];   // KdT transpose
@@ -134,6 +137,11 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     __shared__ float beta0_s[16];
     __shared__ float dmax_s[NB];  // per block: sum over rows of the row's largest log2 decay
     __shared__ __attribute__((aligned(16))) float eg_s[NB][K];  // KDA: 2^(block total) per channel
+    // reverse-pass record only: QG^T, nKG^T (layout of KdT), Aqk and Tb rows
+    __shared__ __attribute__((aligned(16))) uint16_t qgt_s[BREC ? C * K : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t nkgt_s[BREC ? C * K : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t aqk_s[BREC ? C * C : 1];  // [r][s]
+    __shared__ __attribute__((aligned(16))) uint16_t tb_s[BREC ? C * C : 1];   // [r][s]
 
     const int slot = blockIdx.x;
     const int h = blockIdx.y;
@@ -335,9 +343,16 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         for (int e = 0; e < 8; ++e) {
             const int t = 2 * j + (e >> 2), mm = 4 * g + (e & 3);
             const int ee = 4 * blk + (m & 3);
-            kdt_s[((t * 4 + (m >> 2)) * 16 + mm) * EL + ee] =
-                __builtin_bit_cast(uint16_t, (bf16)kd[e]);
+            const int ti = ((t * 4 + (m >> 2)) * 16 + mm) * EL + ee;
+            kdt_s[ti] = __builtin_bit_cast(uint16_t, (bf16)kd[e]);
+            if constexpr (BREC) {
+                qgt_s[ti] = __builtin_bit_cast(uint16_t, (bf16)qg[e]);
+                nkgt_s[ti] = __builtin_bit_cast(uint16_t, (bf16)(-kg[e]));
+            }
         }
+        if constexpr (BREC)  // Kd rows, in the layout of nKG
+            *reinterpret_cast<bf16x8*>(a.brec + ((int64_t)slot * a.H + h) * BRec<K>::BYTES +
+                                       BRec<K>::KD + ((blk * KS + j) * 64 + L) * 16) = pack8(kd);
         const bf16x8 kglf = pack8(kgl), qglf = pack8(qgl);
         if constexpr (GDN) {
             // in-block products of k^ and q^; the decay is applied per element
@@ -376,6 +391,12 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
             const floatx4 hi = {gcv[4], gcv[5], gcv[6], gcv[7]};
             *reinterpret_cast<floatx4*>(gp + 32 * j + 4 * g) = lo;
             *reinterpret_cast<floatx4*>(gp + 32 * j + 16 + 4 * g) = hi;
+            if constexpr (BREC) {
+                float* bp = reinterpret_cast<float*>(a.brec + ((int64_t)slot * a.H + h) * BRec<K>::BYTES +
+                                                     BRec<K>::GAMC);
+                *reinterpret_cast<floatx4*>(bp + 32 * j + 4 * g) = lo;
+                *reinterpret_cast<floatx4*>(bp + 32 * j + 16 + 4 * g) = hi;
+            }
         }
     }
     if (blk == 0 && g == 0) beta0_s[m] = b;
@@ -387,6 +408,13 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         const int off = (p * 64 * NB + threadIdx.x) * 16;
         *reinterpret_cast<u32x4*>(rec + R::KDT + off) =
             *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(kdt_s) + off);
+        if constexpr (BREC) {
+            unsigned char* br = a.brec + ((int64_t)slot * a.H + h) * BRec<K>::BYTES;
+            *reinterpret_cast<u32x4*>(br + BRec<K>::QGT + off) =
+                *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(qgt_s) + off);
+            *reinterpret_cast<u32x4*>(br + BRec<K>::NKGT + off) =
+                *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(nkgt_s) + off);
+        }
     }
     if constexpr (NB == 2) {
         if (blk == 1) {
@@ -466,6 +494,30 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     }
     *reinterpret_cast<bf16xEL*>(rec + R::AQK + (blk * 64 + L) * (2 * EL)) = pack_tok(aq_lo, aq_hi);
     *reinterpret_cast<bf16xEL*>(rec + R::TB + (blk * 64 + L) * (2 * EL)) = pack_tok(tb_lo, tb_hi);
+    if constexpr (BREC) {
+        // rows 16 blk + m of Aqk and Tb through LDS, then their columns:
+        // AQKT[a][g][n][e] = Aqk[tok(g,e)][16a+n], TBT likewise
+        const u32x4 wa = __builtin_bit_cast(u32x4, pack_tok(aq_lo, aq_hi));
+        const u32x4 wt = __builtin_bit_cast(u32x4, pack_tok(tb_lo, tb_hi));
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+            const int s = 16 * (e >> 2) + 4 * g + (e & 3);
+            aqk_s[(16 * blk + m) * C + s] = (uint16_t)(wa[e >> 1] >> (16 * (e & 1)));
+            tb_s[(16 * blk + m) * C + s] = (uint16_t)(wt[e >> 1] >> (16 * (e & 1)));
+        }
+        __syncthreads();
+        u32x4 oa, ot;
+#pragma unroll
+        for (int u = 0; u < EL / 2; ++u) {
+            const int e0 = 2 * u, e1 = 2 * u + 1;
+            const int r0 = 16 * (e0 >> 2) + 4 * g + (e0 & 3), r1 = 16 * (e1 >> 2) + 4 * g + (e1 & 3);
+            oa[u] = (uint32_t)aqk_s[r0 * C + 16 * blk + m] | ((uint32_t)aqk_s[r1 * C + 16 * blk + m] << 16);
+            ot[u] = (uint32_t)tb_s[r0 * C + 16 * blk + m] | ((uint32_t)tb_s[r1 * C + 16 * blk + m] << 16);
+        }
+        unsigned char* br = a.brec + ((int64_t)slot * a.H + h) * BRec<K>::BYTES;
+        *reinterpret_cast<u32x4*>(br + BRec<K>::AQKT + (blk * 64 + L) * (2 * EL)) = oa;
+        *reinterpret_cast<u32x4*>(br + BRec<K>::TBT + (blk * 64 + L) * (2 * EL)) = ot;
+    }
 }
 
 // Sequence table: seq_start[0..N] (flattened token offsets) and
@@ -528,8 +580,12 @@ void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t tota
 
 template <int K, bool GDN>
 void launch_prep_t(const PrepArgs& a, int n_slots, hipStream_t stream) {
-    hipLaunchKernelGGL((kda_prep_kernel<K, GDN>), dim3(n_slots, a.H), dim3(64 * NB), 0, stream,
-                       a);
+    if (a.brec)
+        hipLaunchKernelGGL((kda_prep_kernel<K, GDN, true>), dim3(n_slots, a.H), dim3(64 * NB), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((kda_prep_kernel<K, GDN, false>), dim3(n_slots, a.H), dim3(64 * NB), 0,
+                           stream, a);
 }
 
 void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream) {
