@@ -319,6 +319,7 @@ int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& 
     if (c.ws_bytes < bwd_workspace_bytes(c.B, c.T, c.H, c.K, c.V, N, c.varlen))
         return KDA_ERR_WORKSPACE;
     const WsLayout w = layout(c, N);
+    if ((int64_t)N * c.H * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;  // recurrence grids
     const SplitPlan none{0, 0};
     unsigned char* extra = static_cast<unsigned char*>(c.ws) +
                            align_up(workspace_bytes_for(c.B, c.T, c.H, c.K, c.V, N, c.varlen, none));

@@ -91,6 +91,13 @@ __device__ __forceinline__ void put_split(A& arr, int part, int c, int p, float 
 // value columns read the stored states and [C, V] rows.  Every result that is
 // a function of (token, channel) is produced transposed (channels as MFMA rows
 // in the tile_channel order), which lands it in the owner lane's registers.
+// Swizzle key of state row (channel) ch, over PR pieces per row: bits 0-1 and
+// 3-4 of the channel, which take 16 distinct values over a state tile's rows.
+template <int PR>
+__device__ __forceinline__ int st_key(int ch) {
+    return ((((ch >> 3) & 3) << 2) | (ch & 3)) & (PR - 1);
+}
+
 template <int K, int V, bool GDN>
 __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
     static_assert(NB == 2, "the gradient kernel assumes 32-token chunks");
@@ -100,8 +107,9 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
     static_assert(VT % NQ == 0, "value tiles are dealt evenly to the channel groups");
     constexpr int UP = V + 8;  // padded row of the U' / W1 copies (bf16)
     using R = Rec<K>;
-    // LDS, 80 KB at K = V = 128 so that two workgroups share a CU: regions
-    // whose lifetimes do not overlap share memory (the phase of each is noted).
+    // LDS, 143 KB at K = V = 128 (one workgroup per CU, as the registers
+    // allow): regions whose lifetimes do not overlap share memory (the phase
+    // of each is noted); the state copies have a region of their own.
     constexpr int OFF_GEND = 0;                               // float [2][K], all phases
     constexpr int OFF_BETA = OFF_GEND + 2 * K * 4;            // float [C], until dM
     constexpr int OFF_P = OFF_BETA + C * 4;                   // float [C][C+1], P .. dM
@@ -112,7 +120,17 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
     constexpr int OFF_DM = OFF_W + C * UP * 2;                // bf16 4 x [C][C], dM .. intra;
                                                               //   before: kbc0, norms
     constexpr int OFF_DB = OFF_DM + 4 * C * C * 2;            // float [NQ][C], dM .. end
-    constexpr int LDS_BYTES = OFF_DB + NQ * C * 4;
+    // the chunk's entering state h and dL/d(leaving state), bf16 [K][V] each,
+    // copied in by the DMA engine while the earlier phases run.  Each row's
+    // 16-byte pieces are stored XOR-swizzled by a key taken from the channel
+    // bits that differ between the 16 rows of a state tile, so a tile read
+    // spreads over the banks.
+    constexpr int OFF_ST = (OFF_DB + NQ * C * 4 + 15) / 16 * 16;
+    constexpr int PR = V / 8;                    // 16-byte pieces per state row
+    constexpr int ST_PPT = 2 * K * PR / NT;      // pieces per thread
+    static_assert(2 * K * PR % NT == 0, "state pieces are dealt evenly");
+    constexpr int LDS_BYTES = OFF_ST + 2 * K * V * 2;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
     static_assert(KS * 64 * 16 + NQ * C * 2 * 4 <= 4 * C * C * 2, "early region");
     static_assert(6 * K * 4 + NQ * C * 2 * 4 + 2 * NQ * 4 <= C * UP * 2, "late region");
     __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
@@ -182,6 +200,23 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
     const bool valid = row < nvalid;
     const int64_t lrow = (start + (valid ? row : 0)) * a.H + h;
     const int64_t ch_base = (int64_t)slot * a.H + h;  // chunk-head index of the stored tensors
+
+    // start the copies of h and dS' into LDS; they land while the phases
+    // below run and are waited for before the products over value columns
+    {
+        const int nw = NT / 64;
+#pragma unroll
+        for (int i = 0; i < ST_PPT; ++i) {
+            const int j = i * nw + wave;                 // 1 KB block of the LDS copy
+            const int pc = 64 * j + L;                   // this lane's piece
+            const int arr = pc / (K * PR), pp = pc % (K * PR);
+            const int r = pp / PR, sl = pp % PR;
+            const uint16_t* src = (arr ? a.dss : a.hs) + ch_base * K * V + (int64_t)r * V +
+                                  8 * (sl ^ st_key<PR>(r));
+            __builtin_amdgcn_global_load_lds(
+                src, (__attribute__((address_space(3))) void*)(smem + OFF_ST + 1024 * j), 16, 0, 0);
+        }
+    }
 
     // ---- this lane's row and channels: q^, k^, log2 decay; beta
     float qh[KH][8], kh[KH][8], G[KH][8];
@@ -475,8 +510,9 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
             dvf[jv] = __builtin_bit_cast(bf16x8, valid ? x : zero4);
             uf[jv] = *reinterpret_cast<const bf16x8*>(&u_s[16 * blk + m][32 * jv + 8 * g]);
         }
-        const uint16_t* hbase = a.hs + ch_base * K * V;
-        const uint16_t* dbase = a.dss + ch_base * K * V;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's state copies
+        __syncthreads();                                   // everyone's
+        const unsigned char* st_s = smem + OFF_ST;
 #pragma unroll
         for (int tt2 = 0; tt2 < 2 * KH; ++tt2) {
             const int t = 2 * j0 + tt2;
@@ -485,8 +521,9 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
             float hsp = 0.f;
 #pragma unroll
             for (int jv = 0; jv < VS; ++jv) {
-                const u32x4 wh = *reinterpret_cast<const u32x4*>(hbase + (int64_t)ch * V + 32 * jv + 8 * g);
-                const u32x4 wd = *reinterpret_cast<const u32x4*>(dbase + (int64_t)ch * V + 32 * jv + 8 * g);
+                const int so = ch * (V * 2) + (((4 * jv + g) ^ st_key<PR>(ch)) << 4);
+                const u32x4 wh = *reinterpret_cast<const u32x4*>(st_s + so);
+                const u32x4 wd = *reinterpret_cast<const u32x4*>(st_s + K * V * 2 + so);
                 const bf16x8 ah = __builtin_bit_cast(bf16x8, wh), ad = __builtin_bit_cast(bf16x8, wd);
                 hq = mfma32(ah, dof[jv], hq);
                 hk = mfma32(ah, dvf[jv], hk);
@@ -664,10 +701,19 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(const float* part_d
     __shared__ float acc[4][64];
     __shared__ float al[256];
     const int h = blockIdx.x, c = blockIdx.y * 64 + (threadIdx.x & 63), q = threadIdx.x >> 6;
-    float s = 0.f;
-    if (c < K)
-        for (int sl = q; sl < n_slots; sl += 4) s += part_dt[((int64_t)sl * H + h) * K + c];
-    acc[q][threadIdx.x & 63] = s;
+    // eight independent partial sums, so eight loads are in flight at once;
+    // the combination order is fixed, so the result is reproducible
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c < K) {
+        int sl = q;
+        for (; sl + 28 < n_slots; sl += 32)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s[j] += part_dt[((int64_t)(sl + 4 * j) * H + h) * K + c];
+#pragma unroll
+        for (int j = 0; j < 7; ++j)
+            if (sl + 4 * j < n_slots) s[j] += part_dt[((int64_t)(sl + 4 * j) * H + h) * K + c];
+    }
+    acc[q][threadIdx.x & 63] = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
     float t = 0.f;
     if (blockIdx.y == 0)
         for (int sl = threadIdx.x; sl < n_slots; sl += 256) t += part_alog[(int64_t)sl * H + h];
