@@ -139,3 +139,53 @@ def test_split_workspace_grows_with_segments(lib):
         assert extra < 2 * states + nv * H * K * K * 4 + 4096
     # automatic: 2 heads x 4 column blocks is far too few workgroups, so it splits
     assert kda.workspace_size(B, T, H, K, V) > plain
+
+
+def _kda_bwd_call(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0,
+             scale=0.088, h0=None, cu=None, N=0, B=1, T=16, H=1, K=128, V=128, do=FAKE,
+             dfin=None, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE, dA=FAKE, ddt=FAKE,
+             dh0=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return lib.kda_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"], a["dt_bias"],
+                       a["lb"], a["scale"], a["h0"], a["cu"], a["N"], a["B"], a["T"], a["H"],
+                       a["K"], a["V"], a["do"], a["dfin"], a["dq"], a["dk"], a["dv"], a["dg"],
+                       a["dbeta"], a["dA"], a["ddt"], a["dh0"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(g=None), 1),
+    (dict(beta=None), 1), (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1),
+    (dict(dv=None), 1), (dict(dg=None), 1), (dict(dbeta=None), 1), (dict(dA=None), 1),
+    (dict(ddt=None), 1), (dict(A_log=None), 1), (dict(B=0), 1), (dict(H=0), 1),
+    (dict(lb=-7.0), 1), (dict(scale=float("nan")), 1), (dict(K=96), 2), (dict(V=32), 2),
+    (dict(ws=None), 3), (dict(wsb=4096), 3),
+    (dict(dq=ctypes.c_void_p(0x1002)), 1), (dict(dfin=ctypes.c_void_p(0x1004)), 1),
+    (dict(dh0=ctypes.c_void_p(0x1008)), 1),
+    # more (sequence, head) pairs than the recurrence grids can address
+    (dict(cu=FAKE, N=1 << 27, H=16, wsb=1 << 62), 1),
+])
+def test_kda_bwd_rejects_on_host(lib, over, code):
+    assert _kda_bwd_call(lib, **over) == code
+
+
+def test_kda_bwd_needs_the_larger_workspace(lib):
+    fwd = kda.workspace_size(1, 16, 1, 128, 128)
+    bwd = kda.bwd_workspace_size(1, 16, 1, 128, 128)
+    assert bwd > fwd > 0
+    # enough for the forward pass, not for the backward: rejected before any launch
+    assert _kda_bwd_call(lib, wsb=fwd) == 3
+    assert kda.bwd_workspace_size(1, 16, 1, 96, 128) == 0
+
+
+def test_gdn_bwd_rejects_on_host(lib):
+    def call(**over):
+        a = dict(g=FAKE, K=128, wsb=1 << 30, dg=FAKE)
+        a.update(over)
+        return lib.gdn_bwd(FAKE, FAKE, FAKE, a["g"], FAKE, 0.088, None, None, 0, 1, 16, 1,
+                           a["K"], 128, FAKE, None, FAKE, FAKE, FAKE, a["dg"], FAKE, None, FAKE,
+                           a["wsb"], None)
+    assert call(g=None) == 1
+    assert call(dg=None) == 1
+    assert call(K=32) == 2
+    assert call(wsb=4096) == 3
