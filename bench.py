@@ -11,7 +11,8 @@ resident in HBM.  Several input sets are rotated so that no step finds its
 inputs in the 256 MB last-level cache.  Prints one JSON line.
 
 Roofline: per-kernel durations come from HIP events recorded on the launch
-stream around each stage inside the timed region; the dominant kernel's
+stream around each stage inside the timed region (on a sample of the steps:
+an event between the two kernels would lengthen every step); the dominant kernel's
 algorithmic bytes (what it must read and write, see below) over its average
 duration is compared with 8 TB/s.  Traffic measured with rocprofv3 counters
 is read from profiles/ when it was taken on the current kernel sources.
@@ -286,31 +287,49 @@ def main():
     fin = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
+    # Per-kernel durations are sampled inside the timed region: an event
+    # recorded between the two kernels costs the step 3-5 us, so only every
+    # PERIOD-th step brackets kda_prep and every PERIOD-th (offset PERIOD/2)
+    # brackets kda_recur; the other steps run without events.
+    period = 8 if args.steps >= 16 else 2
+    def bracketed(i):
+        if args.steps < 2:
+            return ("prep", "recur")
+        return {0: ("prep",), period // 2: ("recur",)}.get(i % period, ())
+
+    def step(i, which=(), ev=None):
         d = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record(stream)
+        if "prep" in which:
+            ev["prep"][0].record(stream)
         kda.kda_prep(d["q"], d["k"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
                      base.lower_bound, ws, V=V)
-        if ev is not None:
-            ev[1].record(stream)
+        if "prep" in which:
+            ev["prep"][1].record(stream)
+        if "recur" in which:
+            ev["recur"][0].record(stream)
         kda.kda_recur(d["v"], K, base.scale, ws, out, d["initial_state"], fin)
-        if ev is not None:
-            ev[2].record(stream)
+        if "recur" in which:
+            ev["recur"][1].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    plan = [bracketed(i) for i in range(args.steps)]
+    evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for k in which} for which in plan]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, plan[i], evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    recur_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    def mean_ms(kernel):
+        t = [e[kernel][0].elapsed_time(e[kernel][1]) for e in evs if kernel in e]
+        return sum(t) / len(t)
+
+    prep_ms = mean_ms("prep")
+    recur_ms = mean_ms("recur")
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = B * T
     value = tokens / (ms_per_step * 1e-3)
@@ -325,7 +344,8 @@ def main():
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(dom, workload),
                 "algorithmic_bytes_per_launch": int(ab[dom]),
-                "avg_launch_us": round(kern[dom] * 1e3, 2)}
+                "avg_launch_us": round(kern[dom] * 1e3, 2),
+                "launches_timed": sum(1 for which in plan if dom.removeprefix("kda_") in which)}
     path_s = ms_per_step * 1e-3
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
