@@ -158,7 +158,7 @@ struct Rec {
 };
 
 // Per (chunk slot, head) record of the reverse pass: the same matrices as Rec,
-// transposed for the adjoint recurrence (kda_bwd_rec writes it from Rec).
+// transposed for the adjoint recurrence (kda_prep writes both).
 // With dS' the gradient of the state leaving the chunk and dO its output
 // gradient, the reverse step is
 //   dU = Kd dS' + scale Aqk^T dO,  dV = Tb^T dU,
