@@ -107,13 +107,13 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
     static_assert(VT % NQ == 0, "value tiles are dealt evenly to the channel groups");
     constexpr int UP = V + 8;  // padded row of the U' / W1 copies (bf16)
     using R = Rec<K>;
-    // LDS, 143 KB at K = V = 128 (one workgroup per CU, as the registers
+    // LDS, 155 KB at K = V = 128 (one workgroup per CU, as the registers
     // allow): regions whose lifetimes do not overlap share memory (the phase
     // of each is noted); the state copies have a region of their own.
     constexpr int OFF_GEND = 0;                               // float [2][K], all phases
     constexpr int OFF_BETA = OFF_GEND + 2 * K * 4;            // float [C], until dM
-    constexpr int OFF_P = OFF_BETA + C * 4;                   // float [C][C+1], P .. dM
-    constexpr int OFF_XT = OFF_P + C * (C + 1) * 4;           // bf16 [2][3][K][C], P .. intra
+    constexpr int OFF_P = OFF_BETA + C * 4;                   // float [NQ][C][C+1], P .. dM
+    constexpr int OFF_XT = OFF_P + NQ * C * (C + 1) * 4;      // bf16 [2][3][K][C], P .. intra
     constexpr int OFF_U = OFF_XT + 2 * 3 * K * C * 2;         // bf16 [C][UP], U' .. V-products
     constexpr int OFF_W = OFF_U + C * UP * 2;                 // bf16 [C][UP], U' .. dM;
                                                               //   then the late sums below
@@ -133,10 +133,19 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS per workgroup");
     static_assert(KS * 64 * 16 + NQ * C * 2 * 4 <= 4 * C * C * 2, "early region");
     static_assert(6 * K * 4 + NQ * C * 2 * 4 + 2 * NQ * 4 <= C * UP * 2, "late region");
+
     __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
     auto& gend_s = *reinterpret_cast<float(*)[2][K]>(smem + OFF_GEND);
     auto& beta_s = *reinterpret_cast<float(*)[C]>(smem + OFF_BETA);
-    auto& P_s = *reinterpret_cast<float(*)[C][C + 1]>(smem + OFF_P);  // tril_strict(KG Kinv^T)
+    // tril_strict(KG Kinv^T) as the channel groups' shares: P = sum over q of
+    // P_s[q], added in the order q = 0, 1, .. wherever P is read
+    auto& P_s = *reinterpret_cast<float(*)[NQ][C][C + 1]>(smem + OFF_P);
+    auto P_at = [&](int r, int col) {
+        float sum = P_s[0][r][col];
+#pragma unroll
+        for (int qq = 1; qq < NQ; ++qq) sum += P_s[qq][r][col];
+        return sum;
+    };
     // channel-major token operands [hi/lo][part][c][pos(s)]: 0: k^ 2^-Gl,
     // 1: q^ 2^Gl, 2: k^ 2^Gl (Gl: log2 decay within the token's block), each as
     // a bf16 pair hi + lo.  A token pair (r, j) enters dG_r through one operand
@@ -312,26 +321,13 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
             for (int jj = 0; jj < KH; ++jj) Pc = mfma32(ka_f[jj], kbc0_s[(j0 + jj) * 64 + L], Pc);
         }
-        // the channel groups add up in a fixed order: the last writes, the
-        // others add (one group per step, so the sum is reproducible)
-        if (hf == NQ - 1) {
+        // each channel group's share into a slot of its own; readers add the
+        // shares in a fixed order, so the sum is reproducible
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * blk + 4 * g + i;
-                P_s[r][16 * blk + m] = (m < 4 * g + i) ? Pacc[i] : 0.f;
-                P_s[r][16 * (1 - blk) + m] = blk == 1 ? Pc[i] : 0.f;
-            }
-        }
-        for (int qq = NQ - 2; qq >= 0; --qq) {
-            __syncthreads();
-            if (hf == qq) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * blk + 4 * g + i;
-                    if (m < 4 * g + i) P_s[r][16 * blk + m] += Pacc[i];
-                    if (blk == 1) P_s[r][m] += Pc[i];
-                }
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * blk + 4 * g + i;
+            P_s[hf][r][16 * blk + m] = (m < 4 * g + i) ? Pacc[i] : 0.f;
+            P_s[hf][r][16 * (1 - blk) + m] = blk == 1 ? Pc[i] : 0.f;
         }
     }
     __syncthreads();
@@ -347,7 +343,7 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
         // P^T rows of this block as a token operand: slot (g, e) holds P[tok(g, e)][16 b + m]
         float ptf[EL];
 #pragma unroll
-        for (int e = 0; e < EL; ++e) ptf[e] = P_s[16 * (e >> 2) + 4 * g + (e & 3)][16 * blk + m];
+        for (int e = 0; e < EL; ++e) ptf[e] = P_at(16 * (e >> 2) + 4 * g + (e & 3), 16 * blk + m);
         const bf16xEL apt = pack8(ptf);
         const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -406,7 +402,7 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
             const int r = 16 * blk + 4 * g + i;
             const float dmx = j <= r ? a.scale * dm[i] : 0.f;
             const float dpx = j < r ? -beta_s[r] * e1[i] : 0.f;
-            if (j < r) dbp[i] -= P_s[r][j] * e1[i];
+            if (j < r) dbp[i] -= P_at(r, j) * e1[i];
             dmr_s[r][tok_pos(j)] = bits(dmx);
             dpr_s[r][tok_pos(j)] = bits(dpx);
             dmv[i] = (bf16)dmx;
@@ -556,7 +552,8 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
             }
         }
     }
-    __syncthreads();
+    // (no barrier: the next phase writes only tot_s and dot_s, which no wave
+    // reads or writes in this one; the barrier after it publishes both phases)
 
     // ---- dG, its reverse cumulative sum over the chunk, and the chain rule
     float dla[KH][8];
