@@ -189,3 +189,17 @@ def test_gdn_bwd_rejects_on_host(lib):
     assert call(dg=None) == 1
     assert call(K=32) == 2
     assert call(wsb=4096) == 3
+
+
+@pytest.mark.parametrize("flag,value", [
+    ("use_qk_l2norm_in_kernel", False), ("use_gate_in_kernel", False),
+    ("use_beta_sigmoid_in_kernel", False), ("safe_gate", False),
+    ("transpose_state_layout", True),
+])
+def test_chunk_kda_rejects_unsupported_variants(flag, value):
+    import torch
+    from chunked_gated_delta_kda_amd.autograd import chunk_kda
+    x = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(NotImplementedError, match=flag):
+        chunk_kda(x, x, x, x, torch.zeros(1, 4, 1, dtype=torch.bfloat16), torch.zeros(1),
+                  torch.zeros(64), **{flag: value})
