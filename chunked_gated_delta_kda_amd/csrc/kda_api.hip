@@ -33,8 +33,9 @@ struct SplitPlan {
     int64_t n_virt;
 };
 
-constexpr int32_t SPLIT_MIN_CHUNKS = 64;   // shortest segment the automatic choice makes
-constexpr int32_t SPLIT_TARGET_BLOCKS = 512;  // second-pass workgroups it aims for
+constexpr int32_t SPLIT_MIN_CHUNKS = 64;      // shortest segment the automatic choice makes
+constexpr int32_t SPLIT_MAX_BLOCKS = 128;     // it splits only below this many workgroups
+constexpr int32_t SPLIT_TARGET_BLOCKS = 2048; // second-pass workgroups it aims for
 constexpr int32_t RECUR_COLS = 32;         // value columns per kda_recur workgroup
 constexpr float SPLIT_BOUND_LIMIT = -40.f; // log2: transitions below 2^-40 are negligible
 
@@ -50,7 +51,7 @@ SplitPlan plan_split(int32_t B, int32_t T, int32_t H, int32_t V, int32_t N, bool
         // CUs idle and the sequences are long
         const int64_t blocks = (int64_t)N * H * (V / RECUR_COLS);
         const int64_t avg = (slots + N - 1) / N;
-        if (blocks >= SPLIT_TARGET_BLOCKS / 4 || avg < 2 * SPLIT_MIN_CHUNKS) return p;
+        if (blocks >= SPLIT_MAX_BLOCKS || avg < 2 * SPLIT_MIN_CHUNKS) return p;
         const int64_t segs = (SPLIT_TARGET_BLOCKS + blocks - 1) / blocks;
         L = std::max<int64_t>(SPLIT_MIN_CHUNKS, (avg + segs - 1) / segs);
         if (L >= avg) return p;
