@@ -266,9 +266,11 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
             unpack8(*reinterpret_cast<const u32x4*>(a.g_kda + lrow * K + c), x);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                G[jj][e] = valid ? fmaxf(a.lower_bound,
-                                         -rate * softplus_f(x[e] + a.dt_bias[(int64_t)h * K + c + e])) * LOG2E
-                                 : 0.f;
+                // every row (padding rows re-read a real row; the value is
+                // finite) and zeroed on padding rows: no branch per element
+                G[jj][e] = fmaxf(a.lower_bound,
+                                 -rate * softplus_f(x[e] + a.dt_bias[(int64_t)h * K + c + e])) *
+                           LOG2E * (valid ? 1.f : 0.f);
         }
     }
     // in-block inclusive prefix (log2), block totals to LDS

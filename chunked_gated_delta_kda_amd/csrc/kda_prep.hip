@@ -72,6 +72,12 @@ __device__ __forceinline__ void row_scan16_n(float* x) {
 
 __device__ __forceinline__ float lane_val(float x, int src) { return __shfl(x, src, 64); }
 
+// LDS position of 16-byte unit u of the transposed record matrices: one write
+// instruction of the transpose touches the units of 4 values of bits 4-5 and
+// 4 of bits 2-3 of u; XOR-ing bits 4-5 into bits 0-1 puts those 16 units at
+// 16 different 16-byte positions within 256 bytes, i.e. different banks.
+__device__ __forceinline__ int st_unit(int u) { return u ^ ((u >> 4) & 3); }
+
 __device__ __forceinline__ halfx4 to_h4(floatx4 x) {
     halfx4 r;
     r[0] = (_Float16)x[0];
@@ -198,6 +204,7 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     }
     // beta: KDA logits through the sigmoid, GDN probabilities as given; 0 on padding
     const float b = valid ? (GDN ? braw : sigmoid_f(braw)) : 0.f;
+    const float vmask = valid ? 1.f : 0.f;
 
     // ---- L2 norms: a row's channels live in lanes m, m+16, m+32, m+48
     float sq = 0.f, sk = 0.f;
@@ -237,8 +244,11 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
             const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                // computed for every row and zeroed on padding rows by a product
+                // (the value is finite: padding rows re-read a real row, and the
+                // floor bounds it), so the loop has no branch per element
                 const float la =
-                    valid ? fmaxf(a.lower_bound, -rate * softplus_f(x[e] + dv[e])) * LOG2E : 0.f;
+                    fmaxf(a.lower_bound, -rate * softplus_f(x[e] + dv[e])) * LOG2E * vmask;
                 rowmax = fmaxf(rowmax, la);
                 G[j][e] = la;
             }
@@ -339,11 +349,13 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         *reinterpret_cast<bf16x8*>(rec + R::NKG + ((blk * KS + j) * 64 + L) * 16) = pack8(kg, -1.f);
         *reinterpret_cast<bf16x8*>(rec + R::QG + ((blk * KS + j) * 64 + L) * 16) = pack8(qg);
         // KdT[t][g'][m'][e'] = Kd[tok(g', e')][rho(t, m')]: transposed through LDS
+        // (16-byte units swizzled by st_unit, which the copy-out undoes)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int t = 2 * j + (e >> 2), mm = 4 * g + (e & 3);
             const int ee = 4 * blk + (m & 3);
-            const int ti = ((t * 4 + (m >> 2)) * 16 + mm) * EL + ee;
+            const int tr = ((t * 4 + (m >> 2)) * 16 + mm) * EL + ee;  // record order
+            const int ti = st_unit(tr / 8) * 8 + tr % 8;
             kdt_s[ti] = __builtin_bit_cast(uint16_t, (bf16)kd[e]);
             if constexpr (BREC) {
                 qgt_s[ti] = __builtin_bit_cast(uint16_t, (bf16)qg[e]);
@@ -405,15 +417,16 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     // KdT out, 16 bytes per lane per step
 #pragma unroll
     for (int p = 0; p < C * K * 2 / (64 * NB * 16); ++p) {
-        const int off = (p * 64 * NB + threadIdx.x) * 16;
+        const int u = p * 64 * NB + threadIdx.x;  // 16-byte unit of the record
+        const int off = u * 16, lo = st_unit(u) * 16;
         *reinterpret_cast<u32x4*>(rec + R::KDT + off) =
-            *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(kdt_s) + off);
+            *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(kdt_s) + lo);
         if constexpr (BREC) {
             unsigned char* br = a.brec + ((int64_t)slot * a.H + h) * BRec<K>::BYTES;
             *reinterpret_cast<u32x4*>(br + BRec<K>::QGT + off) =
-                *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(qgt_s) + off);
+                *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(qgt_s) + lo);
             *reinterpret_cast<u32x4*>(br + BRec<K>::NKGT + off) =
-                *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(nkgt_s) + off);
+                *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned char*>(nkgt_s) + lo);
         }
     }
     if constexpr (NB == 2) {
