@@ -265,6 +265,7 @@ int run_recur(const Common& c, int32_t N, hipStream_t stream) {
     p1.trans_flag = w.trans_flag;
     p1.bound = w.bound;
     p1.bound_limit = SPLIT_BOUND_LIMIT;
+    p1.window = 1;  // a segment's zero-start end state needs only its decay window
     kda::launch_recur(p1, c.K, stream);
     kda::SplitScanArgs sa{};
     sa.initial_state = c.initial_state;

@@ -51,6 +51,7 @@ struct RecurArgs {
                                // bound showed the transition negligible (not computed)
     const float* bound;        // [slots, H] chunk bounds from kda_prep (log2)
     float bound_limit;         // a transition with a summed bound below this is negligible
+    int32_t window;            // 1: value columns start at the segment's decay window
     // Backward pass (null for the forward pass):
     uint16_t* chunk_state;     // [slots, H, K, V] bf16: the state entering each chunk
                                // (reverse pass: the state gradient leaving each chunk)

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
     int64_t t0, t1;
     int s0, s1;
     seq_span(a, n, t0, t1, s0, s1);
-    const int nch = s1 - s0;
+    int nch = s1 - s0;
     if (trans) {
         // ||M||_2 <= 2^(sum of the chunk bounds): when that is negligible the
         // transition is not needed (and not computed).  Every wave reaches the
@@ -102,6 +102,35 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
         const bool needed = !(sum < a.bound_limit);
         if (cb == a.V && threadIdx.x == 0) a.trans_flag[(int64_t)n * a.H + h] = needed ? 1 : 0;
         if (!needed) return;
+    }
+    // Decay window (first pass of sequence splitting, value columns): a
+    // segment's end state from a zero start depends, to within
+    // 2^bound_limit of the state's size, only on its trailing chunks back to
+    // where their summed bounds fall below bound_limit (the product of those
+    // chunks' transitions is that small), so the recurrence starts there.
+    // Every wave computes the same start.
+    if (a.window && !trans && nch > 0) {
+        const int ln = threadIdx.x & 63;
+        float acc = 0.f;
+        for (int base = 0; base < nch; base += 64) {
+            const int c = nch - 1 - base - ln;  // this lane's chunk, from the last back
+            float x = c >= 0 ? a.bound[(int64_t)(s0 + c) * a.H + h] : 0.f;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {  // suffix sums: inclusive scan over lanes
+                const float y = __shfl_up(x, o, 64);
+                if (ln >= o) x += y;
+            }
+            x += acc;
+            const unsigned long long hit = __ballot(c >= 0 && x < a.bound_limit);
+            if (hit) {  // uniform: keep chunks nch - w .. nch - 1
+                const int w = base + __ffsll((long long)hit);
+                t0 += (int64_t)C * (nch - w);
+                s0 += nch - w;
+                nch = w;
+                break;
+            }
+            acc = __shfl(x, 63, 64);
+        }
     }
     // Both roles run the same number of iterations (one barrier each), rounded
     // up to the unroll factor; iterations past the last chunk only synchronise.

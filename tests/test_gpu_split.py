@@ -1,8 +1,9 @@
 """GPU parity of sequence splitting (kda_fwd_split / gdn_fwd_split and the
-automatic choice of kda_fwd) against the fp64 oracle, in the three regimes
-of the transition bound: a segment that forgets its entering state (the
-transition is skipped), one that keeps it (the transition is computed and
-applied by the scan) and no decay at all."""
+automatic choice of kda_fwd) against the fp64 oracle, in the regimes of the
+transition bound: a segment that forgets its entering state within a few
+chunks (the transition is skipped and the first pass runs only the decay
+window), one that forgets it within part of the segment, one that keeps it
+(the transition is computed and applied by the scan) and no decay at all."""
 import pytest
 import torch
 
@@ -19,6 +20,9 @@ CASES = [
     ("default decay: transitions negligible",
      lambda: inputs.kda_workload(2, 3000, 2, 128, 128, seed=6100, init_std=0.05,
                                  name="split_fast"), 16),
+    ("medium decay: decay window shorter than the segment",
+     lambda: inputs.kda_workload(1, 3000, 2, 128, 128, seed=6150, dt_bias_value=-2.0,
+                                 init_std=0.05, name="split_medium"), 16),
     ("no decay",
      lambda: inputs.kda_workload(1, 1500, 2, 128, 128, seed=6200, g_mean=-20.0, g_std=1.0,
                                  init_std=0.05, name="split_nodecay"), 8),
