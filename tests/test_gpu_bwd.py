@@ -166,6 +166,12 @@ CASES = [
     ("GDN slow decay",
      lambda: inputs.gdn_workload(2, 180, 2, 128, 128, seed=7600, init_std=0.05, decay_shift=-6.0,
                                  name="bwd_gdn"), 0.05),
+    ("single-token and one-chunk sequences (T = 1, 31, 32, 33)",
+     lambda: inputs.kda_workload(1, 0, 2, 128, 128, seed=7800, dt_bias_value=-6.0,
+                                 init_std=0.05, lengths=[1, 31, 32, 33], name="bwd_short"),
+     0.05),
+    ("B=3 T=1 (every chunk one token)",
+     lambda: inputs.kda_workload(3, 1, 2, 64, 64, seed=7900, init_std=0.05, name="bwd_t1"), 0.05),
     ("GDN default decay, no state",
      lambda: inputs.gdn_workload(1, 100, 3, 128, 128, seed=7700, name="bwd_gdn_default"), None),
 ]

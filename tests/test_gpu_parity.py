@@ -18,7 +18,7 @@ def test_config0_tiny():
 
 
 # odd lengths and head counts in the style of the pages' own test list
-ODD = [(1, 63, 1), (2, 500, 3), (2, 1000, 3), (3, 1024, 4)]
+ODD = [(3, 1, 2), (1, 33, 2), (1, 63, 1), (2, 500, 3), (2, 1000, 3), (3, 1024, 4)]
 
 
 @pytest.mark.parametrize("B,T,H", ODD, ids=lambda x: str(x))
