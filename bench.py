@@ -167,6 +167,68 @@ def bench_decode(args, torch, kda, inputs, dev):
     }), flush=True)
 
 
+def bench_train(args, torch, kda, inputs, dev):
+    """One training step of the recurrence: the forward pass that keeps its chunk
+    states (kda_fwd_save) and the backward pass that reuses them
+    (kda_bwd_saved), on the benchmark workload with rotated input sets; the
+    same step with the plain forward pass and the recomputing backward pass
+    (kda_fwd + kda_bwd) is timed beside it."""
+    base = inputs.config(1)
+    B, T, H, K, V, N = base.B, base.T, base.H, base.K, base.V, base.n_seqs
+    sets = []
+    for r in range(args.sets):
+        w = base if r == 0 else inputs.kda_workload(B, T, H, K, V, seed=1001 + 1000 * r,
+                                                    init_std=0.05)
+        do, dfin = inputs.output_grads(w, seed=5000 + r, dfinal_std=0.05)
+        d = w.to(dev)
+        d["do"], d["dfin"] = do.to(dev), dfin.to(dev)
+        sets.append(d)
+    ws = torch.empty(kda.bwd_workspace_size(B, T, H, K, V), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def saved_step(i):
+        d = sets[i % len(sets)]
+        args_ = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"])
+        kda.kda_fwd_save(*args_, base.lower_bound, base.scale, d["initial_state"], workspace=ws,
+                         out=out, final_out=fin)
+        kda.kda_bwd_saved(*args_, d["do"], ws, base.lower_bound, base.scale, d["initial_state"],
+                          d["dfin"])
+
+    def recompute_step(i):
+        d = sets[i % len(sets)]
+        args_ = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"])
+        kda.kda_fwd(*args_, base.lower_bound, base.scale, d["initial_state"], workspace=ws,
+                    out=out, final_out=fin)
+        kda.kda_bwd(*args_, d["do"], base.lower_bound, base.scale, d["initial_state"],
+                    d["dfin"], workspace=ws)
+
+    def timed(step):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps
+
+    t_saved = timed(saved_step)
+    t_recompute = timed(recompute_step)
+    print(json.dumps({
+        "metric": "kda training step tokens/sec (forward + all gradients), B2 T2048 H32 K=V=128",
+        "value": round(B * T / t_saved, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_saved * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": inputs.CONFIG_NAMES[1] + "_train", "B": B, "T": T, "H": H, "K": K,
+                   "V": V, "chunk": C, "input_sets_rotated": len(sets),
+                   "step": "kda_fwd_save + kda_bwd_saved"},
+        "recompute_ms_per_step": round(t_recompute * 1e3, 5),
+    }), flush=True)
+
+
 def bench_bwd(args, torch, kda, inputs, dev):
     """The backward pass (kda_bwd: every gradient, from dL/do and dL/d final state)
     on the benchmark workload, input sets rotated as for the forward pass.  Its
@@ -235,6 +297,9 @@ def main():
                     help="instead of the forward pass, time the single-token decode step "
                          "(kda_decode) for --decode-seqs sequences x 32 heads, K=V=128")
     ap.add_argument("--decode-seqs", type=int, default=64)
+    ap.add_argument("--train", action="store_true",
+                    help="instead of the forward pass, time a training step (forward pass "
+                         "keeping its states + backward pass reusing them) on the same workload")
     ap.add_argument("--bwd", action="store_true",
                     help="instead of the forward pass, time the backward pass (kda_bwd) on "
                          "the same workload")
@@ -278,6 +343,9 @@ def main():
         return
     if args.bwd:
         bench_bwd(args, torch, kda, inputs, dev)
+        return
+    if args.train:
+        bench_train(args, torch, kda, inputs, dev)
         return
 
     base = inputs.config(1)

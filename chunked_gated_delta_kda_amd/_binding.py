@@ -20,7 +20,8 @@ _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED"
 EXPORTS = ("kda_fwd", "gdn_fwd", "kda_fwd_workspace_size", "gdn_fwd_workspace_size",
            "kda_fwd_split_workspace_size", "kda_fwd_split", "gdn_fwd_split", "kda_prep",
            "gdn_prep", "kda_recur", "kda_decode", "gdn_decode", "kda_bwd_workspace_size",
-           "kda_bwd", "gdn_bwd", "kda_status_str", "kda_version")
+           "kda_bwd", "gdn_bwd", "kda_fwd_save", "gdn_fwd_save", "kda_bwd_saved",
+           "gdn_bwd_saved", "kda_status_str", "kda_version")
 
 
 class LibKdaError(RuntimeError):
@@ -80,6 +81,11 @@ def load(path: Path | str | None = None):
     lib.gdn_bwd.restype = ctypes.c_int
     lib.gdn_bwd.argtypes = [u16p, u16p, u16p, f32p, u16p, f32, f32p, i32p, i32, i32, i32, i32,
                             i32, i32, u16p, f32p, u16p, u16p, u16p, f32p, u16p, f32p, vp, sz, vp]
+    # the training pair shares the signatures of kda_fwd / gdn_fwd and kda_bwd / gdn_bwd
+    for a, b in (("kda_fwd_save", "kda_fwd"), ("gdn_fwd_save", "gdn_fwd"),
+                 ("kda_bwd_saved", "kda_bwd"), ("gdn_bwd_saved", "gdn_bwd")):
+        getattr(lib, a).restype = ctypes.c_int
+        getattr(lib, a).argtypes = getattr(lib, b).argtypes
     for name in ("kda_fwd_workspace_size", "gdn_fwd_workspace_size", "kda_bwd_workspace_size"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_size_t
@@ -242,6 +248,60 @@ def gdn_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state
     return a["o"], a["final"]
 
 
+def _save_workspace(q, v, cu_seqlens, workspace):
+    """A backward-sized workspace for the *_fwd_save calls (checked or allocated)."""
+    torch = _torch()
+    B, T, H, K = q.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    need = bwd_workspace_size(B, T, H, K, v.shape[3], N)
+    if need == 0:
+        raise LibKdaError(2, status_str(2))
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=q.device)
+    if _nbytes(workspace) < need or workspace.device != q.device:
+        raise LibKdaError(3, status_str(3))
+    return workspace
+
+
+def kda_fwd_save(q, k, v, g, beta, A_log, dt_bias, lower_bound=-5.0, scale=None,
+                 initial_state=None, output_final_state=True, cu_seqlens=None, workspace=None,
+                 out=None, final_out=None):
+    """kda_fwd that also leaves in ``workspace`` (backward-sized; allocated when
+    None) what kda_bwd_saved needs.  Returns (o, final_state or None, workspace)."""
+    torch = _torch()
+    ws = _save_workspace(q, v, cu_seqlens, workspace)
+    a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens, ws,
+                 "kda", out, final_out, -1)
+    B, T, H, K = a["B"], a["T"], a["H"], a["K"]
+    _need(g, "g", torch.bfloat16, (B, T, H, K), q.device)
+    _need(A_log, "A_log", torch.float32, (H,), q.device)
+    _need(dt_bias, "dt_bias", torch.float32, None, q.device)
+    if dt_bias.numel() != H * K:
+        raise ValueError("dt_bias must hold H * K values ([H, K] or [H * K])")
+    _check(load().kda_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                               _ptr(dt_bias), float(lower_bound), a["scale"], _ptr(initial_state),
+                               _ptr(a["final"]), _ptr(cu_seqlens), a["N"], B, T, H, K, a["V"],
+                               _ptr(a["o"]), _ptr(ws), _nbytes(ws), a["stream"]))
+    return a["o"], a["final"], ws
+
+
+def gdn_fwd_save(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+                 cu_seqlens=None, workspace=None, out=None, final_out=None):
+    """gdn_fwd that also leaves in ``workspace`` what gdn_bwd_saved needs.
+    Returns (o, final_state or None, workspace)."""
+    torch = _torch()
+    ws = _save_workspace(q, v, cu_seqlens, workspace)
+    a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens, ws,
+                 "gdn", out, final_out, -1)
+    B, T, H = a["B"], a["T"], a["H"]
+    _need(g, "g", torch.float32, (B, T, H), q.device)
+    _check(load().gdn_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), a["scale"],
+                               _ptr(initial_state), _ptr(a["final"]), _ptr(cu_seqlens), a["N"],
+                               B, T, H, a["K"], a["V"], _ptr(a["o"]), _ptr(ws), _nbytes(ws),
+                               a["stream"]))
+    return a["o"], a["final"], ws
+
+
 def _check(st):
     if st != 0:
         raise LibKdaError(st, status_str(st))
@@ -365,8 +425,17 @@ def _bwd_prepare(q, k, v, beta, do, scale, initial_state, dfinal, cu_seqlens, wo
     return a
 
 
+def kda_bwd_saved(q, k, v, g, beta, A_log, dt_bias, do, workspace, lower_bound=-5.0, scale=None,
+                  initial_state=None, dfinal=None, cu_seqlens=None, need_dh0=True):
+    """kda_bwd reusing the ``workspace`` a kda_fwd_save call on the same inputs
+    filled (its chunk records and states are not recomputed)."""
+    return kda_bwd(q, k, v, g, beta, A_log, dt_bias, do, lower_bound, scale, initial_state,
+                   dfinal, cu_seqlens, workspace, need_dh0, _saved=True)
+
+
 def kda_bwd(q, k, v, g, beta, A_log, dt_bias, do, lower_bound=-5.0, scale=None,
-            initial_state=None, dfinal=None, cu_seqlens=None, workspace=None, need_dh0=True):
+            initial_state=None, dfinal=None, cu_seqlens=None, workspace=None, need_dh0=True,
+            _saved=False):
     """Gradients of kda_fwd for dL/do = ``do`` [B,T,H,V] bf16 and dL/d(final state) =
     ``dfinal`` [N,H,K,V] fp32 (None: zero).  Returns a dict with dq, dk [B,T,H,K],
     dv [B,T,H,V], dg [B,T,H,K], dbeta [B,T,H] (bf16), dA_log [H], ddt_bias [H,K]
@@ -386,17 +455,24 @@ def kda_bwd(q, k, v, g, beta, A_log, dt_bias, do, lower_bound=-5.0, scale=None,
     o["dA_log"] = torch.empty((H,), dtype=torch.float32, device=dev)
     o["ddt_bias"] = torch.empty((H, K), dtype=torch.float32, device=dev)
     ws = a["workspace"]
-    _check(load().kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
-                          _ptr(dt_bias), float(lower_bound), a["scale"], _ptr(initial_state),
-                          _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(do), _ptr(dfinal),
-                          _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o["dg"]),
-                          _ptr(o["dbeta"]), _ptr(o["dA_log"]), _ptr(o["ddt_bias"]),
-                          _ptr(o["dh0"]), _ptr(ws), _nbytes(ws), a["stream"]))
+    fn = load().kda_bwd_saved if _saved else load().kda_bwd
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
+              float(lower_bound), a["scale"], _ptr(initial_state), _ptr(cu_seqlens), N, B, T, H,
+              K, V, _ptr(do), _ptr(dfinal), _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]),
+              _ptr(o["dg"]), _ptr(o["dbeta"]), _ptr(o["dA_log"]), _ptr(o["ddt_bias"]),
+              _ptr(o["dh0"]), _ptr(ws), _nbytes(ws), a["stream"]))
     return o
 
 
+def gdn_bwd_saved(q, k, v, g, beta, do, workspace, scale=None, initial_state=None, dfinal=None,
+                  cu_seqlens=None, need_dh0=True):
+    """gdn_bwd reusing the ``workspace`` a gdn_fwd_save call on the same inputs filled."""
+    return gdn_bwd(q, k, v, g, beta, do, scale, initial_state, dfinal, cu_seqlens, workspace,
+                   need_dh0, _saved=True)
+
+
 def gdn_bwd(q, k, v, g, beta, do, scale=None, initial_state=None, dfinal=None, cu_seqlens=None,
-            workspace=None, need_dh0=True):
+            workspace=None, need_dh0=True, _saved=False):
     """Gradients of gdn_fwd: dict with dq, dk, dv, dbeta (bf16), dg [B,T,H] and dh0
     (fp32).  Arguments as kda_bwd."""
     torch = _torch()
@@ -407,9 +483,9 @@ def gdn_bwd(q, k, v, g, beta, do, scale=None, initial_state=None, dfinal=None, c
     o = a["out"]
     o["dg"] = torch.empty_like(g)
     ws = a["workspace"]
-    _check(load().gdn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), a["scale"],
-                          _ptr(initial_state), _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(do),
-                          _ptr(dfinal), _ptr(o["dq"]), _ptr(o["dk"]), _ptr(o["dv"]),
-                          _ptr(o["dg"]), _ptr(o["dbeta"]), _ptr(o["dh0"]), _ptr(ws),
-                          _nbytes(ws), a["stream"]))
+    fn = load().gdn_bwd_saved if _saved else load().gdn_bwd
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), a["scale"], _ptr(initial_state),
+              _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(do), _ptr(dfinal), _ptr(o["dq"]),
+              _ptr(o["dk"]), _ptr(o["dv"]), _ptr(o["dg"]), _ptr(o["dbeta"]), _ptr(o["dh0"]),
+              _ptr(ws), _nbytes(ws), a["stream"]))
     return o

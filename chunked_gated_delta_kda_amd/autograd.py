@@ -5,8 +5,11 @@ call of the cuLA page ("cuLA(CUDA Linear Attention): NVIDIA Blackwell, Hopper
 GPU를 위한 선형 어텐션 고성능 CUDA 커널 라이브러리", section "cuLA 설치 및
 사용법"), where the output is then differentiated with ``o.backward(do)``.  The
 forward pass is kda_fwd / gdn_fwd and the backward pass kda_bwd / gdn_bwd of the
-C ABI; this module only checks and forwards arguments (no arithmetic of the
-method runs outside the library).
+C ABI; when an input needs a gradient the forward pass is kda_fwd_save /
+gdn_fwd_save, which keeps in a workspace what the backward pass would otherwise
+recompute, and the backward pass kda_bwd_saved / gdn_bwd_saved reuses it.
+This module only checks and forwards arguments (no arithmetic of the method
+runs outside the library).
 
 The kernels fix the variant the pages describe as the fast path: q and k are
 L2-normalised inside, the KDA gate is formed inside from g, A_log and dt_bias
@@ -42,8 +45,16 @@ class _KDA:
                 @staticmethod
                 def forward(ctx, q, k, v, g, beta, A_log, dt_bias, initial_state, scale,
                             lower_bound, cu_seqlens, output_final_state):
-                    o, final = _b.kda_fwd(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale,
-                                          initial_state, output_final_state, cu_seqlens)
+                    ctx.workspace = None
+                    if any(ctx.needs_input_grad):
+                        # keep what the backward pass would recompute
+                        o, final, ctx.workspace = _b.kda_fwd_save(
+                            q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
+                            output_final_state, cu_seqlens)
+                    else:
+                        o, final = _b.kda_fwd(q, k, v, g, beta, A_log, dt_bias, lower_bound,
+                                              scale, initial_state, output_final_state,
+                                              cu_seqlens)
                     ctx.save_for_backward(q, k, v, g, beta, A_log, dt_bias, initial_state,
                                           cu_seqlens)
                     ctx.scale, ctx.lower_bound = scale, lower_bound
@@ -56,10 +67,16 @@ class _KDA:
                 def backward(ctx, do, dfinal=None):
                     q, k, v, g, beta, A_log, dt_bias, h0, cu = ctx.saved_tensors
                     need = ctx.needs_input_grad
-                    r = _b.kda_bwd(q, k, v, g, beta, A_log, dt_bias, do.contiguous(),
-                                   ctx.lower_bound, ctx.scale, h0,
-                                   None if dfinal is None else dfinal.contiguous(), cu,
-                                   need_dh0=h0 is not None and need[7])
+                    # the workspace lives as long as the graph (a second backward
+                    # pass under retain_graph reuses it)
+                    args = (q, k, v, g, beta, A_log, dt_bias, do.contiguous())
+                    kw = dict(lower_bound=ctx.lower_bound, scale=ctx.scale, initial_state=h0,
+                              dfinal=None if dfinal is None else dfinal.contiguous(),
+                              cu_seqlens=cu, need_dh0=h0 is not None and need[7])
+                    if ctx.workspace is not None:
+                        r = _b.kda_bwd_saved(*args, ctx.workspace, **kw)
+                    else:
+                        r = _b.kda_bwd(*args, **kw)
                     return (r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], r["dA_log"],
                             r["ddt_bias"].view(ctx.dt_shape), r["dh0"], None, None, None, None)
 
@@ -79,8 +96,14 @@ class _GDN:
                 @staticmethod
                 def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens,
                             output_final_state):
-                    o, final = _b.gdn_fwd(q, k, v, g, beta, scale, initial_state,
-                                          output_final_state, cu_seqlens)
+                    ctx.workspace = None
+                    if any(ctx.needs_input_grad):
+                        o, final, ctx.workspace = _b.gdn_fwd_save(
+                            q, k, v, g, beta, scale, initial_state, output_final_state,
+                            cu_seqlens)
+                    else:
+                        o, final = _b.gdn_fwd(q, k, v, g, beta, scale, initial_state,
+                                              output_final_state, cu_seqlens)
                     ctx.save_for_backward(q, k, v, g, beta, initial_state, cu_seqlens)
                     ctx.scale = scale
                     if final is None:
@@ -91,9 +114,14 @@ class _GDN:
                 def backward(ctx, do, dfinal=None):
                     q, k, v, g, beta, h0, cu = ctx.saved_tensors
                     need = ctx.needs_input_grad
-                    r = _b.gdn_bwd(q, k, v, g, beta, do.contiguous(), ctx.scale, h0,
-                                   None if dfinal is None else dfinal.contiguous(), cu,
-                                   need_dh0=h0 is not None and need[5])
+                    args = (q, k, v, g, beta, do.contiguous())
+                    kw = dict(scale=ctx.scale, initial_state=h0,
+                              dfinal=None if dfinal is None else dfinal.contiguous(),
+                              cu_seqlens=cu, need_dh0=h0 is not None and need[5])
+                    if ctx.workspace is not None:
+                        r = _b.gdn_bwd_saved(*args, ctx.workspace, **kw)
+                    else:
+                        r = _b.gdn_bwd(*args, **kw)
                     return (r["dq"], r["dk"], r["dv"], r["dg"], r["dbeta"], r["dh0"], None, None,
                             None)
 

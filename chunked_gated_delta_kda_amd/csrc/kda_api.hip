@@ -312,20 +312,25 @@ struct BwdIO {
     float *dA_log, *ddt_bias, *dh0;
 };
 
-// The backward pass: kda_prep (forward and reverse-pass records), the
-// forward sweep that keeps every chunk's entering state, the reverse sweep
-// (state gradients, dv, dh0), the chunk gradient kernel and the
-// gate-parameter sums.
-int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& io,
-            hipStream_t stream) {
+// The backward pass's share of its workspace (after the forward layout).
+BwdLayout bwd_part(const Common& c, int32_t N, const WsLayout& w) {
+    const SplitPlan none{0, 0};
+    unsigned char* extra = static_cast<unsigned char*>(c.ws) +
+                           align_up(workspace_bytes_for(c.B, c.T, c.H, c.K, c.V, N, c.varlen, none));
+    return bwd_layout(extra, w.slots, c.H, c.K, c.V);
+}
+
+// kda_prep with the reverse-pass records, then the forward sweep that keeps
+// every chunk's entering state and V - KG S: with outputs (mode
+// RECUR_FWD_STORE, a forward pass whose backward pass follows) or without
+// (RECUR_STORE, inside the backward pass).
+int run_fwd_states(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, bool outputs,
+                   hipStream_t stream) {
     if (c.ws_bytes < bwd_workspace_bytes(c.B, c.T, c.H, c.K, c.V, N, c.varlen))
         return KDA_ERR_WORKSPACE;
     const WsLayout w = layout(c, N);
     if ((int64_t)N * c.H * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;  // recurrence grids
-    const SplitPlan none{0, 0};
-    unsigned char* extra = static_cast<unsigned char*>(c.ws) +
-                           align_up(workspace_bytes_for(c.B, c.T, c.H, c.K, c.V, N, c.varlen, none));
-    const BwdLayout bl = bwd_layout(extra, w.slots, c.H, c.K, c.V);
+    const BwdLayout bl = bwd_part(c, N, w);
     p.brec = bl.brec;  // kda_prep also writes the reverse-pass records
     int st = run_prep(c, N, p, gdn, stream);
     if (st != KDA_OK) return st;
@@ -344,7 +349,48 @@ int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& 
     r.chunk_off = w.chunk_off;
     r.chunk_state = bl.hs;
     r.chunk_u = bl.zt;
-    kda::launch_recur(r, c.K, stream, kda::RECUR_STORE);
+    if (outputs) {
+        r.o = c.o;
+        r.final_state = c.final_state;
+    }
+    kda::launch_recur(r, c.K, stream, outputs ? kda::RECUR_FWD_STORE : kda::RECUR_STORE);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+// The backward pass: the records and chunk states (recomputed, or left by a
+// forward pass that saved them), the reverse sweep (state gradients, dv,
+// dh0), the chunk gradient kernel and the gate-parameter sums.
+int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& io,
+            bool saved, hipStream_t stream) {
+    if (c.ws_bytes < bwd_workspace_bytes(c.B, c.T, c.H, c.K, c.V, N, c.varlen))
+        return KDA_ERR_WORKSPACE;
+    const WsLayout w = layout(c, N);
+    if ((int64_t)N * c.H * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;  // recurrence grids
+    const BwdLayout bl = bwd_part(c, N, w);
+    if (!saved) {
+        const int st = run_fwd_states(c, N, p, gdn, false, stream);
+        if (st != KDA_OK) return st;
+    } else if (c.varlen) {
+        // the sequence table indexes everything below: rebuilt from
+        // cu_seqlens (clamped in range) rather than trusted from the workspace
+        (void)hipGetLastError();
+        kda::launch_seq_table(c.cu, N, c.T, (int64_t)c.B * c.T, w.seq_start, w.chunk_off, stream);
+    }
+    (void)hipGetLastError();
+    kda::RecurArgs r{};
+    r.v = c.v;
+    r.rec = w.rec;
+    r.initial_state = c.initial_state;
+    r.scale = c.scale;
+    r.H = c.H;
+    r.V = c.V;
+    r.n_seqs = N;
+    r.packed = c.varlen;
+    r.T = c.T;
+    r.seq_start = w.seq_start;
+    r.chunk_off = w.chunk_off;
+    r.chunk_state = bl.hs;
+    r.chunk_u = bl.zt;
     kda::RecurArgs rb = r;
     rb.v = io.d_o;
     rb.rec = bl.brec;
@@ -622,13 +668,15 @@ size_t kda_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_
                     bwd_workspace_bytes(B, T, H, K, V, num_seqs, true));
 }
 
-int kda_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
-            const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
-            float scale, const float* initial_state, const int32_t* cu_seqlens,
-            int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
-            const uint16_t* d_o, const float* d_final, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-            uint16_t* dg, uint16_t* dbeta, float* dA_log, float* ddt_bias, float* dh0,
-            void* workspace, size_t workspace_bytes, void* stream) {
+static int kda_bwd_run(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const uint16_t* g, const uint16_t* beta, const float* A_log,
+                       const float* dt_bias, float lower_bound, float scale,
+                       const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                       int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                       const uint16_t* d_o, const float* d_final, uint16_t* dq, uint16_t* dk,
+                       uint16_t* dv, uint16_t* dg, uint16_t* dbeta, float* dA_log,
+                       float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                       void* stream, bool saved) {
     // dv stands in for the forward output in the shared checks
     Common c{q, k, v, beta, initial_state, nullptr, cu_seqlens, cu_seqlens != nullptr,
              num_seqs, B, T, H, K, V, dv, workspace, workspace_bytes, scale, -1};
@@ -645,15 +693,41 @@ int kda_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
     p.A_log = A_log;
     p.dt_bias = dt_bias;
     p.lower_bound = lower_bound;
-    return run_bwd(c, N, p, false, io, static_cast<hipStream_t>(stream));
+    return run_bwd(c, N, p, false, io, saved, static_cast<hipStream_t>(stream));
 }
 
-int gdn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
-            const uint16_t* beta, float scale, const float* initial_state,
-            const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
-            int32_t K, int32_t V, const uint16_t* d_o, const float* d_final, uint16_t* dq,
-            uint16_t* dk, uint16_t* dv, float* dg, uint16_t* dbeta, float* dh0, void* workspace,
-            size_t workspace_bytes, void* stream) {
+int kda_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+            const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
+            float scale, const float* initial_state, const int32_t* cu_seqlens,
+            int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+            const uint16_t* d_o, const float* d_final, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+            uint16_t* dg, uint16_t* dbeta, float* dA_log, float* ddt_bias, float* dh0,
+            void* workspace, size_t workspace_bytes, void* stream) {
+    return kda_bwd_run(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
+                       cu_seqlens, num_seqs, B, T, H, K, V, d_o, d_final, dq, dk, dv, dg, dbeta,
+                       dA_log, ddt_bias, dh0, workspace, workspace_bytes, stream, false);
+}
+
+int kda_bwd_saved(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                  const uint16_t* beta, const float* A_log, const float* dt_bias,
+                  float lower_bound, float scale, const float* initial_state,
+                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                  int32_t K, int32_t V, const uint16_t* d_o, const float* d_final, uint16_t* dq,
+                  uint16_t* dk, uint16_t* dv, uint16_t* dg, uint16_t* dbeta, float* dA_log,
+                  float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    return kda_bwd_run(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
+                       cu_seqlens, num_seqs, B, T, H, K, V, d_o, d_final, dq, dk, dv, dg, dbeta,
+                       dA_log, ddt_bias, dh0, workspace, workspace_bytes, stream, true);
+}
+
+static int gdn_bwd_run(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                       const uint16_t* beta, float scale, const float* initial_state,
+                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                       int32_t H, int32_t K, int32_t V, const uint16_t* d_o,
+                       const float* d_final, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                       float* dg, uint16_t* dbeta, float* dh0, void* workspace,
+                       size_t workspace_bytes, void* stream, bool saved) {
     Common c{q, k, v, beta, initial_state, nullptr, cu_seqlens, cu_seqlens != nullptr,
              num_seqs, B, T, H, K, V, dv, workspace, workspace_bytes, scale, -1};
     const BwdIO io{d_o, d_final, dq, dk, dv, nullptr, dg, dbeta, nullptr, nullptr, dh0};
@@ -665,7 +739,66 @@ int gdn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
     if (st != KDA_OK) return st;
     kda::PrepArgs p{};
     p.g_gdn = g;
-    return run_bwd(c, N, p, true, io, static_cast<hipStream_t>(stream));
+    return run_bwd(c, N, p, true, io, saved, static_cast<hipStream_t>(stream));
+}
+
+int gdn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+            const uint16_t* beta, float scale, const float* initial_state,
+            const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+            int32_t K, int32_t V, const uint16_t* d_o, const float* d_final, uint16_t* dq,
+            uint16_t* dk, uint16_t* dv, float* dg, uint16_t* dbeta, float* dh0, void* workspace,
+            size_t workspace_bytes, void* stream) {
+    return gdn_bwd_run(q, k, v, g, beta, scale, initial_state, cu_seqlens, num_seqs, B, T, H, K,
+                       V, d_o, d_final, dq, dk, dv, dg, dbeta, dh0, workspace, workspace_bytes,
+                       stream, false);
+}
+
+int gdn_bwd_saved(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                  const uint16_t* beta, float scale, const float* initial_state,
+                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                  int32_t K, int32_t V, const uint16_t* d_o, const float* d_final, uint16_t* dq,
+                  uint16_t* dk, uint16_t* dv, float* dg, uint16_t* dbeta, float* dh0,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    return gdn_bwd_run(q, k, v, g, beta, scale, initial_state, cu_seqlens, num_seqs, B, T, H, K,
+                       V, d_o, d_final, dq, dk, dv, dg, dbeta, dh0, workspace, workspace_bytes,
+                       stream, true);
+}
+
+int kda_fwd_save(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                 const uint16_t* beta, const float* A_log, const float* dt_bias,
+                 float lower_bound, float scale, const float* initial_state, float* final_state,
+                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                 int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, cu_seqlens != nullptr,
+             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale, -1};
+    int st = check_kda_gate(T, g, A_log, dt_bias, lower_bound);
+    if (st != KDA_OK) return st;
+    int32_t N = 0;
+    st = check_common(c, N);
+    if (st != KDA_OK) return st;
+    kda::PrepArgs p{};
+    p.g_kda = g;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.lower_bound = lower_bound;
+    return run_fwd_states(c, N, p, false, true, static_cast<hipStream_t>(stream));
+}
+
+int gdn_fwd_save(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                 const uint16_t* beta, float scale, const float* initial_state, float* final_state,
+                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                 int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, cu_seqlens != nullptr,
+             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale, -1};
+    if (T > 0 && !g) return KDA_ERR_INVALID_ARG;
+    int32_t N = 0;
+    int st = check_common(c, N);
+    if (st != KDA_OK) return st;
+    kda::PrepArgs p{};
+    p.g_gdn = g;
+    return run_fwd_states(c, N, p, true, true, static_cast<hipStream_t>(stream));
 }
 
 const char* kda_status_str(int status) {

@@ -63,8 +63,9 @@ struct RecurArgs {
 
 // kda_recur variants: the forward pass; the forward pass that stores every
 // chunk's entering state and V - KG S instead of outputs; the reverse pass
-// over the backward record (state gradient, dL/dU' and dv).
-enum RecurMode { RECUR_FWD = 0, RECUR_STORE = 1, RECUR_BWD = 2 };
+// over the backward record (state gradient, dL/dU' and dv); the forward pass
+// with its outputs that also stores what the state-store variant stores.
+enum RecurMode { RECUR_FWD = 0, RECUR_STORE = 1, RECUR_BWD = 2, RECUR_FWD_STORE = 3 };
 
 struct DecodeArgs {
     const uint16_t* q;         // [pairs, K] bf16 (pairs = N * H, head fastest)

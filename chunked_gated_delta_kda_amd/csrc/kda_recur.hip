@@ -55,12 +55,17 @@ struct StageLayout {
 // MODE (RecurMode): the forward pass; the forward pass that stores, for the
 // backward pass, each chunk's entering state and V - KG S (no outputs); the
 // reverse pass, which walks the chunks backwards over BRec records with the
-// output gradient in place of V (see kda_bwd.hip).
+// output gradient in place of V (see kda_bwd.hip); the forward pass with its
+// outputs and those stores (a forward pass whose backward pass follows).
 template <int K, int NW, int CT, int NL, int DEPTH, int OCC, int MODE>
 __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
     OCC * (NW + NL) / 4))) void kda_recur_kernel(RecurArgs a) {
     static_assert(DEPTH % 2 == 0 && DEPTH >= 2, "the loop is unrolled by DEPTH and by 2");
-    constexpr bool STORE = MODE == RECUR_STORE, BWD = MODE == RECUR_BWD;
+    constexpr bool BWD = MODE == RECUR_BWD;
+    // SAVE: store each chunk's entering state and V - KG S for the backward
+    // pass; OUT: compute and store the outputs
+    constexpr bool SAVE = MODE == RECUR_STORE || MODE == RECUR_FWD_STORE;
+    constexpr bool OUT = MODE == RECUR_FWD || MODE == RECUR_FWD_STORE;
     using R = Rec<K>;
     using BR = BRec<K>;
     using L = StageLayout<K, NW, CT, NL>;
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
                     sb[ct][j][e] = (bf16)S[ct][2 * j][e];
                     sb[ct][j][4 + e] = (bf16)S[ct][2 * j + 1][e];
                 }
-        if constexpr (STORE) store_state(sb, s0 + c);
+        if constexpr (SAVE) store_state(sb, s0 + c);
         // Y_b = V_b - KG_b S for each 16-token block b
         floatx4 Y[CT][NB];
 #pragma unroll
@@ -368,10 +373,10 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
                 for (int ct = 0; ct < CT; ++ct)
                     Y[ct][bb] = mfma32(f.nkg[bb][j], sb[ct][j], Y[ct][bb]);
         read_nkg_v(f, next);
-        if constexpr (STORE) store_tok(a.chunk_u, Y, s0 + c);
+        if constexpr (SAVE) store_tok(a.chunk_u, Y, s0 + c);
         // O_ob^T = S^T QG_ob^T for each 16-token output block ob
         floatx4 OT[CT][NB];
-        if constexpr (!STORE) {
+        if constexpr (OUT) {
 #pragma unroll
             for (int ob = 0; ob < NB; ++ob)
 #pragma unroll
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) S[ct][t] = mfma_tok(f.kdt[t], uc[ct], S[ct][t]);
         read_kdt(f, next);
-        if constexpr (STORE) return;  // no outputs
+        if constexpr (!OUT) return;  // no outputs
         // + U'^T Aqk^T.  With one block the 16x16x16 product is accumulated apart
         // and added on the VALU: a 16x16x16 MFMA must not take the result of a
         // 16x16x32 MFMA as its accumulator input (that dependent pair gave wrong
@@ -737,6 +742,7 @@ void launch_recur_t(const RecurArgs& a, hipStream_t stream) {
 template <int K>
 void launch_recur_k(const RecurArgs& a, hipStream_t stream, RecurMode mode) {
     if (mode == RECUR_STORE) launch_recur_t<K, RECUR_STORE>(a, stream);
+    else if (mode == RECUR_FWD_STORE) launch_recur_t<K, RECUR_FWD_STORE>(a, stream);
     else if (mode == RECUR_BWD) launch_recur_t<K, RECUR_BWD>(a, stream);
     else launch_recur_t<K, RECUR_FWD>(a, stream);
 }

@@ -246,6 +246,52 @@ int gdn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
             uint16_t* dk, uint16_t* dv, float* dg, uint16_t* dbeta, float* dh0, void* workspace,
             size_t workspace_bytes, void* stream);
 
+/* Training pair: a forward pass that keeps what its backward pass would
+ * recompute, and that backward pass.  Same computation as kda_fwd /
+ * gdn_fwd and kda_bwd / gdn_bwd (results bit for bit equal to theirs); the
+ * pages' training use (cuLA README mirror, section "Usage": o.backward(do)
+ * after the forward call) runs the two back to back on the same inputs.
+ *
+ * *_fwd_save: arguments and outputs as kda_fwd / gdn_fwd (no sequence
+ * splitting), but the workspace must hold *_bwd_workspace_size() bytes: it is
+ * left holding the chunk records, the reverse-pass records and the bf16 state
+ * entering every chunk with V - KG S.
+ * *_bwd_saved: arguments and outputs as kda_bwd / gdn_bwd; the workspace must
+ * be the one a *_fwd_save call on the same inputs, sizes and cu_seqlens filled,
+ * unchanged since, on the same stream (or synchronised with it).  It then runs
+ * only the reverse sweep, the chunk gradients and the gate-parameter sums.
+ * With any other workspace contents the gradients are meaningless, but every
+ * access stays in bounds: the sequence table that indexes the workspace is
+ * rebuilt from cu_seqlens. */
+int kda_fwd_save(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                 const uint16_t* beta, const float* A_log, const float* dt_bias,
+                 float lower_bound, float scale, const float* initial_state, float* final_state,
+                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                 int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+int gdn_fwd_save(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                 const uint16_t* beta, float scale, const float* initial_state, float* final_state,
+                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                 int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+int kda_bwd_saved(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                  const uint16_t* beta, const float* A_log, const float* dt_bias,
+                  float lower_bound, float scale, const float* initial_state,
+                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                  int32_t K, int32_t V, const uint16_t* d_o, const float* d_final, uint16_t* dq,
+                  uint16_t* dk, uint16_t* dv, uint16_t* dg, uint16_t* dbeta, float* dA_log,
+                  float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+int gdn_bwd_saved(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                  const uint16_t* beta, float scale, const float* initial_state,
+                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                  int32_t K, int32_t V, const uint16_t* d_o, const float* d_final, uint16_t* dq,
+                  uint16_t* dk, uint16_t* dv, float* dg, uint16_t* dbeta, float* dh0,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* kda_status_str(int status);
 

@@ -203,3 +203,25 @@ def test_chunk_kda_rejects_unsupported_variants(flag, value):
     with pytest.raises(NotImplementedError, match=flag):
         chunk_kda(x, x, x, x, torch.zeros(1, 4, 1, dtype=torch.bfloat16), torch.zeros(1),
                   torch.zeros(64), **{flag: value})
+
+
+def test_fwd_save_needs_the_backward_workspace(lib):
+    fwd = kda.workspace_size(1, 16, 1, 128, 128)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, 0.088, None, None, None, 0, 1, 16, 1,
+            128, 128, FAKE, FAKE, fwd, None]
+    assert lib.kda_fwd_save(*args) == 3  # enough for kda_fwd only
+    args[3] = None
+    assert lib.kda_fwd_save(*args) == 1  # null g
+    gargs = [FAKE, FAKE, FAKE, None, FAKE, 0.1, None, None, None, 0, 1, 16, 1, 128, 128, FAKE,
+             FAKE, 1 << 30, None]
+    assert lib.gdn_fwd_save(*gargs) == 1  # null g
+
+
+def test_bwd_saved_checks_like_bwd(lib):
+    for over, code in ((dict(dq=None), 1), (dict(K=96), 2), (dict(wsb=4096), 3)):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, lb=-5.0,
+                 scale=0.088, h0=None, cu=None, N=0, B=1, T=16, H=1, K=128, V=128, do=FAKE,
+                 dfin=None, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE, dA=FAKE, ddt=FAKE,
+                 dh0=None, ws=FAKE, wsb=1 << 30, stream=None)
+        a.update(over)
+        assert lib.kda_bwd_saved(*a.values()) == code

@@ -76,3 +76,16 @@ def test_chunk_gdn_backward_is_gdn_bwd():
     for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("g", "dg"), ("beta", "dbeta"),
                       ("initial_state", "dh0")):
         assert torch.equal(args[name].grad, ref[key]), name
+
+
+def test_chunk_kda_backward_twice_with_retained_graph():
+    w, do, dfin = kda_case()
+    q = leaf(w.q)
+    rest = dict(k=leaf(w.k), v=leaf(w.v), g=leaf(w.g), beta=leaf(w.beta), A_log=leaf(w.A_log),
+                dt_bias=leaf(w.dt_bias), initial_state=leaf(w.initial_state))
+    o, _ = chunk_kda(q=q, **rest, scale=w.scale, lower_bound=w.lower_bound)
+    o.backward(do.to(DEV), retain_graph=True)
+    g1 = q.grad.clone()
+    q.grad = None
+    o.backward(do.to(DEV))
+    assert torch.equal(q.grad, g1)

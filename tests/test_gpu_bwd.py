@@ -218,3 +218,40 @@ def test_bwd_empty_sequence_batch():
     r = gpu_bwd(w, do, dfin)
     assert torch.equal(r["dh0"].cpu(), dfin)
     assert torch.count_nonzero(r["dA_log"]) == 0 and torch.count_nonzero(r["ddt_bias"]) == 0
+
+
+@pytest.mark.parametrize("kind", ["kda", "kda packed", "gdn"])
+def test_saved_pair_equals_recompute(kind):
+    """kda_fwd_save + kda_bwd_saved (and the GDN pair) run the same arithmetic as
+    kda_fwd and kda_bwd: outputs, final states and every gradient equal bit for bit."""
+    if kind == "gdn":
+        w = inputs.gdn_workload(2, 150, 2, 128, 128, seed=8100, init_std=0.05)
+    elif kind == "kda packed":
+        w = inputs.kda_workload(1, 0, 2, 128, 128, seed=8200, dt_bias_value=-6.0, init_std=0.05,
+                                lengths=[70, 1, 0, 130])
+    else:
+        w = inputs.kda_workload(2, 200, 2, 128, 128, seed=8300, init_std=0.05)
+    do, dfin = inputs.output_grads(w, seed=8400, dfinal_std=0.05)
+    d = w.to(DEV)
+    do, dfin = do.to(DEV), dfin.to(DEV)
+    cu = d["cu_seqlens"]
+    if kind == "gdn":
+        o1, s1 = kda.gdn_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, d["initial_state"])
+        o2, s2, ws = kda.gdn_fwd_save(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale,
+                                      d["initial_state"])
+        r1 = kda.gdn_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, w.scale, d["initial_state"],
+                         dfin)
+        r2 = kda.gdn_bwd_saved(d["q"], d["k"], d["v"], d["g"], d["beta"], do, ws, w.scale,
+                               d["initial_state"], dfin)
+    else:
+        args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"])
+        o1, s1 = kda.kda_fwd(*args, w.lower_bound, w.scale, d["initial_state"], cu_seqlens=cu)
+        o2, s2, ws = kda.kda_fwd_save(*args, w.lower_bound, w.scale, d["initial_state"],
+                                      cu_seqlens=cu)
+        r1 = kda.kda_bwd(*args, do, w.lower_bound, w.scale, d["initial_state"], dfin, cu)
+        r2 = kda.kda_bwd_saved(*args, do, ws, w.lower_bound, w.scale, d["initial_state"], dfin, cu)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    for name, t in r1.items():
+        if t is not None:
+            assert torch.equal(r2[name], t), name
