@@ -229,6 +229,7 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
 
     // ---- this lane's row and channels: q^, k^, log2 decay; beta
     float qh[KH][8], kh[KH][8], G[KH][8];
+    float xg[KH][8];  // KDA: the gate's pre-activation g + dt_bias, kept for the chain rule
     {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -264,13 +265,16 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
             const int c = 32 * (j0 + jj) + 8 * g;
             float x[8];
             unpack8(*reinterpret_cast<const u32x4*>(a.g_kda + lrow * K + c), x);
+            const floatx4 d0 = *reinterpret_cast<const floatx4*>(a.dt_bias + (int64_t)h * K + c);
+            const floatx4 d1 = *reinterpret_cast<const floatx4*>(a.dt_bias + (int64_t)h * K + c + 4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
+            for (int e = 0; e < 8; ++e) {
+                xg[jj][e] = x[e] + (e < 4 ? d0[e] : d1[e - 4]);
                 // every row (padding rows re-read a real row; the value is
                 // finite) and zeroed on padding rows: no branch per element
-                G[jj][e] = fmaxf(a.lower_bound,
-                                 -rate * softplus_f(x[e] + a.dt_bias[(int64_t)h * K + c + e])) *
-                           LOG2E * (valid ? 1.f : 0.f);
+                G[jj][e] = fmaxf(a.lower_bound, -rate * softplus_f(xg[jj][e])) * LOG2E *
+                           (valid ? 1.f : 0.f);
+            }
         }
     }
     // in-block inclusive prefix (log2), block totals to LDS
@@ -640,11 +644,10 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
         for (int jj = 0; jj < KH; ++jj) {
             const int c0 = 32 * (j0 + jj) + 8 * g;
-            float x[8], dx[8];
-            unpack8(*reinterpret_cast<const u32x4*>(a.g_kda + lrow * K + c0), x);
+            float dx[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float xx = x[e] + a.dt_bias[(int64_t)h * K + c0 + e];
+                const float xx = xg[jj][e];
                 const float pre = -rate * softplus_f(xx);
                 const float da = (valid && pre >= a.lower_bound) ? dla[jj][e] : 0.f;
                 dx[e] = -rate * sigmoid_f(xx) * da;
