@@ -101,7 +101,7 @@ def cpu_baseline(w, budget_s):
     heads_total, done, t_total = w.H, 0, 0.0
     head = 0
     reps = 0
-    while t_total < budget_s and reps < 64:
+    while t_total < budget_s and reps < 1024:
         # one pass over `cores` heads (or all) at a time keeps every core busy
         hs = [(head + i) % heads_total for i in range(min(cores, heads_total))]
         t0 = time.perf_counter()
