@@ -203,7 +203,8 @@ WsLayout layout(const Common& c, int32_t N) {
 // Sequence table and kda_prep: fills the workspace.
 int run_prep(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t stream) {
     const WsLayout w = layout(c, N);
-    if (w.slots > INT32_MAX || (int64_t)N * c.H * 2 > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    // (kda_prep's grid is one-dimensional over chunk slots x heads)
+    if (w.slots * c.H > INT32_MAX || (int64_t)N * c.H * 2 > INT32_MAX) return KDA_ERR_INVALID_ARG;
     (void)hipGetLastError();  // clear a stale error from unrelated work
     if (c.varlen || w.sp.L > 0)  // splitting reads the table for fixed lengths too
         kda::launch_seq_table(c.varlen ? c.cu : nullptr, N, c.T, (int64_t)c.B * c.T,
@@ -366,6 +367,7 @@ int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& 
         return KDA_ERR_WORKSPACE;
     const WsLayout w = layout(c, N);
     if ((int64_t)N * c.H * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;  // recurrence grids
+    if (w.slots * c.H > INT32_MAX) return KDA_ERR_INVALID_ARG;  // chunk-gradient grid
     const BwdLayout bl = bwd_part(c, N, w);
     if (!saved) {
         const int st = run_fwd_states(c, N, p, gdn, false, stream);

@@ -171,8 +171,10 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
     auto& red_s = *reinterpret_cast<float(*)[2][K]>(smem + OFF_W + 4 * K * 4 + NQ * C * 2 * 4);
     auto& alog_s = *reinterpret_cast<float(*)[2 * NQ]>(smem + OFF_W + 6 * K * 4 + NQ * C * 2 * 4);
 
-    const int slot = blockIdx.x;
-    const int h = blockIdx.y;
+    // heads fastest: the workgroups in flight together read and write whole
+    // token rows ([H, K] contiguous) and consecutive chunk states
+    const int slot = blockIdx.x / a.H;
+    const int h = blockIdx.x % a.H;
     const int wave = threadIdx.x >> 6;
     const int blk = wave & 1, hf = wave >> 1;  // token block, channel group
     const int L = threadIdx.x & 63, m = L & 15, g = L >> 4;
@@ -675,7 +677,7 @@ __global__ __launch_bounds__(4 * K) void kda_bwd_chunk_kernel(BwdArgs a) {
 
 template <int K, int V>
 void launch_bwd_chunk_kv(const BwdArgs& a, bool gdn, int n_slots, hipStream_t stream) {
-    const dim3 grid(n_slots, a.H), block(4 * K);
+    const dim3 grid(n_slots * a.H), block(4 * K);
     if (gdn) hipLaunchKernelGGL((kda_bwd_chunk_kernel<K, V, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((kda_bwd_chunk_kernel<K, V, false>), grid, block, 0, stream, a);
 }

@@ -143,14 +143,20 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     __shared__ float beta0_s[16];
     __shared__ float dmax_s[NB];  // per block: sum over rows of the row's largest log2 decay
     __shared__ __attribute__((aligned(16))) float eg_s[NB][K];  // KDA: 2^(block total) per channel
+    // KDA, per block and channel: the factor its KG and QG carry from the
+    // blocks before it and the one its Kd carries from the blocks after it
+    __shared__ __attribute__((aligned(16))) float ebef_s[NB][K];
+    __shared__ __attribute__((aligned(16))) float eaft_s[NB][K];
     // reverse-pass record only: QG^T, nKG^T (layout of KdT), Aqk and Tb rows
     __shared__ __attribute__((aligned(16))) uint16_t qgt_s[BREC ? C * K : 1];
     __shared__ __attribute__((aligned(16))) uint16_t nkgt_s[BREC ? C * K : 1];
     __shared__ __attribute__((aligned(16))) uint16_t aqk_s[BREC ? C * C : 1];  // [r][s]
     __shared__ __attribute__((aligned(16))) uint16_t tb_s[BREC ? C * C : 1];   // [r][s]
 
-    const int slot = blockIdx.x;
-    const int h = blockIdx.y;
+    // heads fastest: the workgroups in flight together read whole token rows
+    // ([H, K] contiguous) rather than one head's 256 bytes of many rows
+    const int slot = blockIdx.x / a.H;
+    const int h = blockIdx.x % a.H;
     const int blk = threadIdx.x >> 6;  // this wave's 16-token block
     const int L = threadIdx.x & 63, m = L & 15, g = L >> 4;
 
@@ -196,17 +202,13 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     const float braw = bf2f(a.beta[lrow]);
     const float graw = GDN ? a.g_gdn[lrow] : 0.f;
     const float rate = GDN ? 0.f : exp2_hw(a.A_log[h] * LOG2E);
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < KS; ++j) {
-        qr[j] = valid ? qr[j] : zero4;
-        kr[j] = valid ? kr[j] : zero4;
-    }
     // beta: KDA logits through the sigmoid, GDN probabilities as given; 0 on padding
     const float b = valid ? (GDN ? braw : sigmoid_f(braw)) : 0.f;
     const float vmask = valid ? 1.f : 0.f;
 
-    // ---- L2 norms: a row's channels live in lanes m, m+16, m+32, m+48
+    // ---- L2 norms: a row's channels live in lanes m, m+16, m+32, m+48.
+    // Padding rows get zero scales, which zeroes every q^ and k^ product
+    // below (their q and k are a real row's, so finite).
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     sq += __shfl_xor(sq, 32, 64);
     sk += __shfl_xor(sk, 16, 64);
     sk += __shfl_xor(sk, 32, 64);
-    const float iq = rsq_hw(sq + NORM_EPS), ik = rsq_hw(sk + NORM_EPS);
+    const float iq = rsq_hw(sq + NORM_EPS) * vmask, ik = rsq_hw(sk + NORM_EPS) * vmask;
 
     // ---- in-block inclusive prefix sums of the log2 decay (padding rows add 0)
     float G[KS][8];  // KDA: per channel; GDN uses G[0][0] as the row's value
@@ -235,6 +237,14 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         G[0][0] = row_scan16(rowmax);
         if (m == 15 && g == 0) gend_s[blk][0] = G[0][0];
     } else {
+        // log2 a = max(lb, -rate softplus(y)) log2(e) with softplus(y) = max(y, 0)
+        // + ln2 log2(1 + 2^(-|y| log2 e)), so (ln2 log2 e = 1)
+        //   log2 a = max(lb log2 e, -rate log2(e) max(y, 0) - rate log2(1 + t)).
+        // On padding rows the three per-row constants are zero, which makes
+        // log2 a = 0 with no per-element mask (y is finite there: the row is a
+        // real row re-read).
+        const float lb2 = a.lower_bound * LOG2E * vmask;
+        const float c1 = -rate * LOG2E * vmask, c2 = -rate * vmask;
         rowmax = -INFINITY;
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
@@ -244,11 +254,9 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
             const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                // computed for every row and zeroed on padding rows by a product
-                // (the value is finite: padding rows re-read a real row, and the
-                // floor bounds it), so the loop has no branch per element
-                const float la =
-                    fmaxf(a.lower_bound, -rate * softplus_f(x[e] + dv[e])) * LOG2E * vmask;
+                const float y = x[e] + dv[e];
+                const float t = exp2_hw(-fabsf(y) * LOG2E);
+                const float la = fmaxf(lb2, fmaf(c1, fmaxf(y, 0.f), c2 * log2_hw(1.f + t)));
                 rowmax = fmaxf(rowmax, la);
                 G[j][e] = la;
             }
@@ -274,6 +282,14 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     if constexpr (!GDN) {
         // 2^(block total) per channel, once per workgroup rather than per row
         for (int c = threadIdx.x; c < NB * K; c += 64 * NB) eg_s[c / K][c % K] = exp2_hw(gend_s[c / K][c % K]);
+        for (int c = threadIdx.x; c < K; c += 64 * NB) {
+            ebef_s[0][c] = 1.f;
+            eaft_s[NB - 1][c] = 1.f;
+            if constexpr (NB == 2) {
+                ebef_s[1][c] = exp2_hw(gend_s[0][c]);
+                eaft_s[0][c] = exp2_hw(gend_s[1][c]);
+            }
+        }
     }
     if (threadIdx.x == 0) {
         float d = 0.f;
@@ -322,12 +338,13 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         } else {
             // the floor bounds every block's |G| by 80 nats, so 2^-G and the
             // per-channel 2^(total) are finite: Kd = (k^ 2^-G) 2^(own total)
-            float eown[8], eoth[8];
+            float eown[8], ebef[8], eaft[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int c = 32 * j + 8 * g + e;
                 eown[e] = eg_s[blk][c];
-                eoth[e] = NB == 2 ? eg_s[NB - 1 - blk][c] : 1.f;
+                ebef[e] = ebef_s[blk][c];
+                eaft[e] = eaft_s[blk][c];
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -339,14 +356,17 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
                 kdl[e] = kil[e] * eown[e];                 // decay to the block's end
                 // global factors: block 1 carries block 0's total decay, block
                 // 0's Kd carries block 1's
-                const float before = (NB == 2 && blk == 1) ? eoth[e] : 1.f;
-                const float after = (NB == 2 && blk == 0) ? eoth[e] : 1.f;
-                kg[e] = kgl[e] * before;
-                qg[e] = qgl[e] * before;
-                kd[e] = kdl[e] * after;
+                kg[e] = kgl[e] * ebef[e];
+                qg[e] = qgl[e] * ebef[e];
+                kd[e] = kdl[e] * eaft[e];
             }
         }
-        *reinterpret_cast<bf16x8*>(rec + R::NKG + ((blk * KS + j) * 64 + L) * 16) = pack8(kg, -1.f);
+        {  // -KG: the sign bits of the packed bf16 flipped (exact)
+            u32x4 w = __builtin_bit_cast(u32x4, pack8(kg));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w[u] ^= 0x80008000u;
+            *reinterpret_cast<u32x4*>(rec + R::NKG + ((blk * KS + j) * 64 + L) * 16) = w;
+        }
         *reinterpret_cast<bf16x8*>(rec + R::QG + ((blk * KS + j) * 64 + L) * 16) = pack8(qg);
         // KdT[t][g'][m'][e'] = Kd[tok(g', e')][rho(t, m')]: transposed through LDS
         // (16-byte units swizzled by st_unit, which the copy-out undoes)
@@ -594,10 +614,10 @@ void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t tota
 template <int K, bool GDN>
 void launch_prep_t(const PrepArgs& a, int n_slots, hipStream_t stream) {
     if (a.brec)
-        hipLaunchKernelGGL((kda_prep_kernel<K, GDN, true>), dim3(n_slots, a.H), dim3(64 * NB), 0,
+        hipLaunchKernelGGL((kda_prep_kernel<K, GDN, true>), dim3(n_slots * a.H), dim3(64 * NB), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((kda_prep_kernel<K, GDN, false>), dim3(n_slots, a.H), dim3(64 * NB), 0,
+        hipLaunchKernelGGL((kda_prep_kernel<K, GDN, false>), dim3(n_slots * a.H), dim3(64 * NB), 0,
                            stream, a);
 }
 
