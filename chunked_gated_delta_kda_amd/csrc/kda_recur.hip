@@ -696,7 +696,24 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
 #ifndef KDA_RECUR_DEPTH2
 #define KDA_RECUR_DEPTH2 2  // two workgroups per CU (fewer registers)
 #endif
+// Grids larger than the CU count (forward pass): four compute waves of one
+// tile (64 value columns per workgroup) and four loader waves, one workgroup
+// per CU.  Each record then serves twice the columns per pass through a CU,
+// which beats two 32-column workgroups sharing the CU; with fewer workgroups
+// than CUs it leaves CUs idle and is slower.
+#ifndef KDA_RECUR_WIDE_WAVES
+#define KDA_RECUR_WIDE_WAVES 4
+#endif
+#ifndef KDA_RECUR_WIDE_LOADERS
+#define KDA_RECUR_WIDE_LOADERS 4
+#endif
+#ifndef KDA_RECUR_WIDE_DEPTH
+#define KDA_RECUR_WIDE_DEPTH 2
+#endif
 constexpr int RECUR_WAVES = KDA_RECUR_WAVES;
+constexpr int RECUR_WIDE_WAVES = KDA_RECUR_WIDE_WAVES;
+constexpr int RECUR_WIDE_LOADERS = KDA_RECUR_WIDE_LOADERS;
+constexpr int RECUR_WIDE_DEPTH = KDA_RECUR_WIDE_DEPTH;
 constexpr int RECUR_TILES = KDA_RECUR_TILES;
 constexpr int RECUR_LOADERS = KDA_RECUR_LOADERS;
 constexpr int RECUR_DEPTH = KDA_RECUR_DEPTH;
@@ -723,9 +740,20 @@ int device_cus() {
 // budget.
 template <int K, int MODE>
 void launch_recur_t(const RecurArgs& a, hipStream_t stream) {
-    const int vs = (a.V + (a.trans_out ? K : 0)) / (16 * RECUR_TILES * RECUR_WAVES);
+    const int cols = a.V + (a.trans_out ? K : 0);
+    const int vs = cols / (16 * RECUR_TILES * RECUR_WAVES);
     const int64_t pairs = (int64_t)a.n_seqs * a.H;
     const int64_t groups = (pairs + 7) / 8;  // the grid covers whole groups of 8 pairs
+    if constexpr (MODE == RECUR_FWD) {
+        if (pairs * vs > device_cus()) {
+            const int vsw = cols / (16 * RECUR_WIDE_WAVES);
+            hipLaunchKernelGGL((kda_recur_kernel<K, RECUR_WIDE_WAVES, 1, RECUR_WIDE_LOADERS,
+                                                 RECUR_WIDE_DEPTH, 1, MODE>),
+                               dim3((unsigned)(groups * 8 * vsw)),
+                               dim3(64 * (RECUR_WIDE_WAVES + RECUR_WIDE_LOADERS)), 0, stream, a);
+            return;
+        }
+    }
     const int64_t blocks = groups * 8 * vs;
     const dim3 grid((unsigned)blocks), block(64 * (RECUR_WAVES + RECUR_LOADERS));
     // (the reverse pass needs the larger register budget in any case)
