@@ -216,6 +216,29 @@ def test_full_config(cfg, heads):
     check_parity(inputs.config(cfg), heads=heads)
 
 
+# Grids with more (sequence, head, 32-column block) workgroups than the 256
+# CUs of an MI355X run the 64-column forward recurrence: ragged lengths, slow
+# decay (the state carries across many chunks) and every head-dim pair, on
+# sampled heads.
+WIDE = [(3, 1000, 48, 128, 128), (5, 700, 40, 64, 64), (2, 1111, 80, 128, 64),
+        (3, 513, 48, 64, 128)]
+
+
+@pytest.mark.parametrize("B,T,H,K,V", WIDE, ids=lambda x: str(x))
+def test_wide_recurrence_grids(B, T, H, K, V):
+    w = inputs.kda_workload(B, T, H, K, V, seed=4500 + T + H, dt_bias_value=-6.0,
+                            init_std=0.05, name=f"wide_B{B}_T{T}_H{H}_K{K}_V{V}")
+    check_parity(w, heads=[0, H // 2 + 1, H - 1], first_tokens=32)
+
+
+def test_wide_recurrence_packed():
+    # 40 packed sequences (one empty, several shorter than a chunk) x 8 heads
+    lengths = [(37 * i) % 301 for i in range(40)]
+    w = inputs.kda_workload(1, 0, 8, 128, 128, seed=4600, dt_bias_value=-6.0,
+                            init_std=0.05, lengths=lengths, name="wide_packed_40x8")
+    check_parity(w, heads=[0, 3, 7], first_tokens=32)
+
+
 def test_stages_equal_fused_call():
     """kda_prep followed by kda_recur (the two ABI stages, as the benchmark times
     them) gives bitwise the same result as kda_fwd; the same for gdn_prep."""
