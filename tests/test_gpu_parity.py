@@ -239,6 +239,13 @@ def test_wide_recurrence_packed():
     check_parity(w, heads=[0, 3, 7], first_tokens=32)
 
 
+def test_wide_recurrence_gdn():
+    # the scalar-gate variant on the same large-grid path (slow decay)
+    w = inputs.gdn_workload(3, 600, 48, 128, 128, seed=4700, init_std=0.05, decay_shift=-6.0,
+                            name="wide_gdn_B3_T600_H48")
+    check_parity(w, heads=[0, 20, 47], first_tokens=32)
+
+
 def test_stages_equal_fused_call():
     """kda_prep followed by kda_recur (the two ABI stages, as the benchmark times
     them) gives bitwise the same result as kda_fwd; the same for gdn_prep."""
