@@ -51,7 +51,7 @@ struct StageLayout {
     static constexpr int PADDED = PPL * LTHREADS * 16;  // LDS bytes per buffer
 };
 
-// OCC: workgroups per CU the register allocation must allow (1 or 2).
+// OCC: workgroups per CU the register allocation must allow (launched with 1).
 // MODE (RecurMode): the forward pass; the forward pass that stores, for the
 // backward pass, each chunk's entering state and V - KG S (no outputs); the
 // reverse pass, which walks the chunks backwards over BRec records with the
@@ -675,12 +675,13 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
 
 // Compute waves per workgroup, 16-column state tiles per compute wave, loader
 // waves, and the loaders' prefetch depth in chunks.  Two compute waves of one
-// tile each give 32 value columns per workgroup, so config-sized batches (64
-// sequence-head pairs x 4 column blocks) fill every CU; with two loader waves
-// there is one wave per SIMD, and the compute waves keep every operand of
-// the next chunk in registers.  The LDS traffic per chunk (each compute wave
-// reads the whole record, the loaders write it once) is what bounds a CU, so
-// more compute waves per workgroup do not help.
+// tile each give 32 value columns per workgroup, so a batch of 64
+// sequence-head pairs (4 column blocks each at V = 128) fills every CU; with
+// two loader waves there is one wave per SIMD, and the compute waves keep
+// every operand of the next chunk in registers.  A CU's pace is set by the
+// record bytes it loads per chunk; more columns per workgroup amortise them
+// but leave CUs idle unless the grid exceeds the CU count (the wide form
+// below).
 #ifndef KDA_RECUR_WAVES
 #define KDA_RECUR_WAVES 2
 #endif
@@ -691,10 +692,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
 #define KDA_RECUR_LOADERS 2
 #endif
 #ifndef KDA_RECUR_DEPTH
-#define KDA_RECUR_DEPTH 4  // one workgroup per CU
-#endif
-#ifndef KDA_RECUR_DEPTH2
-#define KDA_RECUR_DEPTH2 2  // two workgroups per CU (fewer registers)
+#define KDA_RECUR_DEPTH 4
 #endif
 // Grids larger than the CU count (forward pass): four compute waves of one
 // tile (64 value columns per workgroup) and four loader waves, one workgroup
@@ -717,7 +715,6 @@ constexpr int RECUR_WIDE_DEPTH = KDA_RECUR_WIDE_DEPTH;
 constexpr int RECUR_TILES = KDA_RECUR_TILES;
 constexpr int RECUR_LOADERS = KDA_RECUR_LOADERS;
 constexpr int RECUR_DEPTH = KDA_RECUR_DEPTH;
-constexpr int RECUR_DEPTH2 = KDA_RECUR_DEPTH2;
 
 // Compute units of the current device (queried once per device).
 int device_cus() {
@@ -734,10 +731,10 @@ int device_cus() {
     return cus[dev];
 }
 
-// A grid with more workgroups than CUs runs the variant whose registers
-// allow two workgroups per CU (the chain of each is latency-bound, so two
-// interleave well); up to one per CU, the variant with the larger register
-// budget.
+// One workgroup per CU in every mode.  Forward grids beyond the CU count run
+// the wide form (64 columns per workgroup); the other modes queue their
+// extra workgroups for free CUs (a register budget for two resident per CU
+// spilled 60-80 registers in the state-storing modes and was 30% slower).
 template <int K, int MODE>
 void launch_recur_t(const RecurArgs& a, hipStream_t stream) {
     const int cols = a.V + (a.trans_out ? K : 0);
@@ -754,17 +751,10 @@ void launch_recur_t(const RecurArgs& a, hipStream_t stream) {
             return;
         }
     }
-    const int64_t blocks = groups * 8 * vs;
-    const dim3 grid((unsigned)blocks), block(64 * (RECUR_WAVES + RECUR_LOADERS));
-    // (the reverse pass needs the larger register budget in any case)
-    if (MODE != RECUR_BWD && pairs * vs > device_cus())
-        hipLaunchKernelGGL((kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS,
-                                             RECUR_DEPTH2, 2, MODE>),
-                           grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS,
-                                             RECUR_DEPTH, 1, MODE>),
-                           grid, block, 0, stream, a);
+    hipLaunchKernelGGL((kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS, RECUR_DEPTH,
+                                         1, MODE>),
+                       dim3((unsigned)(groups * 8 * vs)),
+                       dim3(64 * (RECUR_WAVES + RECUR_LOADERS)), 0, stream, a);
 }
 
 template <int K>
