@@ -202,6 +202,16 @@ def test_bwd_config1_sampled_heads():
     check_bwd(w, do, dfin, heads=[0, 13, 31])
 
 
+def test_bwd_grid_beyond_cus():
+    """More (sequence, head, column block) workgroups than the 256 CUs (the
+    recurrences queue the rest), ragged lengths, slow decay; the oracle on
+    three heads."""
+    w = inputs.kda_workload(3, 700, 40, 128, 128, seed=7950, dt_bias_value=-6.0,
+                            init_std=0.05)
+    do, dfin = inputs.output_grads(w, seed=7951, dfinal_std=0.05)
+    check_bwd(w, do, dfin, heads=[0, 17, 39])
+
+
 def test_bwd_deterministic():
     w = inputs.kda_workload(1, 400, 2, 128, 128, seed=8000, dt_bias_value=-6.0, init_std=0.05)
     do, dfin = inputs.output_grads(w, seed=8001, dfinal_std=0.05)
