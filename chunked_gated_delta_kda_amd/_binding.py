@@ -19,7 +19,7 @@ _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED"
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_fwd", "gdn_fwd", "kda_fwd_workspace_size", "gdn_fwd_workspace_size",
            "kda_fwd_split_workspace_size", "kda_fwd_split", "gdn_fwd_split", "kda_prep",
-           "gdn_prep", "kda_recur", "kda_decode", "gdn_decode", "kda_bwd_workspace_size",
+           "gdn_prep", "kda_recur", "kda_prep_timed", "kda_recur_timed", "kda_decode", "gdn_decode", "kda_bwd_workspace_size",
            "kda_bwd", "gdn_bwd", "kda_fwd_save", "gdn_fwd_save", "kda_bwd_saved",
            "gdn_bwd_saved", "kda_status_str", "kda_version")
 
@@ -81,6 +81,11 @@ def load(path: Path | str | None = None):
     lib.gdn_bwd.restype = ctypes.c_int
     lib.gdn_bwd.argtypes = [u16p, u16p, u16p, f32p, u16p, f32, f32p, i32p, i32, i32, i32, i32,
                             i32, i32, u16p, f32p, u16p, u16p, u16p, f32p, u16p, f32p, vp, sz, vp]
+    # the measurement forms of the stages take two event handles more
+    lib.kda_prep_timed.restype = ctypes.c_int
+    lib.kda_prep_timed.argtypes = lib.kda_prep.argtypes + [vp, vp]
+    lib.kda_recur_timed.restype = ctypes.c_int
+    lib.kda_recur_timed.argtypes = lib.kda_recur.argtypes + [vp, vp]
     # the training pair shares the signatures of kda_fwd / gdn_fwd and kda_bwd / gdn_bwd
     for a, b in (("kda_fwd_save", "kda_fwd"), ("gdn_fwd_save", "gdn_fwd"),
                  ("kda_bwd_saved", "kda_bwd"), ("gdn_bwd_saved", "gdn_bwd")):
@@ -311,14 +316,29 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
-def kda_prep(q, k, g, beta, A_log, dt_bias, lower_bound, workspace, cu_seqlens=None, V=None):
-    """Token-parallel stage only: fills ``workspace`` (see kda_recur)."""
+def _events(events):
+    """(start, stop) torch.cuda.Event pair (timing enabled, recorded once so the
+    underlying events exist) -> two raw handles; None -> two NULLs."""
+    if events is None:
+        return ctypes.c_void_p(0), ctypes.c_void_p(0)
+    start, stop = events
+    if not start.cuda_event or not stop.cuda_event:
+        raise ValueError("record() each event once before passing it (the handle is created then)")
+    return ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event)
+
+
+def kda_prep(q, k, g, beta, A_log, dt_bias, lower_bound, workspace, cu_seqlens=None, V=None,
+             events=None):
+    """Token-parallel stage only: fills ``workspace`` (see kda_recur).  ``events``
+    = (start, stop) torch.cuda.Event: the record kernel's own start and end are
+    recorded into them (kda_prep_timed)."""
     B, T, H, K = q.shape
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     stream = ctypes.c_void_p(_torch().cuda.current_stream(q.device).cuda_stream)
-    _check(load().kda_prep(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
-                           float(lower_bound), _ptr(cu_seqlens), N, B, T, H, K, V or K,
-                           _ptr(workspace), _nbytes(workspace), stream))
+    _check(load().kda_prep_timed(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(A_log),
+                                 _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), N, B, T, H,
+                                 K, V or K, _ptr(workspace), _nbytes(workspace), stream,
+                                 *_events(events)))
 
 
 def gdn_prep(q, k, g, beta, workspace, cu_seqlens=None, V=None):
@@ -329,16 +349,19 @@ def gdn_prep(q, k, g, beta, workspace, cu_seqlens=None, V=None):
                            K, V or K, _ptr(workspace), _nbytes(workspace), stream))
 
 
-def kda_recur(v, K, scale, workspace, out, initial_state=None, final_out=None, num_seqs=None):
+def kda_recur(v, K, scale, workspace, out, initial_state=None, final_out=None, num_seqs=None,
+              events=None):
     """Head-parallel stage only: reads the workspace of the preceding prep call
-    (same sizes and packing; ``num_seqs`` set for packed sequences)."""
+    (same sizes and packing; ``num_seqs`` set for packed sequences).  ``events``
+    as for kda_prep (kda_recur_timed: the recurrence kernel's start and end)."""
     B, T, H, V = v.shape
     varlen = num_seqs is not None
     N = num_seqs if varlen else B
     stream = ctypes.c_void_p(_torch().cuda.current_stream(v.device).cuda_stream)
-    _check(load().kda_recur(_ptr(v), float(scale), _ptr(initial_state), _ptr(final_out),
-                            1 if varlen else 0, N, B, T, H, K, V, _ptr(out), _ptr(workspace),
-                            _nbytes(workspace), stream))
+    _check(load().kda_recur_timed(_ptr(v), float(scale), _ptr(initial_state), _ptr(final_out),
+                                  1 if varlen else 0, N, B, T, H, K, V, _ptr(out),
+                                  _ptr(workspace), _nbytes(workspace), stream,
+                                  *_events(events)))
 
 
 def _decode_prepare(q, k, v, beta, scale, state, state_out, out):

@@ -201,7 +201,8 @@ WsLayout layout(const Common& c, int32_t N) {
 }
 
 // Sequence table and kda_prep: fills the workspace.
-int run_prep(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t stream) {
+int run_prep(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t stream,
+             const kda::LaunchEvents* ev = nullptr) {
     const WsLayout w = layout(c, N);
     // (kda_prep's grid is one-dimensional over chunk slots x heads)
     if (w.slots * c.H > INT32_MAX || (int64_t)N * c.H * 2 > INT32_MAX) return KDA_ERR_INVALID_ARG;
@@ -220,14 +221,21 @@ int run_prep(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t 
     p.chunk_off = w.chunk_off;
     p.rec = w.rec;
     p.bound = w.bound;
-    if (w.slots > 0) kda::launch_prep(p, c.K, gdn, (int)w.slots, stream);
+    if (w.slots > 0) {
+        kda::launch_prep(p, c.K, gdn, (int)w.slots, stream, ev);
+    } else if (ev) {  // no kernel: the events still mark this point of the stream
+        (void)hipEventRecord(ev->start, stream);
+        (void)hipEventRecord(ev->stop, stream);
+    }
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 // kda_recur: consumes the workspace.  With splitting: the segment table, the
 // first pass over all segments (results from a zero start and, where not
 // negligible, transitions), the scan over segments and the second pass.
-int run_recur(const Common& c, int32_t N, hipStream_t stream) {
+// ev (measurement events) applies to the unsplit recurrence only.
+int run_recur(const Common& c, int32_t N, hipStream_t stream,
+              const kda::LaunchEvents* ev = nullptr) {
     const WsLayout w = layout(c, N);
     if ((int64_t)N * c.H * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;
     (void)hipGetLastError();
@@ -246,9 +254,10 @@ int run_recur(const Common& c, int32_t N, hipStream_t stream) {
     r.seq_start = w.seq_start;
     r.chunk_off = w.chunk_off;
     if (w.sp.L == 0) {
-        kda::launch_recur(r, c.K, stream);
+        kda::launch_recur(r, c.K, stream, kda::RECUR_FWD, ev);
         return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
     }
+    if (ev) return KDA_ERR_INVALID_ARG;
     const int32_t nv = (int32_t)w.sp.n_virt;
     if ((int64_t)nv * c.H * 8 > INT32_MAX) return KDA_ERR_INVALID_ARG;
     kda::launch_seg_table(w.seq_start, w.chunk_off, N, w.sp.L, nv, w.vseq_start, w.vchunk_off,
@@ -573,10 +582,15 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
                          num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, 0, stream);
 }
 
-int kda_prep(const uint16_t* q, const uint16_t* k, const uint16_t* g, const uint16_t* beta,
-             const float* A_log, const float* dt_bias, float lower_bound,
-             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
-             int32_t K, int32_t V, void* workspace, size_t workspace_bytes, void* stream) {
+int kda_prep_timed(const uint16_t* q, const uint16_t* k, const uint16_t* g,
+                   const uint16_t* beta, const float* A_log, const float* dt_bias,
+                   float lower_bound, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                   int32_t T, int32_t H, int32_t K, int32_t V, void* workspace,
+                   size_t workspace_bytes, void* stream, void* start_event, void* stop_event) {
+    const bool timed = start_event || stop_event;
+    if (timed && !(start_event && stop_event)) return KDA_ERR_INVALID_ARG;
+    const kda::LaunchEvents ev{static_cast<hipEvent_t>(start_event),
+                               static_cast<hipEvent_t>(stop_event)};
     // v and o are not touched by this stage; stand-ins satisfy the shared checks
     Common c{q, k, q, beta, nullptr, nullptr, cu_seqlens, cu_seqlens != nullptr, num_seqs, B,
              T, H, K, V, const_cast<uint16_t*>(q), workspace, workspace_bytes, 1.f, -1};
@@ -590,7 +604,15 @@ int kda_prep(const uint16_t* q, const uint16_t* k, const uint16_t* g, const uint
     p.A_log = A_log;
     p.dt_bias = dt_bias;
     p.lower_bound = lower_bound;
-    return run_prep(c, N, p, false, static_cast<hipStream_t>(stream));
+    return run_prep(c, N, p, false, static_cast<hipStream_t>(stream), timed ? &ev : nullptr);
+}
+
+int kda_prep(const uint16_t* q, const uint16_t* k, const uint16_t* g, const uint16_t* beta,
+             const float* A_log, const float* dt_bias, float lower_bound,
+             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+             int32_t K, int32_t V, void* workspace, size_t workspace_bytes, void* stream) {
+    return kda_prep_timed(q, k, g, beta, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs, B, T,
+                          H, K, V, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 int gdn_prep(const uint16_t* q, const uint16_t* k, const float* g, const uint16_t* beta,
@@ -607,16 +629,28 @@ int gdn_prep(const uint16_t* q, const uint16_t* k, const float* g, const uint16_
     return run_prep(c, N, p, true, static_cast<hipStream_t>(stream));
 }
 
-int kda_recur(const uint16_t* v, float scale, const float* initial_state, float* final_state,
-              int32_t varlen, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
-              int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes, void* stream) {
+int kda_recur_timed(const uint16_t* v, float scale, const float* initial_state,
+                    float* final_state, int32_t varlen, int32_t num_seqs, int32_t B, int32_t T,
+                    int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                    size_t workspace_bytes, void* stream, void* start_event, void* stop_event) {
+    const bool timed = start_event || stop_event;
+    if (timed && !(start_event && stop_event)) return KDA_ERR_INVALID_ARG;
+    const kda::LaunchEvents ev{static_cast<hipEvent_t>(start_event),
+                               static_cast<hipEvent_t>(stop_event)};
     // q, k, beta are not read by this stage; v stands in for them in the shared checks
     Common c{v, v, v, v, initial_state, final_state, nullptr, varlen != 0, num_seqs, B, T, H,
              K, V, o, workspace, workspace_bytes, scale, -1};
     int32_t N = 0;
     int st = check_common(c, N);
     if (st != KDA_OK) return st;
-    return run_recur(c, N, static_cast<hipStream_t>(stream));
+    return run_recur(c, N, static_cast<hipStream_t>(stream), timed ? &ev : nullptr);
+}
+
+int kda_recur(const uint16_t* v, float scale, const float* initial_state, float* final_state,
+              int32_t varlen, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
+              int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes, void* stream) {
+    return kda_recur_timed(v, scale, initial_state, final_state, varlen, num_seqs, B, T, H, K, V,
+                           o, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 int kda_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,

@@ -142,8 +142,18 @@ void launch_seg_table(const int32_t* seq_start, const int32_t* chunk_off, int32_
 void launch_split_scan(const SplitScanArgs& a, int K, hipStream_t stream);
 void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t total_tokens,
                       int32_t* seq_start, int32_t* chunk_off, hipStream_t stream);
-void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream);
-void launch_recur(const RecurArgs& a, int K, hipStream_t stream, RecurMode mode = RECUR_FWD);
+// Measurement events for a stage's main kernel (both non-null or ev null):
+// the kernel is then launched with hipExtLaunchKernel, which records its own
+// start and end on the GPU into the two events.
+struct LaunchEvents {
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+
+void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream,
+                 const LaunchEvents* ev = nullptr);
+void launch_recur(const RecurArgs& a, int K, hipStream_t stream, RecurMode mode = RECUR_FWD,
+                  const LaunchEvents* ev = nullptr);
 void launch_decode(const DecodeArgs& a, int K, bool gdn, hipStream_t stream);
 int record_bytes(int K);
 

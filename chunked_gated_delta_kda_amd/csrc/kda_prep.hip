@@ -14,6 +14,8 @@
 // parameter table of the same page (section "FlashKDA의 KDA 연산 구조"); the
 // chunk size and the exact 16x16 inverse follow its section "Flash Linear
 // Attention과 비교".
+#include <hip/hip_ext.h>
+
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -612,22 +614,24 @@ void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t tota
 }
 
 template <int K, bool GDN>
-void launch_prep_t(const PrepArgs& a, int n_slots, hipStream_t stream) {
-    if (a.brec)
-        hipLaunchKernelGGL((kda_prep_kernel<K, GDN, true>), dim3(n_slots * a.H), dim3(64 * NB), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((kda_prep_kernel<K, GDN, false>), dim3(n_slots * a.H), dim3(64 * NB), 0,
-                           stream, a);
+void launch_prep_t(const PrepArgs& a, int n_slots, hipStream_t stream, const LaunchEvents* ev) {
+    const dim3 grid(n_slots * a.H), block(64 * NB);
+    auto go = [&](auto kernel) {
+        if (ev) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev->start, ev->stop, 0, a);
+        else hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
+    };
+    if (a.brec) go(kda_prep_kernel<K, GDN, true>);
+    else go(kda_prep_kernel<K, GDN, false>);
 }
 
-void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream) {
+void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t stream,
+                 const LaunchEvents* ev) {
     if (K == 128) {
-        if (gdn) launch_prep_t<128, true>(a, n_slots, stream);
-        else launch_prep_t<128, false>(a, n_slots, stream);
+        if (gdn) launch_prep_t<128, true>(a, n_slots, stream, ev);
+        else launch_prep_t<128, false>(a, n_slots, stream, ev);
     } else {
-        if (gdn) launch_prep_t<64, true>(a, n_slots, stream);
-        else launch_prep_t<64, false>(a, n_slots, stream);
+        if (gdn) launch_prep_t<64, true>(a, n_slots, stream, ev);
+        else launch_prep_t<64, false>(a, n_slots, stream, ev);
     }
 }
 

@@ -31,6 +31,8 @@
 //   compute waves: during iteration c they compute chunk c and read the
 //     critical-path operands of chunk c + 1 (nKG, Tb, V) into registers.
 // One barrier per chunk separates the iterations.
+#include <hip/hip_ext.h>
+
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -735,8 +737,17 @@ int device_cus() {
 // the wide form (64 columns per workgroup); the other modes queue their
 // extra workgroups for free CUs (a register budget for two resident per CU
 // spilled 60-80 registers in the state-storing modes and was 30% slower).
+template <class F>
+void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t stream, const LaunchEvents* ev,
+                   const RecurArgs& a) {
+    if (ev)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev->start, ev->stop, 0, a);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
+}
+
 template <int K, int MODE>
-void launch_recur_t(const RecurArgs& a, hipStream_t stream) {
+void launch_recur_t(const RecurArgs& a, hipStream_t stream, const LaunchEvents* ev) {
     const int cols = a.V + (a.trans_out ? K : 0);
     const int vs = cols / (16 * RECUR_TILES * RECUR_WAVES);
     const int64_t pairs = (int64_t)a.n_seqs * a.H;
@@ -744,30 +755,31 @@ void launch_recur_t(const RecurArgs& a, hipStream_t stream) {
     if constexpr (MODE == RECUR_FWD) {
         if (pairs * vs > device_cus()) {
             const int vsw = cols / (16 * RECUR_WIDE_WAVES);
-            hipLaunchKernelGGL((kda_recur_kernel<K, RECUR_WIDE_WAVES, 1, RECUR_WIDE_LOADERS,
-                                                 RECUR_WIDE_DEPTH, 1, MODE>),
-                               dim3((unsigned)(groups * 8 * vsw)),
-                               dim3(64 * (RECUR_WIDE_WAVES + RECUR_WIDE_LOADERS)), 0, stream, a);
+            launch_kernel(kda_recur_kernel<K, RECUR_WIDE_WAVES, 1, RECUR_WIDE_LOADERS,
+                                           RECUR_WIDE_DEPTH, 1, MODE>,
+                          dim3((unsigned)(groups * 8 * vsw)),
+                          dim3(64 * (RECUR_WIDE_WAVES + RECUR_WIDE_LOADERS)), stream, ev, a);
             return;
         }
     }
-    hipLaunchKernelGGL((kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS, RECUR_DEPTH,
-                                         1, MODE>),
-                       dim3((unsigned)(groups * 8 * vs)),
-                       dim3(64 * (RECUR_WAVES + RECUR_LOADERS)), 0, stream, a);
+    launch_kernel(kda_recur_kernel<K, RECUR_WAVES, RECUR_TILES, RECUR_LOADERS, RECUR_DEPTH, 1, MODE>,
+                  dim3((unsigned)(groups * 8 * vs)), dim3(64 * (RECUR_WAVES + RECUR_LOADERS)),
+                  stream, ev, a);
 }
 
 template <int K>
-void launch_recur_k(const RecurArgs& a, hipStream_t stream, RecurMode mode) {
-    if (mode == RECUR_STORE) launch_recur_t<K, RECUR_STORE>(a, stream);
-    else if (mode == RECUR_FWD_STORE) launch_recur_t<K, RECUR_FWD_STORE>(a, stream);
-    else if (mode == RECUR_BWD) launch_recur_t<K, RECUR_BWD>(a, stream);
-    else launch_recur_t<K, RECUR_FWD>(a, stream);
+void launch_recur_k(const RecurArgs& a, hipStream_t stream, RecurMode mode,
+                    const LaunchEvents* ev) {
+    if (mode == RECUR_STORE) launch_recur_t<K, RECUR_STORE>(a, stream, ev);
+    else if (mode == RECUR_FWD_STORE) launch_recur_t<K, RECUR_FWD_STORE>(a, stream, ev);
+    else if (mode == RECUR_BWD) launch_recur_t<K, RECUR_BWD>(a, stream, ev);
+    else launch_recur_t<K, RECUR_FWD>(a, stream, ev);
 }
 
-void launch_recur(const RecurArgs& a, int K, hipStream_t stream, RecurMode mode) {
-    if (K == 128) launch_recur_k<128>(a, stream, mode);
-    else launch_recur_k<64>(a, stream, mode);
+void launch_recur(const RecurArgs& a, int K, hipStream_t stream, RecurMode mode,
+                  const LaunchEvents* ev) {
+    if (K == 128) launch_recur_k<128>(a, stream, mode, ev);
+    else launch_recur_k<64>(a, stream, mode, ev);
 }
 
 }  // namespace kda

@@ -172,6 +172,28 @@ int kda_recur(const uint16_t* v, float scale, const float* initial_state, float*
               int32_t varlen, int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K,
               int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Measurement forms of the two stages: exactly kda_prep and kda_recur (same
+ * arguments, same work, same results), plus two events.  start_event and
+ * stop_event are hipEvent_t handles the caller created with timing enabled
+ * (for instance those of torch.cuda.Event(enable_timing=True) after a first
+ * record()); the stage's main kernel (the record kernel; the recurrence
+ * kernel) is launched with hipExtLaunchKernel, which records that kernel's
+ * own start and end on the GPU into them, so hipEventElapsedTime gives its
+ * execution time without the dispatch gap that events recorded between
+ * kernels include.  With no token (no kernel) both events are recorded at
+ * that point of the stream.  Both NULL: the plain stage.  Exactly one NULL:
+ * KDA_ERR_INVALID_ARG.  The events are only written, never owned or freed. */
+int kda_prep_timed(const uint16_t* q, const uint16_t* k, const uint16_t* g,
+                   const uint16_t* beta, const float* A_log, const float* dt_bias,
+                   float lower_bound, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                   int32_t T, int32_t H, int32_t K, int32_t V, void* workspace,
+                   size_t workspace_bytes, void* stream, void* start_event, void* stop_event);
+
+int kda_recur_timed(const uint16_t* v, float scale, const float* initial_state,
+                    float* final_state, int32_t varlen, int32_t num_seqs, int32_t B, int32_t T,
+                    int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                    size_t workspace_bytes, void* stream, void* start_event, void* stop_event);
+
 /* One recurrent step per sequence: the single-token form of the same
  * recurrence, for decoding after a prefill (the cuLA pages list decode
  * kernels on their inference roadmap: cuLA blog, section "Status &

@@ -225,3 +225,21 @@ def test_bwd_saved_checks_like_bwd(lib):
                  dh0=None, ws=FAKE, wsb=1 << 30, stream=None)
         a.update(over)
         assert lib.kda_bwd_saved(*a.values()) == code
+
+
+def test_timed_stages_need_both_events_or_none(lib):
+    """kda_prep_timed / kda_recur_timed: exactly one event handle is rejected on the
+    host (before any HIP call); the other checks are those of the plain stages."""
+    ev = ctypes.c_void_p(0x2000)
+    prep = lambda s, e: lib.kda_prep_timed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, None, 0, 1,
+                                           16, 1, 128, 128, FAKE, 1 << 30, None, s, e)
+    recur = lambda s, e: lib.kda_recur_timed(FAKE, 0.088, None, None, 0, 0, 1, 16, 1, 128, 128,
+                                             FAKE, FAKE, 1 << 30, None, s, e)
+    for call in (prep, recur):
+        assert call(ev, None) == 1
+        assert call(None, ev) == 1
+    # plain-stage checks still apply with both events given
+    assert lib.kda_recur_timed(FAKE, 0.088, None, None, 0, 0, 1, 16, 1, 96, 128, FAKE, FAKE,
+                               1 << 30, None, ev, ev) == 2
+    assert lib.kda_prep_timed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, None, 0, 1, 16, 1, 128,
+                              128, None, 1 << 30, None, ev, ev) == 3

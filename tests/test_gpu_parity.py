@@ -266,3 +266,34 @@ def test_stages_equal_fused_call():
                       num_seqs=None if w.cu_seqlens is None else w.n_seqs)
         torch.cuda.synchronize()
         assert torch.equal(o, o2) and torch.equal(S, S2)
+
+
+def test_timed_stages_equal_plain_stages():
+    """kda_prep_timed and kda_recur_timed (the measurement forms) give bitwise the
+    results of the plain stages and record positive kernel times into the events;
+    with packed sequences too, and with the wide recurrence (grid beyond the CUs)."""
+    for w in (inputs.kda_workload(2, 300, 3, 128, 128, seed=4800, init_std=0.05),
+              inputs.kda_workload(1, 0, 4, 64, 128, seed=4801, lengths=[70, 0, 33, 1]),
+              inputs.kda_workload(3, 200, 48, 128, 128, seed=4802, init_std=0.05)):
+        o, S = gpu_run(w)
+        d = w.to("cuda:0")
+        ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.K, w.V, w.n_seqs),
+                         dtype=torch.uint8, device="cuda:0")
+        stream = torch.cuda.current_stream()
+        ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for n in ("prep", "recur")}
+        for pair in ev.values():
+            for x in pair:
+                x.record(stream)
+        kda.kda_prep(d["q"], d["k"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
+                     w.lower_bound, ws, d["cu_seqlens"], V=w.V, events=ev["prep"])
+        o2 = torch.empty_like(o)
+        S2 = torch.empty_like(S)
+        kda.kda_recur(d["v"], w.K, w.scale, ws, o2, d["initial_state"], S2,
+                      num_seqs=None if w.cu_seqlens is None else w.n_seqs, events=ev["recur"])
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(S, S2)
+        for name, (a, b) in ev.items():
+            ms = a.elapsed_time(b)
+            say(f"  {w.name} {name}: {ms * 1e3:.1f} us")
+            assert 0.0 < ms < 1000.0, (name, ms)
