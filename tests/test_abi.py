@@ -243,3 +243,12 @@ def test_timed_stages_need_both_events_or_none(lib):
                                1 << 30, None, ev, ev) == 2
     assert lib.kda_prep_timed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, None, 0, 1, 16, 1, 128,
                               128, None, 1 << 30, None, ev, ev) == 3
+
+
+def test_prep_grid_limit_checked_on_host(lib):
+    """kda_prep's grid is one-dimensional over chunk slots x heads: a batch whose
+    slots x heads exceeds 2^31 - 1 is rejected before any launch (2^19 slots x
+    8192 heads here; the workspace size passed is large enough to get there)."""
+    st = lib.kda_prep(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, None, 0, 1, 1 << 24, 8192, 64,
+                      64, FAKE, 1 << 62, None)
+    assert st == 1
