@@ -1,21 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the chunked KDA forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1|2|3|4]
 
-Workload: KDA forward, B=2, T=2048, H=32, K=V=128, bf16 q/k/v/g/beta, fp32
-initial and final states (seeded synthetic inputs, chunked_gated_delta_kda_amd.
-inputs.config(1)).  One step = one full forward pass (kda_prep then
-kda_recur, the two stages of kda_fwd) over one batch whose inputs are already
-resident in HBM.  Several input sets are rotated so that no step finds its
-inputs in the 256 MB last-level cache.  Prints one JSON line.
+Default workload: KDA forward, B=2, T=2048, H=32, K=V=128, bf16
+q/k/v/g/beta, fp32 initial and final states (seeded synthetic inputs,
+chunked_gated_delta_kda_amd.inputs.config(1)).  One step = one full forward
+pass over one batch whose inputs are already resident in HBM.  Several input
+sets are rotated so that no step finds its inputs in the 256 MB last-level
+cache.  Prints one JSON line.
 
-Roofline: per-kernel durations come from HIP events recorded on the launch
-stream around each stage inside the timed region (on a sample of the steps:
-an event between the two kernels would lengthen every step); the dominant kernel's
-algorithmic bytes (what it must read and write, see below) over its average
-duration is compared with 8 TB/s.  Traffic measured with rocprofv3 counters
-is read from profiles/ when it was taken on the current kernel sources.
+Roofline: the method's compulsory bytes (inputs read once, outputs and states
+written once: 6K + 4V + 2 bytes per token-head for KDA, plus the states) over
+the measured time, against 8 TB/s -- for the whole step (``path``) and for the
+dominant kernel on its share of those bytes (``roofline``).  Kernel durations
+come from HIP events that the kernel launch itself records, on the launch
+stream, inside the timed steps.  The bytes each kernel moves by its own design
+(``traffic_design``) and the HBM traffic measured with rocprofv3 counters
+(``traffic``, read from profiles/ only when it was taken on the current kernel
+sources) are reported beside it.
 """
 from __future__ import annotations
 
@@ -55,23 +58,43 @@ def source_digest(names=None) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(B, T, H, K, V, N, init=True, final=True):
-    """Compulsory HBM bytes of the method and of each kernel, for T a multiple of
-    the chunk.  The per-(chunk, head) record holds nKG, QG and KdT (C x K bf16
-    each), Aqk and Tb (C x C bf16 each) and Gamma_C (K fp32): 29184 B at K = 128."""
-    th = B * T * H
-    states = N * H * K * V * 4 * ((1 if init else 0) + (1 if final else 0))
-    rec_per_th = (3 * C * K * 2 + 2 * C * C * 2 + K * 4) / C
-    path = th * (2 * K + 2 * K + 2 * K + 2 * V + 2 + 2 * V) + states  # q k g v beta o
-    prep = th * (3 * 2 * K + 2 + rec_per_th) + H * 4 + H * K * 4
-    recur = th * (rec_per_th + 2 * V + 2 * V) + states
-    return dict(path=path, kda_prep=prep, kda_recur=recur)
+def method_bytes(w):
+    """Compulsory HBM bytes of the method on workload ``w`` (inputs read once,
+    outputs written once, no intermediates), split by what each stage of the
+    two-stage path touches: the token-parallel stage reads q, k, g, beta (and
+    the per-head gate parameters), the recurrence reads v and the states and
+    writes o and the final states.  KDA: 6K + 4V + 2 bytes per token-head; GDN
+    (fp32 log decay, bf16 beta): 4K + 4V + 6."""
+    th = w.B * w.T * w.H
+    K, V, H, N = w.K, w.V, w.H, w.n_seqs
+    states = N * H * K * V * 4 * ((1 if w.initial_state is not None else 0) + 1)
+    if w.kind == "kda":
+        front = th * (3 * 2 * K + 2) + H * 4 + H * K * 4
+    else:
+        front = th * (2 * 2 * K + 4 + 2)
+    back = th * (2 * V + 2 * V) + states
+    return dict(path=front + back, kda_prep=front, kda_recur=back)
 
 
-def algorithmic_flops(B, T, H, K, V):
+def design_bytes(w):
+    """Bytes each kernel of the two-stage path moves by its own design: the
+    method's bytes plus the per-(chunk, head) record that kda_prep writes and
+    kda_recur reads (nKG, QG, KdT: C x K bf16 each; Aqk, Tb: C x C bf16 each;
+    Gamma_C: K fp32 -- 29184 B at K = 128)."""
+    K = w.K
+    mb = method_bytes(w)
+    n_chunks = w.H * (w.B * ((w.T + C - 1) // C) if w.cu_seqlens is None else
+                      sum((int(e - b) + C - 1) // C
+                          for b, e in zip(w.cu_seqlens[:-1], w.cu_seqlens[1:])))
+    rec = n_chunks * (3 * C * K * 2 + 2 * C * C * 2 + K * 4)
+    return dict(kda_prep=mb["kda_prep"] + rec, kda_recur=mb["kda_recur"] + rec)
+
+
+def algorithmic_flops(w):
     """Flops of the chunked method per token-head at chunk C: state read, output and
     state update (6 K V), intra-chunk products 2 C (3 K + 2 V), inverse 12 C^2."""
-    return B * T * H * (6 * K * V + 2 * C * (3 * K + 2 * V) + 12 * C * C)
+    K, V = w.K, w.V
+    return w.B * w.T * w.H * (6 * K * V + 2 * C * (3 * K + 2 * V) + 12 * C * C)
 
 
 def measured_traffic(kernel, workload):
@@ -91,9 +114,21 @@ def measured_traffic(kernel, workload):
     return int(fields["hbm_bytes_per_launch"])
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s):
-    """The fp64 oracle on this host's cores, on whole heads of the same workload,
-    repeated until about budget_s seconds of work."""
+    """The fp64 oracle on this host's cores, on whole heads of the same workload
+    (every head is an independent recurrence over all the workload's
+    sequences), repeated until about budget_s seconds of work; tokens/s are
+    scaled from the heads done to all heads."""
     import oracle
 
     orc = oracle.default()
@@ -102,21 +137,28 @@ def cpu_baseline(w, budget_s):
     head = 0
     reps = 0
     while t_total < budget_s and reps < 1024:
-        # one pass over `cores` heads (or all) at a time keeps every core busy
-        hs = [(head + i) % heads_total for i in range(min(cores, heads_total))]
+        # a batch of heads per call keeps every core busy (work items are
+        # (sequence, head) pairs)
+        per = max(1, min(heads_total, -(-cores // max(1, w.n_seqs))))
+        hs = [(head + i) % heads_total for i in range(per)]
         t0 = time.perf_counter()
-        orc.kda(w.q, w.k, w.v, w.g, w.beta, w.A_log, w.dt_bias, w.lower_bound, w.scale,
-                w.initial_state, True, None, heads=hs, threads=cores)
+        if w.kind == "kda":
+            orc.kda(w.q, w.k, w.v, w.g, w.beta, w.A_log, w.dt_bias, w.lower_bound, w.scale,
+                    w.initial_state, True, w.cu_seqlens, heads=hs, threads=cores)
+        else:
+            orc.gdn(w.q, w.k, w.v, w.g, w.beta, w.scale, w.initial_state, True, w.cu_seqlens,
+                    heads=hs, threads=cores)
         t_total += time.perf_counter() - t0
         done += len(hs)
         head = (head + len(hs)) % heads_total
         reps += 1
     tokens = w.B * w.T * done / heads_total
     return {"value": tokens / t_total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"fp64 token recurrence over {done} (sequence-batch x head) passes of "
-                       f"{w.B} x {w.T} tokens ({done} of {heads_total} heads per pass-set, "
-                       f"{t_total:.1f} s); tokens/s scaled by heads/{heads_total}; "
-                       f"input up-cast excluded")}
+            "cpu": cpu_model(),
+            "sample": (f"fp64 token recurrence (C oracle, OpenMP over sequence x head) on "
+                       f"{done} head passes over all {w.n_seqs} sequences ({w.B * w.T} tokens), "
+                       f"{t_total:.1f} s; tokens/s = tokens x heads done / {heads_total} / "
+                       f"seconds; input up-cast excluded")}
 
 
 def bench_decode(args, torch, kda, inputs, dev):
@@ -285,6 +327,155 @@ def bench_bwd(args, torch, kda, inputs, dev):
     }), flush=True)
 
 
+def make_sets(inputs, cfg, n_sets):
+    """The workload's seeded inputs, plus n_sets - 1 more drawn the same way with
+    other seeds (rotated across steps so that no step finds its inputs in the
+    256 MB MALL)."""
+    base = inputs.config(cfg)
+    sets = [base]
+    for r in range(1, n_sets):
+        seed = 1000 + cfg + 1000 * r
+        if cfg == 1:
+            w = inputs.kda_workload(base.B, base.T, base.H, base.K, base.V, seed, init_std=0.05)
+        elif cfg == 2:
+            lengths = (base.cu_seqlens[1:] - base.cu_seqlens[:-1]).tolist()
+            w = inputs.kda_workload(1, 0, base.H, base.K, base.V, seed, lengths=lengths)
+        elif cfg == 3:
+            w = inputs.gdn_workload(base.B, base.T, base.H, base.K, base.V, seed)
+        else:
+            w = inputs.kda_workload(base.B, base.T, base.H, base.K, base.V, seed, init_std=0.05)
+        sets.append(w)
+    return base, sets
+
+
+def bench_fwd(args, torch, kda, inputs, dev):
+    """The forward pass on one workload.  A step is one whole forward call on one
+    input set (kda_prep then kda_recur for the fixed-length KDA benchmark, whose
+    stages can be timed apart; kda_fwd / gdn_fwd otherwise).  Step times come
+    from a second pass of K steps with events recorded between steps (median
+    and mean reported); `value` is tokens / (wall time of the K timed steps /
+    K), timed without those events."""
+    cfg = args.workload
+    n_sets = args.sets if cfg in (1, 3) else min(args.sets, 2)
+    base, host_sets = make_sets(inputs, cfg, n_sets)
+    sets = [w.to(dev) for w in host_sets]
+    B, T, H, K, V, N = base.B, base.T, base.H, base.K, base.V, base.n_seqs
+    ws = torch.empty(kda.workspace_size(B, T, H, K, V, N, kind=base.kind), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    staged = cfg == 1
+
+    # Per-kernel durations (staged path): every PERIOD-th step times kda_prep
+    # and every PERIOD-th (offset PERIOD/2) kda_recur through the stages'
+    # measurement forms (kda_prep_timed / kda_recur_timed: the kernel's own
+    # start and end land in the two events, so no dispatch gap is counted).
+    period = 8 if args.steps >= 16 else 2
+
+    def bracketed(i):
+        if not staged:
+            return ()
+        if args.steps < 2:
+            return ("prep", "recur")
+        return {0: ("prep",), period // 2: ("recur",)}.get(i % period, ())
+
+    def step(i, which=(), ev=None):
+        d = sets[i % len(sets)]
+        if staged:
+            kda.kda_prep(d["q"], d["k"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
+                         base.lower_bound, ws, V=V, events=ev["prep"] if "prep" in which else None)
+            kda.kda_recur(d["v"], K, base.scale, ws, out, d["initial_state"], fin,
+                          events=ev["recur"] if "recur" in which else None)
+        elif base.kind == "kda":
+            kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
+                        base.lower_bound, base.scale, d["initial_state"], True, d["cu_seqlens"],
+                        workspace=ws, out=out, final_out=fin)
+        else:
+            kda.gdn_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], base.scale,
+                        d["initial_state"], True, d["cu_seqlens"], workspace=ws, out=out,
+                        final_out=fin)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    plan = [bracketed(i) for i in range(args.steps)]
+    evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for k in which} for which in plan]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for e in evs:  # a first record creates each event's handle (outside the timed region)
+        for pair in e.values():
+            for x in pair:
+                x.record(stream)
+    # timed region: K plain steps between two synchronisations (the value)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # the same K steps again with an event between consecutive steps (step
+    # times: median) and the sampled per-kernel events
+    for i in range(args.steps):
+        marks[i].record(stream)
+        step(args.warmup + i, plan[i], evs[i])
+    marks[-1].record(stream)
+    torch.cuda.synchronize()
+
+    step_us = sorted(marks[i].elapsed_time(marks[i + 1]) * 1e3 for i in range(args.steps))
+    median_us = step_us[len(step_us) // 2] if len(step_us) % 2 else \
+        0.5 * (step_us[len(step_us) // 2 - 1] + step_us[len(step_us) // 2])
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = B * T
+    value = tokens / (ms_per_step * 1e-3)
+
+    mb = method_bytes(base)
+    db = design_bytes(base)
+    flops = algorithmic_flops(base)
+    workload = inputs.CONFIG_NAMES[cfg]
+    line = {
+        "metric": METRIC if cfg == 1 else
+        f"{base.kind}_fwd tokens/sec, {workload}; HBM GB/s & MFMA % of peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "B": B, "T": T, "H": H, "K": K, "V": V, "N": N,
+                   "chunk": C, "input_sets_rotated": len(sets),
+                   "initial_state": None if base.initial_state is None else "fp32 N(0,0.05)",
+                   "final_state": True},
+        "step_us": {"median": round(median_us, 2), "mean": round(sum(step_us) / len(step_us), 2),
+                    "min": round(step_us[0], 2), "max": round(step_us[-1], 2)},
+    }
+    # the method's bytes over the median step: the whole path against 8 TB/s
+    path_s = median_us * 1e-6
+    line["path"] = {"method_bytes": int(mb["path"]),
+                    "method_GBps": round(mb["path"] / path_s / 1e9, 1),
+                    "hbm_frac": round(mb["path"] / path_s / 1e9 / HBM_PEAK_GBPS, 4),
+                    "algorithmic_TFLOPs": round(flops / path_s / 1e12, 2),
+                    "mfma_frac": round(flops / path_s / 1e12 / BF16_PEAK_TFLOPS, 5)}
+    if staged:
+        def mean_ms(kernel):
+            t = [e[kernel][0].elapsed_time(e[kernel][1]) for e in evs if kernel in e]
+            return sum(t) / len(t)
+
+        kern = {"kda_prep": mean_ms("prep"), "kda_recur": mean_ms("recur")}
+        dom = max(kern, key=kern.get)
+        achieved = mb[dom] / (kern[dom] * 1e-3) / 1e9
+        line["roofline"] = {
+            "bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(dom, workload),
+            "algorithmic_bytes_per_launch": int(mb[dom]),
+            "traffic_design": int(db[dom]),
+            "avg_launch_us": round(kern[dom] * 1e3, 2),
+            "launches_timed": sum(1 for which in plan if dom.removeprefix("kda_") in which)}
+        line["kernels_us"] = {k: round(v * 1e3, 2) for k, v in kern.items()}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +494,10 @@ def main():
     ap.add_argument("--bwd", action="store_true",
                     help="instead of the forward pass, time the backward pass (kda_bwd) on "
                          "the same workload")
+    ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 3, 4),
+                    help="forward workload (configuration index of inputs.config): 1 is the "
+                         "benchmark line; 2 (packed KDA), 3 (GDN), 4 (long KDA) time the same "
+                         "call on the other parity workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, copy BYTES bytes device-to-device "
                          "--steps times (the known-size reference for HBM byte counters)")
@@ -348,95 +543,7 @@ def main():
         bench_train(args, torch, kda, inputs, dev)
         return
 
-    base = inputs.config(1)
-    B, T, H, K, V, N = base.B, base.T, base.H, base.K, base.V, base.n_seqs
-    sets = [base.to(dev)]
-    for r in range(1, args.sets):
-        w = inputs.kda_workload(B, T, H, K, V, seed=1001 + 1000 * r, init_std=0.05)
-        sets.append(w.to(dev))
-    ws = torch.empty(kda.workspace_size(B, T, H, K, V), dtype=torch.uint8, device=dev)
-    out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
-    fin = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    # Per-kernel durations are sampled inside the timed region through the
-    # stages' measurement forms (kda_prep_timed, kda_recur_timed): the kernel's
-    # own start and end land in the two events, so the figure excludes the
-    # dispatch gap that events recorded between kernels would add.  Every
-    # PERIOD-th step times kda_prep and every PERIOD-th (offset PERIOD/2)
-    # times kda_recur; the other steps launch plainly.
-    period = 8 if args.steps >= 16 else 2
-    def bracketed(i):
-        if args.steps < 2:
-            return ("prep", "recur")
-        return {0: ("prep",), period // 2: ("recur",)}.get(i % period, ())
-
-    def step(i, which=(), ev=None):
-        d = sets[i % len(sets)]
-        kda.kda_prep(d["q"], d["k"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
-                     base.lower_bound, ws, V=V, events=ev["prep"] if "prep" in which else None)
-        kda.kda_recur(d["v"], K, base.scale, ws, out, d["initial_state"], fin,
-                      events=ev["recur"] if "recur" in which else None)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    plan = [bracketed(i) for i in range(args.steps)]
-    evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for k in which} for which in plan]
-    for e in evs:  # a first record creates each event's handle (outside the timed region)
-        for pair in e.values():
-            for x in pair:
-                x.record(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, plan[i], evs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    def mean_ms(kernel):
-        t = [e[kernel][0].elapsed_time(e[kernel][1]) for e in evs if kernel in e]
-        return sum(t) / len(t)
-
-    prep_ms = mean_ms("prep")
-    recur_ms = mean_ms("recur")
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens = B * T
-    value = tokens / (ms_per_step * 1e-3)
-
-    ab = algorithmic_bytes(B, T, H, K, V, N)
-    flops = algorithmic_flops(B, T, H, K, V)
-    kern = {"kda_prep": prep_ms, "kda_recur": recur_ms}
-    dom = max(kern, key=kern.get)
-    achieved = ab[dom] / (kern[dom] * 1e-3) / 1e9
-    workload = inputs.CONFIG_NAMES[1]
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(dom, workload),
-                "algorithmic_bytes_per_launch": int(ab[dom]),
-                "avg_launch_us": round(kern[dom] * 1e3, 2),
-                "launches_timed": sum(1 for which in plan if dom.removeprefix("kda_") in which)}
-    path_s = ms_per_step * 1e-3
-    line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": workload, "B": B, "T": T, "H": H, "K": K, "V": V, "chunk": C,
-                   "input_sets_rotated": len(sets), "initial_state": "fp32 N(0,0.05)",
-                   "final_state": True},
-        "roofline": roofline,
-        "path": {"algorithmic_bytes": int(ab["path"]),
-                 "algorithmic_GBps": round(ab["path"] / path_s / 1e9, 1),
-                 "hbm_frac": round(ab["path"] / path_s / 1e9 / HBM_PEAK_GBPS, 4),
-                 "algorithmic_TFLOPs": round(flops / path_s / 1e12, 2),
-                 "mfma_frac": round(flops / path_s / 1e12 / BF16_PEAK_TFLOPS, 5)},
-        "kernels_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    bench_fwd(args, torch, kda, inputs, dev)
 
 
 if __name__ == "__main__":

@@ -251,6 +251,8 @@ int run_recur(const Common& c, int32_t N, hipStream_t stream,
     r.n_seqs = N;
     r.packed = c.varlen;
     r.T = c.T;
+    r.slot_limit = (int32_t)w.slots;
+    r.tok_limit = (int64_t)c.B * c.T;
     r.seq_start = w.seq_start;
     r.chunk_off = w.chunk_off;
     if (w.sp.L == 0) {
@@ -355,6 +357,8 @@ int run_fwd_states(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, bool o
     r.n_seqs = N;
     r.packed = c.varlen;
     r.T = c.T;
+    r.slot_limit = (int32_t)w.slots;
+    r.tok_limit = (int64_t)c.B * c.T;
     r.seq_start = w.seq_start;
     r.chunk_off = w.chunk_off;
     r.chunk_state = bl.hs;
@@ -398,6 +402,8 @@ int run_bwd(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, const BwdIO& 
     r.n_seqs = N;
     r.packed = c.varlen;
     r.T = c.T;
+    r.slot_limit = (int32_t)w.slots;
+    r.tok_limit = (int64_t)c.B * c.T;
     r.seq_start = w.seq_start;
     r.chunk_off = w.chunk_off;
     r.chunk_state = bl.hs;

@@ -42,6 +42,12 @@ struct RecurArgs {
     int32_t T;
     const int32_t* seq_start;
     const int32_t* chunk_off;
+    // Bounds known on the host: chunk slots in the workspace and tokens in the
+    // batch.  Every range read from seq_start / chunk_off is clamped to them,
+    // so a table that does not match these arguments (a workspace filled for
+    // other sizes, or never filled) cannot send an access out of bounds.
+    int32_t slot_limit;
+    int64_t tok_limit;
     // Sequence splitting (all null / 0 for the plain forward pass):
     const int32_t* final_map;  // [n_seqs] or null: final state of sequence n goes to
                                // final_state[final_map[n]] (skipped when < 0)

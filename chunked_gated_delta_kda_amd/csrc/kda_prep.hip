@@ -37,18 +37,19 @@ namespace kda {
 //            (GDN: products of k^, q^ times exp(G_r - G_j) <= 1 per element)
 //  - cross-block A10, Aqk10^T (two blocks): (k^ Gam_loc1)(k^ Gam_end0/Gam0)^T,
 //            both factors <= 1
-//  - (I + A)^-1 per block = (I + N)(I + N^2)(I + N^4)(I + N^8), N = -A,
-//    exact because A is strictly lower triangular (A^16 = 0).  With the MFMA
-//    primitive M(P, Q) = P^T Q on D-layout operands (the D layout of P read as
-//    an A operand is P^T), every matrix is kept together with its transpose,
-//    so no product needs a layout change.  Operands are fp16 (|N| <= 1 and
-//    its powers stay far below the fp16 range for a 16 x 16 triangle),
-//    products accumulate in fp32.  Two blocks: T10 = -T11 A10 T00.
+//  - (I + A)^-1 per block by fp32 forward substitution (T (I + A) = I, one
+//    row of T per lane, A broadcast from LDS).  A power series of A (the
+//    Neumann / doubling form on the FlashKDA page) is exact in exact
+//    arithmetic because A^16 = 0, but with near-parallel keys and beta ~ 1
+//    its partial sums reach ~10^3 before cancelling to O(1), so low-precision
+//    operands lose the result; substitution only ever forms entries of T.
+//    Two blocks: T10 = -T11 A10 T00 on fp32 MFMA, with the primitive
+//    M(P, Q) = P^T Q on D-layout operands (the D layout of P read as an A
+//    operand is P^T), so no product needs a layout change.
 namespace {
 
 constexpr int ROW_SHR1 = 0x111, ROW_SHR2 = 0x112, ROW_SHR4 = 0x114, ROW_SHR8 = 0x118;
 
-typedef __attribute__((ext_vector_type(4))) _Float16 halfx4;
 
 __device__ __forceinline__ float row_scan16(float x) {
     x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR1, 0xf, 0xf, false);
@@ -80,25 +81,51 @@ __device__ __forceinline__ float lane_val(float x, int src) { return __shfl(x, s
 // 16 different 16-byte positions within 256 bytes, i.e. different banks.
 __device__ __forceinline__ int st_unit(int u) { return u ^ ((u >> 4) & 3); }
 
-__device__ __forceinline__ halfx4 to_h4(floatx4 x) {
-    halfx4 r;
-    r[0] = (_Float16)x[0];
-    r[1] = (_Float16)x[1];
-    r[2] = (_Float16)x[2];
-    r[3] = (_Float16)x[3];
-    return r;
-}
-
-// M(P, Q) = P^T Q for 16 x 16 matrices given in D layout.
+// M(P, Q) = P^T Q for 16 x 16 fp32 matrices given in D layout (lane n + 16 g
+// holds rows 4 g .. 4 g + 3 of column n): four v_mfma_f32_16x16x4_f32, the
+// i-th contracting over the rows 4 g + i that element i of every lane holds
+// (that element read as an A operand is P^T[n][4 g + i], as a B operand
+// Q[4 g + i][n]).
 __device__ __forceinline__ floatx4 mt(floatx4 p, floatx4 q) {
-    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(to_h4(p), to_h4(q), zero, 0, 0, 0);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p[i], q[i], acc, 0, 0, 0);
+    return acc;
 }
 
-__device__ __forceinline__ floatx4 add4(floatx4 a, floatx4 b) {
+// Row m of T = (I + A)^-1 for a strictly lower-triangular 16 x 16 A stored
+// row-major in LDS (a[16 k + j] = A[k][j]), in fp32.  From T (I + A) = I:
+// T[m][m] = 1, T[m][j] = 0 for j > m, and for j < m
+//   T[m][j] = -sum_{k > j} T[m][k] A[k][j].
+// The columns are finished from k = 15 down; each finished T[m][k] is added
+// into the pending sums of all columns before it, so the dependent chain is
+// one fma per column.  Every lane computes its whole row (lanes of one row
+// agree); the result is T[m][4 g + i], i = 0..3: the D layout of T^T.
+__device__ __forceinline__ floatx4 tri_inv_row(const float* a, int m, int g) {
+    float t[16], s[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        t[j] = j == m ? 1.f : 0.f;
+        s[j] = 0.f;
+    }
+#pragma unroll
+    for (int k = 15; k >= 1; --k) {
+        if (k < 15) t[k] = k < m ? -s[k] : t[k];
+        float row[16];
+#pragma unroll
+        for (int q = 0; q < (k + 3) / 4; ++q) {
+            const floatx4 v = *reinterpret_cast<const floatx4*>(a + 16 * k + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) row[4 * q + e] = v[e];
+        }
+#pragma unroll
+        for (int j = 0; j < k; ++j) s[j] = fmaf(t[k], row[j], s[j]);
+    }
+    t[0] = 0 < m ? -s[0] : t[0];
     floatx4 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = a[i] + b[i];
+    for (int i = 0; i < 4; ++i)
+        r[i] = g == 0 ? t[i] : g == 1 ? t[4 + i] : g == 2 ? t[8 + i] : t[12 + i];
     return r;
 }
 
@@ -141,7 +168,8 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t kdt_s[C * K];   // KdT transpose
     __shared__ __attribute__((aligned(16))) float gend_s[NB][K];     // block log2-decay totals
     __shared__ __attribute__((aligned(16))) bf16x8 kd0_s[NB == 2 ? KS * 64 : 1];  // block 0
-    __shared__ __attribute__((aligned(16))) floatx4 t00_s[64];       // block 0's T, D layout
+    __shared__ __attribute__((aligned(16))) float t00_s[256];        // block 0's T, row-major
+    __shared__ __attribute__((aligned(16))) float a_s[NB][256];      // each block's A, row-major
     __shared__ float beta0_s[16];
     __shared__ float dmax_s[NB];  // per block: sum over rows of the row's largest log2 decay
     __shared__ __attribute__((aligned(16))) float eg_s[NB][K];  // KDA: 2^(block total) per channel
@@ -305,7 +333,7 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
     // mfma32(X, Y) gives D = X Y^T: lane (n, g) holds element i of D at row
     // 4g + i, column n.
     unsigned char* rec = a.rec + ((int64_t)slot * a.H + h) * R::BYTES;
-    floatx4 dA = {0.f, 0.f, 0.f, 0.f}, dAT = dA, dQT = dA, dX = dA, dXQT = dA;
+    floatx4 dA = {0.f, 0.f, 0.f, 0.f}, dQT = dA, dX = dA, dXQT = dA;
     bf16x8 kgl_f[KS], qgl_f[KS];  // block 1's local KG and QG (cross-block products)
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
@@ -396,7 +424,6 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         } else {
             const bf16x8 kif = pack8(kil);
             dA = mfma32(kglf, kif, dA);    // KG KiG^T
-            dAT = mfma32(kif, kglf, dAT);  // KiG KG^T
             dQT = mfma32(kif, qglf, dQT);  // KiG QG^T = Aqk^T
         }
         if constexpr (NB == 2) {
@@ -405,7 +432,6 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
             qgl_f[j] = qglf;
         }
     }
-    if constexpr (GDN) dAT = dA;  // k^ k^T is symmetric
     // Gam_C, tile order: channel 32 j + 8 g + e is tile 2j + e/4, row 4g + e%4
     if (blk == 0 && m == 15) {
         float* gp = reinterpret_cast<float*>(rec + R::GAMC);
@@ -463,14 +489,14 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
         }
     }
 
-    // ---- masks, the in-block N, N^T and Aqk
+    // ---- masks: the in-block A (row-major into LDS) and Aqk
     float br[4], Gr[4];  // beta and (GDN) prefix log decay of rows 4g .. 4g+3
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         br[i] = lane_val(b, 4 * g + i);
         if constexpr (GDN) Gr[i] = lane_val(G[0][0], 4 * g + i);
     }
-    floatx4 N, NT, aq;
+    floatx4 aq;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;  // this element's row; its column is m
@@ -479,28 +505,16 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
             dec_rm = r > m ? exp2_hw(Gr[i] - G[0][0]) : 0.f;   // exp(G_r - G_m), r > m
             dec_mr = m >= r ? exp2_hw(G[0][0] - Gr[i]) : 0.f;  // exp(G_m - G_r), m >= r
         }
-        N[i] = m < r ? -br[i] * dA[i] * dec_rm : 0.f;  // N[r][m], m < r
-        NT[i] = r < m ? -b * dAT[i] * dec_mr : 0.f;    // N^T[r][m] = N[m][r], r < m
-        aq[i] = r <= m ? dQT[i] * dec_mr : 0.f;        // Aqk[m][r], r <= m
+        a_s[blk][16 * r + m] = m < r ? br[i] * dA[i] * dec_rm : 0.f;  // A[r][m], m < r
+        aq[i] = r <= m ? dQT[i] * dec_mr : 0.f;                     // Aqk[m][r], r <= m
     }
+    __syncthreads();  // A is in LDS (each wave reads back its own block's)
 
-    // ---- T^T = ((I + N)(I + N^2)(I + N^4)(I + N^8))^T by transposed products
-    const floatx4 N2 = mt(NT, N), N2T = mt(N, NT);
-    const floatx4 N4 = mt(N2T, N2), N4T = mt(N2, N2T);
-    const floatx4 N8 = mt(N4T, N4);
-    floatx4 I4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) I4[i] = (4 * g + i == m) ? 1.f : 0.f;
-    const floatx4 P1T = add4(add4(I4, NT), add4(N2T, mt(N2, NT)));  // (I + N + N^2 + N^3)^T
-    const floatx4 P2T = add4(P1T, mt(N4, P1T));                     // (P1 (I + N^4))^T
-    const floatx4 TT = add4(P2T, mt(N8, P2T));                      // (P2 (I + N^8))^T
+    // ---- T^T in D layout: lane (m, g) holds T[m][4g + i]
+    const floatx4 TT = tri_inv_row(a_s[blk], m, g);
     if constexpr (NB == 2) {
-        if (blk == 0) {
-            // T itself for the coupling block: T = P2 + P2 N^8 with P2 = P1 + P1 N^4
-            const floatx4 P1 = add4(add4(I4, N), add4(N2, mt(NT, N2)));
-            const floatx4 P2 = add4(P1, mt(P1T, N4));
-            t00_s[L] = add4(P2, mt(P2T, N8));
-        }
+        if (blk == 0)  // block 0's T row-major, for the coupling block
+            *reinterpret_cast<floatx4*>(&t00_s[16 * m + 4 * g]) = TT;
     }
 
     // ---- records Aqk (output block blk) and Tb (row block blk)
@@ -515,8 +529,11 @@ __global__ __launch_bounds__(64 * NB) void kda_prep_kernel(PrepArgs a) {
             floatx4 A10;
 #pragma unroll
             for (int i = 0; i < 4; ++i) A10[i] = br[i] * dX[i];  // A10[r][j] = b1_r (...)
+            floatx4 T00;  // D layout: T00[4g + i][m]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) T00[i] = t00_s[16 * (4 * g + i) + m];
             const floatx4 Z = mt(A10, TT);
-            const floatx4 T10T = mt(t00_s[L], Z);
+            const floatx4 T10T = mt(T00, Z);
             // row block 1: columns of block 0 then block 1
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

@@ -97,6 +97,13 @@ __global__ __launch_bounds__(64 * (NW + NL)) __attribute__((amdgpu_waves_per_eu(
     int64_t t0, t1;
     int s0, s1;
     seq_span(a, n, t0, t1, s0, s1);
+    if (a.packed) {  // a table from the workspace: keep every access inside the batch
+        t0 = min(max(t0, (int64_t)0), a.tok_limit);
+        t1 = min(max(t1, t0), a.tok_limit);
+        s0 = min(max(s0, 0), a.slot_limit);
+        s1 = min(max(s1, s0), a.slot_limit);
+        s1 = (int)min((int64_t)s1, s0 + (t1 - t0 + C - 1) / C);
+    }
     int nch = s1 - s0;
     if (trans) {
         // ||M||_2 <= 2^(sum of the chunk bounds): when that is negligible the

@@ -98,13 +98,21 @@ def cu_from_lengths(lengths):
 
 def kda_workload(B, T, H, K, V, seed, *, g_std=0.1, g_mean=0.0, A_log_std=0.01,
                  dt_bias_value=0.0, lower_bound=-5.0, init_std=None, lengths=None,
-                 random_lengths=None, name="kda"):
-    """KDA inputs: q,k,v ~N(0,1) bf16; g ~N(g_mean, g_std) bf16; beta logits ~N(0,1)
-    bf16; A_log ~N(0, A_log_std) fp32; dt_bias = dt_bias_value fp32 [H,K];
-    initial_state ~N(0, init_std) fp32 [N,H,K,V] or None.
+                 random_lengths=None, beta_mean=0.0, beta_value=None, A_log_value=None,
+                 key_cos=None, key_pool=None, q_equals_k=False, name="kda"):
+    """KDA inputs: q,k,v ~N(0,1) bf16; g ~N(g_mean, g_std) bf16; beta logits
+    ~N(beta_mean, 1) bf16; A_log ~N(0, A_log_std) fp32; dt_bias = dt_bias_value fp32
+    [H,K]; initial_state ~N(0, init_std) fp32 [N,H,K,V] or None.
 
     ``lengths`` (packed varlen) forces B=1 and T=sum(lengths);
     ``random_lengths=(n, lo, hi)`` draws n lengths uniform in [lo, hi] first.
+
+    Stress variants (drawn after everything above, so the default draws are
+    unchanged): ``beta_value`` / ``A_log_value`` replace the logits / A_log by a
+    constant; ``key_cos=c`` makes the keys of a head share a direction, k_t =
+    sqrt(c) u_h + sqrt(1 - c) z_t with u_h, z_t ~N(0, I) (pairwise cosine about
+    c); ``key_pool=P`` draws each key from P fixed vectors per head (keys repeat
+    within a chunk); ``q_equals_k`` sets q = k.
     """
     gen = torch.Generator().manual_seed(seed)
     if random_lengths is not None:
@@ -119,10 +127,24 @@ def kda_workload(B, T, H, K, V, seed, *, g_std=0.1, g_mean=0.0, A_log_std=0.01,
     k = _normal(gen, (B, T, H, K)).to(torch.bfloat16)
     v = _normal(gen, (B, T, H, V)).to(torch.bfloat16)
     g = _normal(gen, (B, T, H, K), g_std, g_mean).to(torch.bfloat16)
-    beta = _normal(gen, (B, T, H)).to(torch.bfloat16)
+    beta = _normal(gen, (B, T, H), 1.0, beta_mean).to(torch.bfloat16)
     A_log = _normal(gen, (H,), A_log_std)
     dt_bias = torch.full((H, K), float(dt_bias_value), dtype=torch.float32)
     h0 = None if init_std is None else _normal(gen, (N, H, K, V), init_std)
+    if beta_value is not None:
+        beta = torch.full((B, T, H), float(beta_value)).to(torch.bfloat16)
+    if A_log_value is not None:
+        A_log = torch.full((H,), float(A_log_value), dtype=torch.float32)
+    if key_cos is not None:
+        u = _normal(gen, (1, 1, H, K))
+        z = _normal(gen, (B, T, H, K))
+        k = (u * float(key_cos) ** 0.5 + z * (1.0 - float(key_cos)) ** 0.5).to(torch.bfloat16)
+    if key_pool is not None:
+        pool = _normal(gen, (H, int(key_pool), K))
+        idx = torch.randint(0, int(key_pool), (B, T, H), generator=gen)
+        k = pool[torch.arange(H)[None, None, :], idx].to(torch.bfloat16)
+    if q_equals_k:
+        q = k.clone()
     return Workload("kda", name, q, k, v, g, beta, A_log, dt_bias, float(lower_bound),
                     K ** -0.5, h0, cu)
 

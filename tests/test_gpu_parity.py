@@ -45,6 +45,33 @@ def test_clamp_active():
     check_parity(w, first_tokens=32)
 
 
+# ------------------------------------------------ stress: the chunk inverse
+@pytest.mark.parametrize("cos", [0.8, 0.95])
+def test_correlated_keys(cos):
+    """Keys of a head share a direction (pairwise cosine ~cos), beta logits
+    ~N(2, 1) and slow decay: the intra-chunk A has entries near 1, and a power
+    series for (I + A)^-1 would build partial sums far above its O(1) result.
+    (Closer to parallel the bf16 operands themselves, not the inverse, set the
+    error: the inverse is checked at cosine 0.99 in test_gpu_record.py.)"""
+    w = inputs.kda_workload(2, 320, 3, 128, 128, seed=3400 + int(round(cos * 100)),
+                            dt_bias_value=-6.0, beta_mean=2.0, key_cos=cos, init_std=0.05,
+                            name=f"corr_keys_{cos}")
+    check_parity(w, first_tokens=32)
+
+
+@pytest.mark.parametrize("pool", [4, 8])
+def test_retrieval_repeated_keys(pool):
+    """The delta rule's retrieval invariant at chunk scale: beta = 1 (logit 20,
+    whose sigmoid rounds to 1 in fp32), no decay (A_log = -1e4), q = k drawn from
+    `pool` vectors per head, so every 32-token chunk repeats keys and A has
+    entries equal to 1.  Then S_t^T k^_t = v_t and o_t = scale * v_t."""
+    w = inputs.kda_workload(1, 512, 4, 128, 128, seed=3500 + pool, beta_value=20.0,
+                            A_log_value=-1e4, key_pool=pool, q_equals_k=True, init_std=0.05,
+                            name=f"retrieval_pool{pool}")
+    o, _ = check_parity(w)
+    assert_close("o vs scale * v", to64(o), w.scale * w.v.double().numpy())
+
+
 def test_lower_bound_other_than_default():
     w = inputs.kda_workload(1, 200, 2, 128, 128, seed=3150, g_mean=4.0, g_std=1.0,
                             lower_bound=-1.5, init_std=0.05, name="lower_bound_-1.5")

@@ -1,0 +1,232 @@
+"""Chunk-level intermediates on the GPU: the record kda_prep / gdn_prep writes
+for every (32-token chunk, head), decoded from the layout documented in
+csrc/kda_common.h, against the fp64 chunkwise oracle (oracle/chunked.py) at
+the same chunk size.  This checks the token-parallel stage on its own: the
+decayed operands (-K^*Gamma, Q^*Gamma, K^*Gamma_C/Gamma), the intra-chunk
+products (Aqk), the inverse (Tb = (I + A)^-1 diag(beta)) and Gamma_C.
+
+Tolerances: every matrix is stored as bf16 (relative rounding 2^-9) and
+formed from bf16 operands, so each entry must match within 2e-2 of the
+largest entry of its matrix (and 1e-2 in relative Frobenius norm); Gamma_C is
+stored in fp32 and must match to 1e-4 relative (decays below 2^-120, which
+the floored gate reaches over a chunk, count as zero).
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_kda_amd as kda
+from chunked_gated_delta_kda_amd import inputs
+from oracle import chunked
+from parity_util import say
+
+pytestmark = pytest.mark.gpu
+
+C = 32          # tokens per chunk of the GPU record
+META = 256      # the packed-sequence table ahead of the records (N + 1 <= 32)
+
+
+def tok(g, e):
+    """Chunk token held in k-slot (g, e) of a token-contracting operand."""
+    return 16 * (e // 4) + 4 * g + e % 4
+
+
+def rho(t, r):
+    """Channel of row r of 16-channel state tile t."""
+    return 32 * (t // 2) + 8 * (r // 4) + 4 * (t % 2) + r % 4
+
+
+def record_size(K):
+    return 3 * C * K * 2 + 2 * C * C * 2 + K * 4
+
+
+def bf16_to_f64(u16):
+    return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def decode(rec, K):
+    """The record's matrices as dense fp64 arrays (rows = chunk tokens)."""
+    ks, kt = K // 32, K // 16
+    u16 = rec[: 3 * C * K * 2 + 2 * C * C * 2].view(np.uint16)
+    vals = bf16_to_f64(u16)
+    out = {}
+    # nKG, QG: [block][k-step j][g][m][e] = X[16 block + m][32 j + 8 g + e]
+    for name, base in (("nKG", 0), ("QG", C * K)):
+        x = vals[base: base + C * K].reshape(2, ks, 4, 16, 8)
+        d = np.zeros((C, K))
+        for b in range(2):
+            for j in range(ks):
+                for g in range(4):
+                    for m in range(16):
+                        d[16 * b + m, 32 * j + 8 * g: 32 * j + 8 * g + 8] = x[b, j, g, m]
+        out[name] = d
+    # KdT: [t][g][m][e] = Kd[tok(g, e)][rho(t, m)]
+    x = vals[2 * C * K: 3 * C * K].reshape(kt, 4, 16, 8)
+    d = np.zeros((C, K))
+    for t in range(kt):
+        for g in range(4):
+            for m in range(16):
+                for e in range(8):
+                    d[tok(g, e), rho(t, m)] = x[t, g, m, e]
+    out["Kd"] = d
+    # Aqk, Tb: [a][g][n][e] = X[16 a + n][tok(g, e)]
+    for name, base in (("Aqk", 3 * C * K), ("Tb", 3 * C * K + C * C)):
+        x = vals[base: base + C * C].reshape(2, 4, 16, 8)
+        d = np.zeros((C, C))
+        for a in range(2):
+            for g in range(4):
+                for n in range(16):
+                    for e in range(8):
+                        d[16 * a + n, tok(g, e)] = x[a, g, n, e]
+        out[name] = d
+    gam = rec[3 * C * K * 2 + 2 * C * C * 2: record_size(K)].view(np.float32).astype(np.float64)
+    d = np.zeros(K)
+    for t in range(kt):
+        for r in range(16):
+            d[rho(t, r)] = gam[16 * t + r]
+    out["GamC"] = d
+    return out
+
+
+def embed(x, rows, cols=None):
+    """x in the top-left corner of a zero (rows x cols) array (ragged chunks)."""
+    d = np.zeros((rows, x.shape[1] if cols is None else cols))
+    d[: x.shape[0], : x.shape[1]] = x
+    return d
+
+
+def close(name, got, want, atol_frac=2e-2, rel=1e-2):
+    scale = max(1.0, float(np.max(np.abs(want))))
+    err = float(np.max(np.abs(got - want)))
+    nrm = np.linalg.norm(want)
+    fro = float(np.linalg.norm(got - want) / nrm) if nrm > 0 else float(np.linalg.norm(got))
+    assert err <= atol_frac * scale and fro <= rel, \
+        f"{name}: max err {err:.3e} (limit {atol_frac * scale:.3e}), rel {fro:.3e}"
+    return err, fro
+
+
+def f64(t):
+    return None if t is None else t.double().numpy()
+
+
+def expected_records(w, kind):
+    """{(sequence, head, chunk): dense fp64 record matrices} from the chunkwise
+    oracle at chunk C (padding rows and columns of a ragged chunk are zero)."""
+    recs = []
+    chunked.chunked_forward(f64(w.q), f64(w.k), f64(w.v), f64(w.g), f64(w.beta), f64(w.A_log),
+                            f64(w.dt_bias), w.lower_bound, w.scale, None, None, chunk=C,
+                            gdn=(kind == "gdn"), record=recs)
+    beta = chunked.sigmoid(f64(w.beta)) if kind == "kda" else f64(w.beta)
+    kn = chunked.l2_normalise(f64(w.k))
+    qn = chunked.l2_normalise(f64(w.q))
+    out = {}
+    for r in recs:
+        n, h, s = r["seq"], r["head"], r["start"]
+        m = r["T"].shape[0]
+        gam = r["Gamma"]
+        b = beta[n, s: s + m, h]
+        out[(n, h, s // C)] = {
+            "Tb": embed(r["T"] * b[None, :], C, C),
+            "Aqk": embed(r["Aqk"], C, C),
+            "nKG": embed(-kn[n, s: s + m, h] * gam, C),
+            "QG": embed(qn[n, s: s + m, h] * gam, C),
+            "Kd": embed(kn[n, s: s + m, h] * gam[-1][None, :] / gam, C),
+            "GamC": gam[-1].copy(),
+        }
+    return out
+
+
+def encode(mats, K):
+    """Inverse of decode (fp32 stored exactly, matrices rounded to bf16 by
+    truncation): lets the CPU tests check that decode reads every position of
+    the documented layout once."""
+    ks, kt = K // 32, K // 16
+    bits = lambda x: (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    parts = []
+    for name in ("nKG", "QG"):
+        d = mats[name]
+        x = np.zeros((2, ks, 4, 16, 8))
+        for b in range(2):
+            for j in range(ks):
+                for g in range(4):
+                    for m in range(16):
+                        x[b, j, g, m] = d[16 * b + m, 32 * j + 8 * g: 32 * j + 8 * g + 8]
+        parts.append(bits(x).ravel())
+    x = np.zeros((kt, 4, 16, 8))
+    for t in range(kt):
+        for g in range(4):
+            for m in range(16):
+                for e in range(8):
+                    x[t, g, m, e] = mats["Kd"][tok(g, e), rho(t, m)]
+    parts.append(bits(x).ravel())
+    for name in ("Aqk", "Tb"):
+        x = np.zeros((2, 4, 16, 8))
+        for a in range(2):
+            for g in range(4):
+                for n in range(16):
+                    for e in range(8):
+                        x[a, g, n, e] = mats[name][16 * a + n, tok(g, e)]
+        parts.append(bits(x).ravel())
+    raw = np.concatenate(parts).view(np.uint8)
+    gam = np.zeros(K, np.float32)
+    for t in range(kt):
+        for r in range(16):
+            gam[16 * t + r] = mats["GamC"][rho(t, r)]
+    return np.concatenate([raw, gam.view(np.uint8)])
+
+
+CASES = {
+    # slow decay, correlated keys (cos ~0.95) and large beta: A has entries near 1
+    "kda_corr": dict(kind="kda", B=1, T=80, H=2, K=128, V=128, seed=4100, dt_bias_value=-6.0,
+                     beta_mean=2.0, key_cos=0.95),
+    # the floor binds: in-chunk cumulative log decay reaches -160 over 32 tokens
+    # near-parallel keys (cos ~0.99) with beta = 1 and no decay: A's entries
+    # are ~1 and every power-series partial sum of (I + A)^-1 is ~10^3
+    "kda_parallel": dict(kind="kda", B=1, T=64, H=2, K=128, V=128, seed=4104, beta_value=20.0,
+                         A_log_value=-1e4, key_cos=0.99),
+    "kda_clamp": dict(kind="kda", B=1, T=64, H=2, K=128, V=128, seed=4101, g_mean=8.0, g_std=1.0),
+    "kda_default_K64": dict(kind="kda", B=2, T=70, H=2, K=64, V=64, seed=4102),
+    "gdn": dict(kind="gdn", B=1, T=90, H=2, K=128, V=128, seed=4103),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_prep_record_matches_chunked_oracle(case):
+    cfg = dict(CASES[case])
+    kind = cfg.pop("kind")
+    B, T, H, K, V, seed = (cfg.pop(n) for n in ("B", "T", "H", "K", "V", "seed"))
+    if kind == "kda":
+        w = inputs.kda_workload(B, T, H, K, V, seed, name=case, **cfg)
+    else:
+        w = inputs.gdn_workload(B, T, H, K, V, seed, name=case)
+    say(f"[record] {case}: B={B} T={T} H={H} K={K}")
+    d = w.to("cuda:0")
+    ws = torch.empty(kda.workspace_size(B, T, H, K, V, kind=kind), dtype=torch.uint8,
+                     device="cuda:0")
+    if kind == "kda":
+        kda.kda_prep(d["q"], d["k"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
+                     w.lower_bound, ws, V=V)
+    else:
+        kda.gdn_prep(d["q"], d["k"], d["g"], d["beta"], ws, V=V)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+
+    nt = (T + C - 1) // C
+    size = record_size(K)
+    worst = {}
+    for (n, h, c), want in expected_records(w, kind).items():
+        slot = n * nt + c
+        off = META + (slot * H + h) * size
+        got = decode(raw[off: off + size], K)
+        for name, ref in want.items():
+            if name == "GamC":
+                continue
+            e, f = close(f"{name} (seq {n}, head {h}, chunk {c})", got[name], ref)
+            worst[name] = max(worst.get(name, 0.0), e)
+        gc, gam_c = got["GamC"], want["GamC"]
+        # fp32: decays below 2^-120 (the clamped case reaches e^-160) are zero
+        # to the state they scale
+        rel = float(np.max(np.abs(gc - gam_c) / np.maximum(gam_c, 2.0 ** -120)))
+        assert rel <= 1e-4, f"Gamma_C (seq {n}, head {h}, chunk {c}): rel err {rel:.3e}"
+        worst["GamC_rel"] = max(worst.get("GamC_rel", 0.0), rel)
+    say("  worst: " + ", ".join(f"{k} {v:.2e}" for k, v in sorted(worst.items())))
