@@ -40,8 +40,8 @@ C = 32  # tokens per chunk (two 16-token blocks)
 
 # The sources that build and launch the forward kernels: a counter summary of
 # the forward pass stays valid while none of them changes.
-FWD_SOURCES = ("kda_api.hip", "kda_common.h", "kda_launch.h", "kda_prep.hip", "kda_recur.hip",
-               "kda_split.hip")
+FWD_SOURCES = ("kda_api.hip", "kda_common.h", "kda_launch.h", "kda_ops.h", "kda_prep.hip",
+               "kda_recur.hip", "kda_split.hip", "kda_fused.hip")
 
 
 def source_digest(names=None) -> str:
@@ -88,6 +88,29 @@ def design_bytes(w):
                           for b, e in zip(w.cu_seqlens[:-1], w.cu_seqlens[1:])))
     rec = n_chunks * (3 * C * K * 2 + 2 * C * C * 2 + K * 4)
     return dict(kda_prep=mb["kda_prep"] + rec, kda_recur=mb["kda_recur"] + rec)
+
+
+def fused_design_bytes(w, seg_chunks, warm=2):
+    """Bytes the single-launch kernel moves by its own design: the method's
+    bytes plus the warm-up re-reads (q, k, g, beta, v of `warm` chunks before
+    every segment that starts inside its sequence).  Fixed-length batches only
+    (seg_chunks: the segment length the launch uses)."""
+    mb = method_bytes(w)
+    nc = (w.T + C - 1) // C
+    segs = max(1, -(-nc // seg_chunks))
+    per_tok = (3 * 2 * w.K + 2 + 2 * w.V) if w.kind == "kda" else (2 * 2 * w.K + 6 + 2 * w.V)
+    return mb["path"] + w.B * w.H * (segs - 1) * warm * C * per_tok
+
+
+def fused_segment_chunks(w, cus=256, min_chunks=8):
+    """The automatic segment length of kda_fwd for a fixed-length batch (the
+    library plans for the 256 compute units of an MI355X)."""
+    nc = (w.T + C - 1) // C
+    pairs = w.B * w.H
+    if pairs >= cus:
+        return max(nc, 1)
+    segs = -(-cus // pairs)
+    return max(min_chunks, -(-nc // segs))
 
 
 def algorithmic_flops(w):
@@ -350,35 +373,44 @@ def make_sets(inputs, cfg, n_sets):
 
 def bench_fwd(args, torch, kda, inputs, dev):
     """The forward pass on one workload.  A step is one whole forward call on one
-    input set (kda_prep then kda_recur for the fixed-length KDA benchmark, whose
-    stages can be timed apart; kda_fwd / gdn_fwd otherwise).  Step times come
-    from a second pass of K steps with events recorded between steps (median
-    and mean reported); `value` is tokens / (wall time of the K timed steps /
-    K), timed without those events."""
+    input set: the single-launch pass kda_fwd / gdn_fwd (--path fused, the
+    default) or, for the fixed-length KDA workloads, the two stages kda_prep
+    then kda_recur (--path staged).  Step times come from a second pass of K
+    steps with events recorded between steps (median and mean reported);
+    `value` is tokens / (wall time of the K timed steps / K), timed without
+    those events."""
     cfg = args.workload
     n_sets = args.sets if cfg in (1, 3) else min(args.sets, 2)
     base, host_sets = make_sets(inputs, cfg, n_sets)
     sets = [w.to(dev) for w in host_sets]
     B, T, H, K, V, N = base.B, base.T, base.H, base.K, base.V, base.n_seqs
-    ws = torch.empty(kda.workspace_size(B, T, H, K, V, N, kind=base.kind), dtype=torch.uint8,
-                     device=dev)
+    staged = args.path == "staged"
+    if staged and (base.kind != "kda" or base.cu_seqlens is not None):
+        raise SystemExit("--path staged times the fixed-length KDA workloads (1, 4)")
+    if staged:
+        ws_bytes = kda.workspace_size(B, T, H, K, V, N, kind=base.kind, segment_chunks=-1,
+                                      path="staged")
+    else:
+        ws_bytes = kda.workspace_size(B, T, H, K, V, N, kind=base.kind)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
     fin = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    staged = cfg == 1
 
-    # Per-kernel durations (staged path): every PERIOD-th step times kda_prep
-    # and every PERIOD-th (offset PERIOD/2) kda_recur through the stages'
-    # measurement forms (kda_prep_timed / kda_recur_timed: the kernel's own
-    # start and end land in the two events, so no dispatch gap is counted).
+    # Per-kernel durations: every PERIOD-th step launches its kernel(s) through
+    # the measurement forms (kda_fwd_timed / gdn_fwd_timed for the single
+    # launch, kda_prep_timed and (offset PERIOD/2) kda_recur_timed for the
+    # stages): the kernel's own start and end land in the two events, so no
+    # dispatch gap is counted.
     period = 8 if args.steps >= 16 else 2
+    names = ("prep", "recur") if staged else ("fused",)
 
     def bracketed(i):
-        if not staged:
-            return ()
         if args.steps < 2:
-            return ("prep", "recur")
-        return {0: ("prep",), period // 2: ("recur",)}.get(i % period, ())
+            return names
+        if staged:
+            return {0: ("prep",), period // 2: ("recur",)}.get(i % period, ())
+        return ("fused",) if i % (period // 2) == 0 else ()
 
     def step(i, which=(), ev=None):
         d = sets[i % len(sets)]
@@ -387,14 +419,16 @@ def bench_fwd(args, torch, kda, inputs, dev):
                          base.lower_bound, ws, V=V, events=ev["prep"] if "prep" in which else None)
             kda.kda_recur(d["v"], K, base.scale, ws, out, d["initial_state"], fin,
                           events=ev["recur"] if "recur" in which else None)
-        elif base.kind == "kda":
+            return
+        e = ev["fused"] if "fused" in which else None
+        if base.kind == "kda":
             kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
                         base.lower_bound, base.scale, d["initial_state"], True, d["cu_seqlens"],
-                        workspace=ws, out=out, final_out=fin)
+                        workspace=ws, out=out, final_out=fin, events=e)
         else:
             kda.gdn_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], base.scale,
                         d["initial_state"], True, d["cu_seqlens"], workspace=ws, out=out,
-                        final_out=fin)
+                        final_out=fin, events=e)
 
     for i in range(args.warmup):
         step(i)
@@ -430,7 +464,6 @@ def bench_fwd(args, torch, kda, inputs, dev):
     value = tokens / (ms_per_step * 1e-3)
 
     mb = method_bytes(base)
-    db = design_bytes(base)
     flops = algorithmic_flops(base)
     workload = inputs.CONFIG_NAMES[cfg]
     line = {
@@ -441,7 +474,7 @@ def bench_fwd(args, torch, kda, inputs, dev):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": workload, "B": B, "T": T, "H": H, "K": K, "V": V, "N": N,
-                   "chunk": C, "input_sets_rotated": len(sets),
+                   "chunk": C, "path": args.path, "input_sets_rotated": len(sets),
                    "initial_state": None if base.initial_state is None else "fp32 N(0,0.05)",
                    "final_state": True},
         "step_us": {"median": round(median_us, 2), "mean": round(sum(step_us) / len(step_us), 2),
@@ -454,23 +487,32 @@ def bench_fwd(args, torch, kda, inputs, dev):
                     "hbm_frac": round(mb["path"] / path_s / 1e9 / HBM_PEAK_GBPS, 4),
                     "algorithmic_TFLOPs": round(flops / path_s / 1e12, 2),
                     "mfma_frac": round(flops / path_s / 1e12 / BF16_PEAK_TFLOPS, 5)}
-    if staged:
-        def mean_ms(kernel):
-            t = [e[kernel][0].elapsed_time(e[kernel][1]) for e in evs if kernel in e]
-            return sum(t) / len(t)
 
+    def mean_ms(kernel):
+        t = [e[kernel][0].elapsed_time(e[kernel][1]) for e in evs if kernel in e]
+        return sum(t) / len(t)
+
+    if staged:
+        db = design_bytes(base)
         kern = {"kda_prep": mean_ms("prep"), "kda_recur": mean_ms("recur")}
         dom = max(kern, key=kern.get)
-        achieved = mb[dom] / (kern[dom] * 1e-3) / 1e9
-        line["roofline"] = {
-            "bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(dom, workload),
-            "algorithmic_bytes_per_launch": int(mb[dom]),
-            "traffic_design": int(db[dom]),
-            "avg_launch_us": round(kern[dom] * 1e3, 2),
-            "launches_timed": sum(1 for which in plan if dom.removeprefix("kda_") in which)}
-        line["kernels_us"] = {k: round(v * 1e3, 2) for k, v in kern.items()}
+        algo, design = mb[dom], db[dom]
+    else:
+        kern = {"kda_fused": mean_ms("fused")}
+        dom = "kda_fused"
+        algo = mb["path"]
+        design = (fused_design_bytes(base, fused_segment_chunks(base))
+                  if base.cu_seqlens is None else None)
+    achieved = algo / (kern[dom] * 1e-3) / 1e9
+    line["roofline"] = {
+        "bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": measured_traffic(dom, workload),
+        "algorithmic_bytes_per_launch": int(algo),
+        "traffic_design": None if design is None else int(design),
+        "avg_launch_us": round(kern[dom] * 1e3, 2),
+        "launches_timed": sum(1 for which in plan if dom.removeprefix("kda_") in which)}
+    line["kernels_us"] = {k: round(v * 1e3, 2) for k, v in kern.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
     print(json.dumps(line), flush=True)
@@ -498,6 +540,9 @@ def main():
                     help="forward workload (configuration index of inputs.config): 1 is the "
                          "benchmark line; 2 (packed KDA), 3 (GDN), 4 (long KDA) time the same "
                          "call on the other parity workloads")
+    ap.add_argument("--path", choices=("fused", "staged"), default="fused",
+                    help="forward path: the single launch kda_fwd (default) or the two "
+                         "stages kda_prep + kda_recur (fixed-length KDA workloads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the benchmark, copy BYTES bytes device-to-device "
                          "--steps times (the known-size reference for HBM byte counters)")

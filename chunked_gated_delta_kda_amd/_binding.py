@@ -18,6 +18,8 @@ _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED"
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_fwd", "gdn_fwd", "kda_fwd_workspace_size", "gdn_fwd_workspace_size",
+           "kda_fwd_segmented_workspace_size", "kda_fwd_segmented", "gdn_fwd_segmented",
+           "kda_fwd_timed", "gdn_fwd_timed",
            "kda_fwd_split_workspace_size", "kda_fwd_split", "gdn_fwd_split", "kda_prep",
            "gdn_prep", "kda_recur", "kda_prep_timed", "kda_recur_timed", "kda_decode", "gdn_decode", "kda_bwd_workspace_size",
            "kda_bwd", "gdn_bwd", "kda_fwd_save", "gdn_fwd_save", "kda_bwd_saved",
@@ -59,6 +61,18 @@ def load(path: Path | str | None = None):
                                   i32, i32, i32, i32, u16p, vp, sz, i32, vp]
     lib.kda_fwd_split_workspace_size.restype = ctypes.c_size_t
     lib.kda_fwd_split_workspace_size.argtypes = [i32] * 7
+    lib.kda_fwd_segmented_workspace_size.restype = ctypes.c_size_t
+    lib.kda_fwd_segmented_workspace_size.argtypes = [i32] * 7
+    # the segmented forms take the segment length before the stream, the timed
+    # forms two event handles after it
+    lib.kda_fwd_segmented.restype = ctypes.c_int
+    lib.kda_fwd_segmented.argtypes = lib.kda_fwd_split.argtypes
+    lib.gdn_fwd_segmented.restype = ctypes.c_int
+    lib.gdn_fwd_segmented.argtypes = lib.gdn_fwd_split.argtypes
+    lib.kda_fwd_timed.restype = ctypes.c_int
+    lib.kda_fwd_timed.argtypes = lib.kda_fwd.argtypes + [vp, vp]
+    lib.gdn_fwd_timed.restype = ctypes.c_int
+    lib.gdn_fwd_timed.argtypes = lib.gdn_fwd.argtypes + [vp, vp]
     lib.kda_prep.restype = ctypes.c_int
     lib.kda_prep.argtypes = [u16p, u16p, u16p, u16p, f32p, f32p, f32, i32p, i32, i32, i32, i32,
                              i32, i32, vp, sz, vp]
@@ -112,10 +126,19 @@ def version() -> int:
     return int(load().kda_version())
 
 
-def workspace_size(B, T, H, K, V, num_seqs=None, kind="kda", segment_chunks=None) -> int:
+def workspace_size(B, T, H, K, V, num_seqs=None, kind="kda", segment_chunks=None,
+                   path="fused") -> int:
+    """Workspace bytes of the single-launch forward pass (path "fused": kda_fwd,
+    kda_fwd_segmented) or of the two-stage one (path "staged": kda_fwd_split;
+    segment_chunks=-1 also sizes kda_prep / kda_recur).  0: unsupported sizes."""
     n = B if num_seqs is None else num_seqs
+    seg = 0 if segment_chunks is None else int(segment_chunks)
+    if path == "staged":
+        return int(load().kda_fwd_split_workspace_size(B, T, H, K, V, n, seg))
+    if path != "fused":
+        raise ValueError(f"unknown path {path!r}")
     if segment_chunks is not None:
-        return int(load().kda_fwd_split_workspace_size(B, T, H, K, V, n, int(segment_chunks)))
+        return int(load().kda_fwd_segmented_workspace_size(B, T, H, K, V, n, seg))
     fn = load().kda_fwd_workspace_size if kind == "kda" else load().gdn_fwd_workspace_size
     return int(fn(B, T, H, K, V, n))
 
@@ -177,7 +200,7 @@ def _shapes(q, k, v, beta, scale, initial_state, cu_seqlens):
 
 
 def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens, workspace,
-             kind, out=None, final_out=None, segment_chunks=None):
+             kind, out=None, final_out=None, segment_chunks=None, path="fused"):
     torch = _torch()
     B, T, H, K, V, N, scale = _shapes(q, k, v, beta, scale, initial_state, cu_seqlens)
     dev = q.device
@@ -193,7 +216,7 @@ def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens
         else:
             _need(final_out, "final_out", torch.float32, (N, H, K, V), dev)
         final = final_out
-    need = workspace_size(B, T, H, K, V, N, kind, segment_chunks)
+    need = workspace_size(B, T, H, K, V, N, kind, segment_chunks, path)
     if need == 0:
         raise LibKdaError(2, status_str(2))
     if workspace is None:
@@ -205,49 +228,106 @@ def _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens
                 workspace=workspace, stream=stream)
 
 
+def _kda_gate_checks(g, A_log, dt_bias, B, T, H, K, dev):
+    torch = _torch()
+    _need(g, "g", torch.bfloat16, (B, T, H, K), dev)
+    _need(A_log, "A_log", torch.float32, (H,), dev)
+    _need(dt_bias, "dt_bias", torch.float32, None, dev)
+    if dt_bias.numel() != H * K:
+        raise ValueError("dt_bias must hold H * K values ([H, K] or [H * K])")
+
+
 def kda_fwd(q, k, v, g, beta, A_log, dt_bias, lower_bound=-5.0, scale=None, initial_state=None,
             output_final_state=True, cu_seqlens=None, workspace=None, out=None,
-            final_out=None, segment_chunks=None):
-    """KDA forward on the GPU.  q, k, g [B,T,H,K] bf16; v [B,T,H,V] bf16; beta logits
-    [B,T,H] bf16; A_log [H] fp32; dt_bias [H,K] (or [H*K]) fp32; initial_state
-    [N,H,K,V] fp32 or None; cu_seqlens int32 [N+1] or None (B must then be 1).
-    ``workspace``, ``out`` and ``final_out`` optionally supply preallocated device
-    buffers.  ``segment_chunks`` (None: automatic) controls sequence splitting
-    (kda_fwd_split).  Returns (o [B,T,H,V] bf16, final_state [N,H,K,V] fp32 or None)."""
-    torch = _torch()
+            final_out=None, segment_chunks=None, events=None):
+    """KDA forward on the GPU (the single-launch pass).  q, k, g [B,T,H,K] bf16;
+    v [B,T,H,V] bf16; beta logits [B,T,H] bf16; A_log [H] fp32; dt_bias [H,K] (or
+    [H*K]) fp32; initial_state [N,H,K,V] fp32 or None; cu_seqlens int32 [N+1] or
+    None (B must then be 1).  ``workspace``, ``out`` and ``final_out`` optionally
+    supply preallocated device buffers.  ``segment_chunks`` (None: automatic)
+    sets the sequence segments (kda_fwd_segmented); ``events`` = (start, stop)
+    torch.cuda.Event records the kernel's own start and end (kda_fwd_timed).
+    Returns (o [B,T,H,V] bf16, final_state [N,H,K,V] fp32 or None)."""
     a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens,
                  workspace, "kda", out, final_out, segment_chunks)
     B, T, H, K = a["B"], a["T"], a["H"], a["K"]
-    _need(g, "g", torch.bfloat16, (B, T, H, K), q.device)
-    _need(A_log, "A_log", torch.float32, (H,), q.device)
-    _need(dt_bias, "dt_bias", torch.float32, None, q.device)
-    if dt_bias.numel() != H * K:
-        raise ValueError("dt_bias must hold H * K values ([H, K] or [H * K])")
-    st = load().kda_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
-                              _ptr(dt_bias), float(lower_bound), a["scale"], _ptr(initial_state),
-                              _ptr(a["final"]), _ptr(cu_seqlens), a["N"], B, T, H, K, a["V"],
-                              _ptr(a["o"]), _ptr(a["workspace"]),
-                              a["workspace"].numel() * a["workspace"].element_size(),
-                              0 if segment_chunks is None else int(segment_chunks), a["stream"])
+    _kda_gate_checks(g, A_log, dt_bias, B, T, H, K, q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
+            float(lower_bound), a["scale"], _ptr(initial_state), _ptr(a["final"]),
+            _ptr(cu_seqlens), a["N"], B, T, H, K, a["V"], _ptr(a["o"]), _ptr(a["workspace"]),
+            _nbytes(a["workspace"]))
+    if events is not None:
+        if segment_chunks is not None:
+            raise ValueError("events time the automatic segments only")
+        st = load().kda_fwd_timed(*args, a["stream"], *_events(events))
+    elif segment_chunks is not None:
+        st = load().kda_fwd_segmented(*args, int(segment_chunks), a["stream"])
+    else:
+        st = load().kda_fwd(*args, a["stream"])
     if st != 0:
         raise LibKdaError(st, status_str(st))
     return a["o"], a["final"]
 
 
 def gdn_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
-            cu_seqlens=None, workspace=None, out=None, final_out=None, segment_chunks=None):
-    """GDN forward on the GPU.  g is the fp32 log decay [B,T,H] (<= 0); beta are
-    probabilities [B,T,H] bf16, used as given.  Other arguments as kda_fwd."""
+            cu_seqlens=None, workspace=None, out=None, final_out=None, segment_chunks=None,
+            events=None):
+    """GDN forward on the GPU (the single-launch pass).  g is the fp32 log decay
+    [B,T,H] (<= 0); beta are probabilities [B,T,H] bf16, used as given.  Other
+    arguments as kda_fwd."""
     torch = _torch()
     a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens,
                  workspace, "gdn", out, final_out, segment_chunks)
     B, T, H = a["B"], a["T"], a["H"]
     _need(g, "g", torch.float32, (B, T, H), q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), a["scale"], _ptr(initial_state),
+            _ptr(a["final"]), _ptr(cu_seqlens), a["N"], B, T, H, a["K"], a["V"], _ptr(a["o"]),
+            _ptr(a["workspace"]), _nbytes(a["workspace"]))
+    if events is not None:
+        if segment_chunks is not None:
+            raise ValueError("events time the automatic segments only")
+        st = load().gdn_fwd_timed(*args, a["stream"], *_events(events))
+    elif segment_chunks is not None:
+        st = load().gdn_fwd_segmented(*args, int(segment_chunks), a["stream"])
+    else:
+        st = load().gdn_fwd(*args, a["stream"])
+    if st != 0:
+        raise LibKdaError(st, status_str(st))
+    return a["o"], a["final"]
+
+
+def kda_fwd_split(q, k, v, g, beta, A_log, dt_bias, lower_bound=-5.0, scale=None,
+                  initial_state=None, output_final_state=True, cu_seqlens=None, workspace=None,
+                  out=None, final_out=None, segment_chunks=0):
+    """The two-stage KDA forward (kda_prep then kda_recur, records in the
+    workspace) with its sequence splitting: segment_chunks < 0 never, 0
+    automatic, > 0 segments of that many chunks.  Arguments as kda_fwd."""
+    a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens,
+                 workspace, "kda", out, final_out, segment_chunks, path="staged")
+    B, T, H, K = a["B"], a["T"], a["H"], a["K"]
+    _kda_gate_checks(g, A_log, dt_bias, B, T, H, K, q.device)
+    st = load().kda_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                              _ptr(dt_bias), float(lower_bound), a["scale"], _ptr(initial_state),
+                              _ptr(a["final"]), _ptr(cu_seqlens), a["N"], B, T, H, K, a["V"],
+                              _ptr(a["o"]), _ptr(a["workspace"]), _nbytes(a["workspace"]),
+                              int(segment_chunks), a["stream"])
+    if st != 0:
+        raise LibKdaError(st, status_str(st))
+    return a["o"], a["final"]
+
+
+def gdn_fwd_split(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+                  cu_seqlens=None, workspace=None, out=None, final_out=None, segment_chunks=0):
+    """The two-stage GDN forward with its sequence splitting (see kda_fwd_split)."""
+    torch = _torch()
+    a = _prepare(q, k, v, beta, scale, initial_state, output_final_state, cu_seqlens,
+                 workspace, "gdn", out, final_out, segment_chunks, path="staged")
+    B, T, H = a["B"], a["T"], a["H"]
+    _need(g, "g", torch.float32, (B, T, H), q.device)
     st = load().gdn_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), a["scale"],
                               _ptr(initial_state), _ptr(a["final"]), _ptr(cu_seqlens), a["N"],
                               B, T, H, a["K"], a["V"], _ptr(a["o"]), _ptr(a["workspace"]),
-                              a["workspace"].numel() * a["workspace"].element_size(),
-                              0 if segment_chunks is None else int(segment_chunks), a["stream"])
+                              _nbytes(a["workspace"]), int(segment_chunks), a["stream"])
     if st != 0:
         raise LibKdaError(st, status_str(st))
     return a["o"], a["final"]

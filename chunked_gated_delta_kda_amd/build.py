@@ -16,8 +16,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libkda.so"
-SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_decode.hip", "kda_split.hip",
-           "kda_bwd.hip"]
+SOURCES = ["kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_fused.hip", "kda_decode.hip",
+           "kda_split.hip", "kda_bwd.hip"]
 ARCH = "gfx950"
 
 
@@ -31,7 +31,8 @@ def hipcc() -> str:
 # Sources whose kernels keep MFMA results in VGPRs (see FLAGS_VGPR_FORM).  The
 # backward gradient kernel is left to the compiler's default: its register
 # demand exceeds the VGPR file, and the VGPR-form rewrite crashes on it.
-VGPR_FORM = {"kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_decode.hip", "kda_split.hip"}
+VGPR_FORM = {"kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_fused.hip", "kda_decode.hip",
+             "kda_split.hip"}
 
 
 def _compile(src: str, obj: Path, extra_flags) -> subprocess.CompletedProcess:

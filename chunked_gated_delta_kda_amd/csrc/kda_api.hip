@@ -307,6 +307,161 @@ int run(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t strea
     return st != KDA_OK ? st : run_recur(c, N, stream);
 }
 
+// ---------------------------------------------- the single-launch forward pass
+// One workgroup per (sequence segment, head) (kda_fused.hip).  Segments of L
+// chunks: automatic (request 0) only when the (sequence, head) pairs are
+// fewer than the compute units, aiming at one workgroup per unit, never
+// shorter than FUSED_MIN_CHUNKS; a request < 0 keeps whole sequences, > 0
+// sets L.  A segment that starts mid-sequence warms up over FUSED_WARM_CHUNKS
+// chunks from a zero state, exact to 2^FUSED_BOUND_LIMIT of the entering
+// state or else restarted from the sequence start (see kda_fused.hip).
+constexpr int32_t FUSED_MIN_CHUNKS = 8;
+constexpr int32_t FUSED_WARM_CHUNKS = 2;
+// The plan targets MI355X's 256 compute units.  It is a constant, not a
+// device query, so that the workspace size is a pure function of the sizes.
+constexpr int64_t FUSED_CUS = 256;
+constexpr float FUSED_BOUND_LIMIT = -40.f;
+
+struct FusedPlan {
+    int32_t L;             // chunks per segment
+    int32_t segs_per_seq;  // fixed length
+    int64_t n_virt;        // packed: segment slots (at most N + ceil(slots / L))
+};
+
+FusedPlan plan_fused(int32_t B, int32_t T, int32_t H, int32_t N, bool varlen, int32_t request) {
+    FusedPlan p{1, 1, 0};
+    const int64_t cus = FUSED_CUS;
+    if (!varlen) {
+        const int64_t nc = ((int64_t)T + kda::C - 1) / kda::C;
+        int64_t L = std::max<int64_t>(nc, 1);
+        if (request > 0) {
+            L = request;
+        } else if (request == 0) {
+            const int64_t pairs = (int64_t)B * H;
+            if (pairs < cus) {
+                const int64_t segs = (cus + pairs - 1) / pairs;
+                L = std::max<int64_t>(FUSED_MIN_CHUNKS, (nc + segs - 1) / segs);
+            }
+        }
+        L = std::min<int64_t>(L, INT32_MAX);
+        p.L = (int32_t)L;
+        p.segs_per_seq = (int32_t)std::max<int64_t>(1, (nc + L - 1) / L);
+    } else {
+        const int64_t slots = ((int64_t)B * T + kda::C - 1) / kda::C + N;
+        int64_t L = std::max<int64_t>(slots, 1);
+        if (request > 0) {
+            L = request;
+        } else if (request == 0) {
+            // about two workgroups per compute unit over the whole batch
+            const int64_t work = slots * H;
+            L = std::max<int64_t>(FUSED_MIN_CHUNKS, (work + 2 * cus - 1) / (2 * cus));
+        }
+        L = std::min<int64_t>(L, INT32_MAX);
+        p.L = (int32_t)L;
+        p.n_virt = N + (slots + L - 1) / L;
+    }
+    return p;
+}
+
+// Workspace of the single-launch pass: the packed-sequence and segment tables
+// (nothing for fixed-length batches; one alignment unit is still reported,
+// so that a size of 0 keeps meaning "unsupported").
+size_t fused_workspace_bytes(const FusedPlan& p, int32_t N, bool varlen) {
+    if (!varlen) return ALIGN;
+    const size_t nv = (size_t)p.n_virt;
+    return meta_bytes(N) + align_up(sizeof(int32_t) * (2 * (nv + 1) + nv + ((size_t)N + 1)));
+}
+
+// Argument checks of the single-launch pass (its workspace instead of the
+// two-stage one); sets N.
+int check_fused(const Common& c, int32_t& N) {
+    if (c.B < 1 || c.T < 0 || c.H < 1) return KDA_ERR_INVALID_ARG;
+    const bool tokens = c.T > 0;
+    if (tokens && (!c.q || !c.k || !c.v || !c.beta || !c.o)) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(c.K) || !supported_dim(c.V)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)c.B * c.T >= ((int64_t)1 << 31)) return KDA_ERR_INVALID_ARG;
+    if (!std::isfinite(c.scale)) return KDA_ERR_INVALID_ARG;
+    if (c.varlen) {
+        if (c.B != 1 || c.num_seqs < 1) return KDA_ERR_INVALID_ARG;
+        N = c.num_seqs;
+    } else {
+        N = c.B;
+    }
+    if (!aligned(c.q, 16) || !aligned(c.k, 16) || !aligned(c.v, 16) || !aligned(c.o, 16) ||
+        !aligned(c.beta, 2) || !aligned(c.initial_state, 16) || !aligned(c.final_state, 16))
+        return KDA_ERR_INVALID_ARG;
+    const FusedPlan fp = plan_fused(c.B, c.T, c.H, N, c.varlen, c.split);
+    if (fp.n_virt > INT32_MAX / 4) return KDA_ERR_INVALID_ARG;
+    const int64_t groups =
+        c.varlen ? fp.n_virt * c.H : (int64_t)N * fp.segs_per_seq * c.H;
+    if (groups > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (c.varlen) {
+        if (!c.ws || !aligned(c.ws, ALIGN)) return KDA_ERR_WORKSPACE;
+        if (c.ws_bytes < fused_workspace_bytes(fp, N, true)) return KDA_ERR_WORKSPACE;
+    }
+    return KDA_OK;
+}
+
+int run_fused(const Common& c, int32_t N, kda::FusedArgs f, bool gdn, hipStream_t stream,
+              const kda::LaunchEvents* ev = nullptr) {
+    const FusedPlan fp = plan_fused(c.B, c.T, c.H, N, c.varlen, c.split);
+    (void)hipGetLastError();  // clear a stale error from unrelated work
+    f.q = c.q;
+    f.k = c.k;
+    f.v = c.v;
+    f.beta = c.beta;
+    f.scale = c.scale;
+    f.initial_state = c.initial_state;
+    f.final_state = c.final_state;
+    f.o = c.o;
+    f.H = c.H;
+    f.T = c.T;
+    f.n_seqs = N;
+    f.packed = c.varlen;
+    f.warm_chunks = FUSED_WARM_CHUNKS;
+    f.bound_limit = FUSED_BOUND_LIMIT;
+    f.tok_limit = (int64_t)c.B * c.T;
+    int64_t groups;
+    if (!c.varlen) {
+        f.seg_chunks = fp.L;
+        f.segs_per_seq = fp.segs_per_seq;
+        groups = (int64_t)N * fp.segs_per_seq * c.H;
+    } else {
+        const int32_t nv = (int32_t)fp.n_virt;
+        unsigned char* base = static_cast<unsigned char*>(c.ws);
+        int32_t* seq_start = reinterpret_cast<int32_t*>(base);
+        int32_t* chunk_off = seq_start + (N + 1);
+        int32_t* vseq_start = reinterpret_cast<int32_t*>(base + meta_bytes(N));
+        int32_t* vchunk_off = vseq_start + (nv + 1);
+        int32_t* final_map = vchunk_off + (nv + 1);
+        int32_t* vfirst = final_map + nv;
+        kda::launch_seq_table(c.cu, N, c.T, (int64_t)c.B * c.T, seq_start, chunk_off, stream);
+        kda::launch_seg_table(seq_start, chunk_off, N, fp.L, nv, vseq_start, vchunk_off,
+                              final_map, vfirst, stream);
+        f.seq_start = seq_start;
+        f.vseq_start = vseq_start;
+        f.vfirst = vfirst;
+        f.final_map = final_map;
+        f.n_segs = nv;
+        groups = (int64_t)nv * c.H;
+    }
+    kda::launch_fused(f, c.K, c.V, gdn, (int)groups, stream, ev);
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+size_t fused_size_either_layout(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                int32_t num_seqs, int32_t segment_chunks) {
+    if (B < 1 || T < 0 || H < 1 || num_seqs < 1 || !supported_dim(K) || !supported_dim(V))
+        return 0;
+    size_t need = 0;
+    for (int varlen = 0; varlen < 2; ++varlen) {
+        const int32_t N = varlen ? num_seqs : B;
+        const FusedPlan fp = plan_fused(B, T, H, N, varlen != 0, segment_chunks);
+        need = std::max(need, fused_workspace_bytes(fp, N, varlen != 0));
+    }
+    return need;
+}
+
 size_t bwd_workspace_bytes(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t N,
                            bool varlen) {
     const SplitPlan none{0, 0};
@@ -521,14 +676,19 @@ size_t kda_fwd_split_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, 
     return need;
 }
 
+size_t kda_fwd_segmented_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                        int32_t num_seqs, int32_t segment_chunks) {
+    return fused_size_either_layout(B, T, H, K, V, num_seqs, segment_chunks);
+}
+
 size_t kda_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                               int32_t num_seqs) {
-    return kda_fwd_split_workspace_size(B, T, H, K, V, num_seqs, 0);
+    return fused_size_either_layout(B, T, H, K, V, num_seqs, 0);
 }
 
 size_t gdn_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                               int32_t num_seqs) {
-    return kda_fwd_workspace_size(B, T, H, K, V, num_seqs);
+    return fused_size_either_layout(B, T, H, K, V, num_seqs, 0);
 }
 
 int kda_fwd_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
@@ -552,15 +712,86 @@ int kda_fwd_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
     return run(c, N, p, false, static_cast<hipStream_t>(stream));
 }
 
+static int kda_fwd_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* g, const uint16_t* beta, const float* A_log,
+                         const float* dt_bias, float lower_bound, float scale,
+                         const float* initial_state, float* final_state,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                         int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                         size_t workspace_bytes, int32_t segment_chunks, void* stream,
+                         void* start_event, void* stop_event) {
+    const bool timed = start_event || stop_event;
+    if (timed && !(start_event && stop_event)) return KDA_ERR_INVALID_ARG;
+    const kda::LaunchEvents ev{static_cast<hipEvent_t>(start_event),
+                               static_cast<hipEvent_t>(stop_event)};
+    Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, cu_seqlens != nullptr,
+             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale, segment_chunks};
+    int st = check_kda_gate(T, g, A_log, dt_bias, lower_bound);
+    if (st != KDA_OK) return st;
+    int32_t N = 0;
+    st = check_fused(c, N);
+    if (st != KDA_OK) return st;
+    kda::FusedArgs f{};
+    f.g_kda = g;
+    f.A_log = A_log;
+    f.dt_bias = dt_bias;
+    f.lower_bound = lower_bound;
+    return run_fused(c, N, f, false, static_cast<hipStream_t>(stream), timed ? &ev : nullptr);
+}
+
+static int gdn_fwd_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                         const uint16_t* beta, float scale, const float* initial_state,
+                         float* final_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                         int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o,
+                         void* workspace, size_t workspace_bytes, int32_t segment_chunks,
+                         void* stream, void* start_event, void* stop_event) {
+    const bool timed = start_event || stop_event;
+    if (timed && !(start_event && stop_event)) return KDA_ERR_INVALID_ARG;
+    const kda::LaunchEvents ev{static_cast<hipEvent_t>(start_event),
+                               static_cast<hipEvent_t>(stop_event)};
+    Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, cu_seqlens != nullptr,
+             num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, scale, segment_chunks};
+    if (T > 0 && !g) return KDA_ERR_INVALID_ARG;
+    int32_t N = 0;
+    int st = check_fused(c, N);
+    if (st != KDA_OK) return st;
+    kda::FusedArgs f{};
+    f.g_gdn = g;
+    return run_fused(c, N, f, true, static_cast<hipStream_t>(stream), timed ? &ev : nullptr);
+}
+
 int kda_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
             const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
             float scale, const float* initial_state, float* final_state,
             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
             int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
             void* stream) {
-    return kda_fwd_split(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
+    return kda_fwd_fused(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
                          final_state, cu_seqlens, num_seqs, B, T, H, K, V, o, workspace,
-                         workspace_bytes, 0, stream);
+                         workspace_bytes, 0, stream, nullptr, nullptr);
+}
+
+int kda_fwd_segmented(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* g, const uint16_t* beta, const float* A_log,
+                      const float* dt_bias, float lower_bound, float scale,
+                      const float* initial_state, float* final_state, const int32_t* cu_seqlens,
+                      int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                      uint16_t* o, void* workspace, size_t workspace_bytes,
+                      int32_t segment_chunks, void* stream) {
+    return kda_fwd_fused(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
+                         final_state, cu_seqlens, num_seqs, B, T, H, K, V, o, workspace,
+                         workspace_bytes, segment_chunks, stream, nullptr, nullptr);
+}
+
+int kda_fwd_timed(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                  const uint16_t* beta, const float* A_log, const float* dt_bias,
+                  float lower_bound, float scale, const float* initial_state,
+                  float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                  int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                  size_t workspace_bytes, void* stream, void* start_event, void* stop_event) {
+    return kda_fwd_fused(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
+                         final_state, cu_seqlens, num_seqs, B, T, H, K, V, o, workspace,
+                         workspace_bytes, 0, stream, start_event, stop_event);
 }
 
 int gdn_fwd_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
@@ -584,8 +815,30 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
             int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
             void* stream) {
-    return gdn_fwd_split(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens,
-                         num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, 0, stream);
+    return gdn_fwd_fused(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens,
+                         num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, 0, stream,
+                         nullptr, nullptr);
+}
+
+int gdn_fwd_segmented(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                      const uint16_t* beta, float scale, const float* initial_state,
+                      float* final_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                      int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o,
+                      void* workspace, size_t workspace_bytes, int32_t segment_chunks,
+                      void* stream) {
+    return gdn_fwd_fused(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens,
+                         num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, segment_chunks,
+                         stream, nullptr, nullptr);
+}
+
+int gdn_fwd_timed(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                  const uint16_t* beta, float scale, const float* initial_state,
+                  float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                  int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                  size_t workspace_bytes, void* stream, void* start_event, void* stop_event) {
+    return gdn_fwd_fused(q, k, v, g, beta, scale, initial_state, final_state, cu_seqlens,
+                         num_seqs, B, T, H, K, V, o, workspace, workspace_bytes, 0, stream,
+                         start_event, stop_event);
 }
 
 int kda_prep_timed(const uint16_t* q, const uint16_t* k, const uint16_t* g,

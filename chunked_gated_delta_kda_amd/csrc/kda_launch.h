@@ -104,6 +104,41 @@ struct SplitScanArgs {
     int32_t n_seqs;
 };
 
+// The single-launch forward pass (kda_fused.hip): one workgroup per
+// (sequence segment, head).  Fixed-length batches: sequence n is tokens
+// [n T, (n+1) T), cut into segs_per_seq segments of seg_chunks chunks.
+// Packed batches: the segment table of kda_seg_table (vseq_start, vfirst,
+// final_map over n_segs segment slots) and the sequence table (seq_start).
+struct FusedArgs {
+    const uint16_t* q;          // [tokens, H, K] bf16
+    const uint16_t* k;          // [tokens, H, K] bf16
+    const uint16_t* v;          // [tokens, H, V] bf16
+    const uint16_t* g_kda;      // KDA: pre-activation gate [tokens, H, K] bf16
+    const float* g_gdn;         // GDN: log decay [tokens, H] fp32
+    const uint16_t* beta;       // [tokens, H] bf16 (KDA logits / GDN probabilities)
+    const float* A_log;         // [H] (KDA)
+    const float* dt_bias;       // [H, K] (KDA)
+    float lower_bound;
+    float scale;
+    const float* initial_state; // [n_seqs, H, K, V] or null (zeros)
+    float* final_state;         // [n_seqs, H, K, V] or null (not written)
+    uint16_t* o;                // [tokens, H, V] bf16
+    int32_t H;
+    int32_t T;                  // tokens per sequence (fixed length)
+    int32_t n_seqs;
+    int32_t packed;
+    int32_t seg_chunks;         // fixed length: chunks per segment
+    int32_t segs_per_seq;       // fixed length: segments per sequence
+    int32_t n_segs;             // packed: segment slots in the tables
+    const int32_t* seq_start;   // packed: [n_seqs + 1] token offsets
+    const int32_t* vseq_start;  // packed: [n_segs + 1] first token of each segment
+    const int32_t* vfirst;      // packed: [n_seqs + 1] first segment of each sequence
+    const int32_t* final_map;   // packed: [n_segs] sequence whose final state a segment ends
+    int32_t warm_chunks;        // warm-up chunks before a segment that starts mid-sequence
+    float bound_limit;          // log2: a warm-up whose transitions are below this suffices
+    int64_t tok_limit;          // tokens in the batch
+};
+
 // Backward pass: the chunk-parallel gradient kernel (kda_bwd.hip).
 struct BwdArgs {
     const uint16_t* q;         // [tokens, H, K] bf16
@@ -161,6 +196,10 @@ void launch_prep(const PrepArgs& a, int K, bool gdn, int n_slots, hipStream_t st
 void launch_recur(const RecurArgs& a, int K, hipStream_t stream, RecurMode mode = RECUR_FWD,
                   const LaunchEvents* ev = nullptr);
 void launch_decode(const DecodeArgs& a, int K, bool gdn, hipStream_t stream);
+void launch_fused(const FusedArgs& a, int K, int V, bool gdn, int n_groups, hipStream_t stream,
+                  const LaunchEvents* ev = nullptr);
 int record_bytes(int K);
+// compute units of the current device (queried once per device)
+int device_cus();
 
 }  // namespace kda

@@ -47,8 +47,8 @@
  *    written).  An empty sequence returns its initial state.
  *  - Only K, V in {64, 128} are supported.  B * T must be < 2^31.  Token
  *    tensors (q, k, v, g, beta, o) may be NULL only when T == 0.
- *  - Alignment: q, k, v, g (KDA), dt_bias 16 bytes; o 8 bytes; workspace
- *    256 bytes.
+ *  - Alignment: q, k, v, g (KDA), dt_bias 16 bytes; o 16 bytes for
+ *    kda_fwd / gdn_fwd, 8 bytes elsewhere; workspace 256 bytes.
  *  - Ownership: the caller allocates and frees every buffer, including the
  *    workspace (at least *_workspace_size() bytes).  The library allocates
  *    nothing, keeps no pointer after it returns and never synchronises.
@@ -77,16 +77,34 @@ enum kda_status {
     KDA_ERR_LAUNCH = 4       /* a kernel launch failed */
 };
 
-/* Bytes of device workspace that kda_fwd needs (including what its automatic
- * sequence splitting needs, see kda_fwd_split).  num_seqs: the number of
- * packed sequences when cu_seqlens will be passed, else B.  Pure host
- * function; returns 0 for invalid sizes. */
+/* Bytes of device workspace that kda_fwd needs: the packed-sequence and
+ * segment tables when cu_seqlens is given (one alignment unit otherwise; a
+ * fixed-length call reads no workspace and accepts NULL).  num_seqs: the
+ * number of packed sequences when cu_seqlens will be passed, else B.  Pure
+ * host function; returns 0 for invalid sizes. */
 size_t kda_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                               int32_t num_seqs);
 
 /* KDA forward.  beta holds logits (sigmoid applied inside); lower_bound must
  * be finite and in [-5, 0]; scale must be finite (K^-0.5 is customary).
- * num_seqs is read only when cu_seqlens is non-NULL (then B must be 1). */
+ * num_seqs is read only when cu_seqlens is non-NULL (then B must be 1).
+ *
+ * One launch computes the whole pass: a workgroup per (sequence segment,
+ * head) forms each 32-token chunk's decayed operands, intra-chunk matrices
+ * and (I + A)^-1 in LDS and runs the recurrence over them, so HBM sees the
+ * inputs and states read once and the outputs written once.  The FlashKDA
+ * summary (discuss.pytorch.kr, section "커널 퓨전(Kernel Fusion) 전략의 분리")
+ * describes the same two computations as a token-parallel and a sequential
+ * kernel; here they are wave roles of one workgroup.  When the (sequence,
+ * head) pairs are fewer than the compute units, sequences are cut into
+ * segments that run in parallel; a segment that starts mid-sequence begins
+ * two chunks early from a zero state and keeps that start only if those
+ * chunks' transitions provably scale the true entering state by less than
+ * 2^-40 (for one token ||(I - b k^ k^T) Diag(a)||_2 <= max_c a_c), else it
+ * restarts from the sequence start: the result is the unsplit one up to
+ * rounding and that bound.  The FlashQLA summary (section "핵심 기능")
+ * describes intra-card parallelism switched on when the gate's decay allows
+ * it.  o must be 16-byte aligned. */
 int kda_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
             const uint16_t* beta, const float* A_log, const float* dt_bias, float lower_bound,
             float scale, const float* initial_state, float* final_state,
@@ -107,7 +125,51 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
             int32_t K, int32_t V, uint16_t* o, void* workspace, size_t workspace_bytes,
             void* stream);
 
-/* kda_fwd / gdn_fwd with explicit control of sequence splitting.
+/* kda_fwd / gdn_fwd with explicit segments: segment_chunks > 0 cuts every
+ * sequence into segments of that many 32-token chunks, < 0 keeps whole
+ * sequences, 0 is kda_fwd's automatic choice.  The workspace must hold
+ * kda_fwd_segmented_workspace_size(..., segment_chunks) bytes; everything
+ * else is as for kda_fwd / gdn_fwd. */
+size_t kda_fwd_segmented_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                        int32_t num_seqs, int32_t segment_chunks);
+
+int kda_fwd_segmented(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* g, const uint16_t* beta, const float* A_log,
+                      const float* dt_bias, float lower_bound, float scale,
+                      const float* initial_state, float* final_state, const int32_t* cu_seqlens,
+                      int32_t num_seqs, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                      uint16_t* o, void* workspace, size_t workspace_bytes,
+                      int32_t segment_chunks, void* stream);
+
+int gdn_fwd_segmented(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                      const uint16_t* beta, float scale, const float* initial_state,
+                      float* final_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                      int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o,
+                      void* workspace, size_t workspace_bytes, int32_t segment_chunks,
+                      void* stream);
+
+/* Measurement forms of kda_fwd / gdn_fwd: the same call, plus two events
+ * (hipEvent_t handles created with timing enabled) into which the forward
+ * kernel's own start and end are recorded on the GPU (it is launched with
+ * hipExtLaunchKernel), so hipEventElapsedTime gives its execution time
+ * without the dispatch gap of events recorded between kernels.  Both NULL:
+ * the plain call; exactly one NULL: KDA_ERR_INVALID_ARG. */
+int kda_fwd_timed(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                  const uint16_t* beta, const float* A_log, const float* dt_bias,
+                  float lower_bound, float scale, const float* initial_state,
+                  float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                  int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                  size_t workspace_bytes, void* stream, void* start_event, void* stop_event);
+
+int gdn_fwd_timed(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                  const uint16_t* beta, float scale, const float* initial_state,
+                  float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                  int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
+                  size_t workspace_bytes, void* stream, void* start_event, void* stop_event);
+
+/* The two-stage form of kda_fwd / gdn_fwd (kda_prep then kda_recur, with the
+ * chunk records in the workspace), with explicit control of its sequence
+ * splitting.
  *
  * A sequence is one chain of dependent chunk steps, so a batch of few long
  * sequences leaves most of the GPU idle.  Splitting cuts every sequence into
@@ -121,11 +183,12 @@ int gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
  * long sequences, the FlashQLA summary (section "핵심 기능") switches it on
  * from the gate's decay.
  *
- * segment_chunks: < 0 never split; 0 automatic (what kda_fwd / gdn_fwd do:
- * only when the sequences are long and (sequence, head) pairs too few to
- * fill the GPU); > 0 segments of that many 32-token chunks.  The workspace
- * must hold kda_fwd_split_workspace_size(..., segment_chunks) bytes; the
- * other arguments, layouts and errors are those of kda_fwd / gdn_fwd. */
+ * segment_chunks: < 0 never split; 0 automatic (only when the sequences are
+ * long and the (sequence, head, 32-column) workgroups too few to fill the
+ * GPU); > 0 segments of that many 32-token chunks.  The workspace must hold
+ * kda_fwd_split_workspace_size(..., segment_chunks) bytes (with -1, also the
+ * workspace of kda_prep / kda_recur); the other arguments, layouts and
+ * errors are those of kda_fwd / gdn_fwd (o 8-byte aligned). */
 size_t kda_fwd_split_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                                     int32_t num_seqs, int32_t segment_chunks);
 
@@ -142,8 +205,10 @@ int gdn_fwd_split(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
                   int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
                   size_t workspace_bytes, int32_t segment_chunks, void* stream);
 
-/* The two stages of kda_fwd / gdn_fwd, callable on their own (same
- * conventions; kda_fwd is exactly kda_prep followed by kda_recur).
+/* The two stages of the two-stage form, callable on their own (same
+ * conventions; kda_fwd_split with segment_chunks = -1 is exactly kda_prep
+ * followed by kda_recur).  Workspace: kda_fwd_split_workspace_size(...,
+ * -1) bytes.
  *
  * kda_prep / gdn_prep: the token-parallel stage.  Gate activation, sigmoid
  * of beta (KDA), in-chunk cumulative decay, q/k L2 norm, the intra-chunk

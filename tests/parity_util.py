@@ -24,15 +24,22 @@ def say(msg):
     sys.stdout.flush()
 
 
-def gpu_run(w, device="cuda:0", output_final_state=True, **kw):
+def gpu_run(w, device="cuda:0", output_final_state=True, path="fused", **kw):
+    """One forward pass of w on the GPU: path "fused" is the single-launch pass
+    (kda_fwd / gdn_fwd), "staged" the two-stage one (kda_fwd_split / gdn_fwd_split)."""
     d = w.to(device)
+    staged = path == "staged"
+    if path not in ("fused", "staged"):
+        raise ValueError(path)
     if w.kind == "kda":
-        o, S = kda.kda_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
-                           w.lower_bound, w.scale, d["initial_state"], output_final_state,
-                           d["cu_seqlens"], **kw)
+        fn = kda.kda_fwd_split if staged else kda.kda_fwd
+        o, S = fn(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
+                  w.lower_bound, w.scale, d["initial_state"], output_final_state,
+                  d["cu_seqlens"], **kw)
     else:
-        o, S = kda.gdn_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale,
-                           d["initial_state"], output_final_state, d["cu_seqlens"], **kw)
+        fn = kda.gdn_fwd_split if staged else kda.gdn_fwd
+        o, S = fn(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, d["initial_state"],
+                  output_final_state, d["cu_seqlens"], **kw)
     torch.cuda.synchronize()
     return o, S
 
@@ -72,7 +79,7 @@ def check_parity(w, heads=None, first_tokens=None, **kw):
     the comparison) to a subset of heads.  ``first_tokens`` adds a max-abs check on
     the first tokens of every sequence (where the initial state still matters)."""
     say(f"[parity] {w.name}: B={w.B} T={w.T} H={w.H} K={w.K} V={w.V} N={w.n_seqs}"
-        f" heads={'all' if heads is None else heads}")
+        f" heads={'all' if heads is None else heads} {kw if kw else ''}")
     o, S = gpu_run(w, **kw)
     ro, rS = oracle_run(w, heads)
     go = to64(o, heads, 2)

@@ -41,14 +41,28 @@ def test_workspace_size_formula(lib):
     C = 32  # tokens per chunk
     rec = 3 * C * 128 * 2 + 2 * C * C * 2 + 128 * 4  # bytes per (chunk, head) at K=128
     B, T, H, N = 2, 2048, 32, 2
-    meta = 256
+    al = lambda x: (x + 255) // 256 * 256
+    meta = al(2 * 4 * (N + 1))
     slots = (B * T + C - 1) // C + N  # the packed-sequence bound covers both layouts
-    bound = (slots * H * 4 + 255) // 256 * 256  # one fp32 transition bound per (chunk, head)
+    bound = al(slots * H * 4)  # one fp32 transition bound per (chunk, head)
     want = meta + slots * H * rec + bound
-    assert kda.workspace_size(B, T, H, 128, 128) == want  # 64 pairs x 4 blocks: no splitting
-    assert kda.workspace_size(B, T, H, 128, 128, segment_chunks=-1) == want
-    assert kda.workspace_size(1, 100, 1, 96, 128) == 0  # unsupported K
-    assert kda.workspace_size(0, 100, 1, 128, 128) == 0
+    # the two-stage pass: 64 pairs x 4 blocks, no splitting
+    assert kda.workspace_size(B, T, H, 128, 128, path="staged") == want
+    assert kda.workspace_size(B, T, H, 128, 128, segment_chunks=-1, path="staged") == want
+    # the single-launch pass: only the packed layout's tables (segments of
+    # L = max(8, ceil(slots H / 512)) chunks, at most N + ceil(slots / L) of them)
+    L = max(8, -(-slots * H // 512))
+    nv = N + -(-slots // L)
+    fused = meta + al(4 * (2 * (nv + 1) + nv + N + 1))
+    assert kda.workspace_size(B, T, H, 128, 128) == fused
+    assert fused < 4096 < want
+    L = 16
+    nv = N + -(-slots // L)
+    assert kda.workspace_size(B, T, H, 128, 128, segment_chunks=L) == \
+        meta + al(4 * (2 * (nv + 1) + nv + N + 1))
+    for path in ("fused", "staged"):
+        assert kda.workspace_size(1, 100, 1, 96, 128, path=path) == 0  # unsupported K
+        assert kda.workspace_size(0, 100, 1, 128, 128, path=path) == 0
 
 
 def _kda_call(lib, **over):
@@ -69,12 +83,48 @@ def _kda_call(lib, **over):
     (dict(scale=float("inf")), 1),
     (dict(K=96), 2), (dict(V=256), 2),
     (dict(cu=FAKE, B=2, N=2), 1), (dict(cu=FAKE, N=0), 1),
-    (dict(ws=None), 3), (dict(wsb=100), 3), (dict(ws=ctypes.c_void_p(0x1010)), 3),
+    # packed sequences need the segment tables in the workspace
+    (dict(cu=FAKE, N=2, ws=None), 3), (dict(cu=FAKE, N=2, wsb=100), 3),
+    (dict(cu=FAKE, N=2, ws=ctypes.c_void_p(0x1010)), 3),
     (dict(q=ctypes.c_void_p(0x1002)), 1), (dict(dt_bias=ctypes.c_void_p(0x1008)), 1),
+    (dict(o=ctypes.c_void_p(0x1008)), 1), (dict(h0=ctypes.c_void_p(0x1004)), 1),
+    (dict(hT=ctypes.c_void_p(0x1008)), 1), (dict(beta=ctypes.c_void_p(0x1001)), 1),
     (dict(B=1 << 16, T=1 << 15), 1),
 ])
 def test_kda_rejects_on_host(lib, over, code):
     assert _kda_call(lib, **over) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ws=None), 3), (dict(wsb=100), 3), (dict(ws=ctypes.c_void_p(0x1010)), 3),
+    (dict(g=None), 1), (dict(K=96), 2),
+])
+def test_two_stage_rejects_on_host(lib, over, code):
+    """kda_fwd_split keeps its record workspace for fixed-length batches too."""
+    a = dict(g=FAKE, K=128, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    st = lib.kda_fwd_split(FAKE, FAKE, FAKE, a["g"], FAKE, FAKE, FAKE, -5.0, 0.088, None, None,
+                           None, 0, 1, 16, 1, a["K"], 128, FAKE, a["ws"], a["wsb"], -1, None)
+    assert st == code
+
+
+def test_segmented_and_timed_check_like_kda_fwd(lib):
+    base = [FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, -5.0, 0.088, None, None, None, 0, 1, 16,
+            1, 128, 128, FAKE, FAKE, 1 << 30]
+    assert lib.kda_fwd_segmented(*base, 4, None) == 1  # null g
+    assert lib.kda_fwd_timed(*base, None, None, None) == 1
+    base[3] = FAKE
+    ev = ctypes.c_void_p(0x2000)
+    assert lib.kda_fwd_timed(*base, None, ev, None) == 1  # one event of two
+    assert lib.kda_fwd_timed(*base, None, None, ev) == 1
+    base[16] = 32
+    assert lib.kda_fwd_segmented(*base, 4, None) == 2
+    gbase = [FAKE, FAKE, FAKE, None, FAKE, 0.1, None, None, None, 0, 1, 16, 1, 128, 128, FAKE,
+             FAKE, 1 << 30]
+    assert lib.gdn_fwd_segmented(*gbase, 4, None) == 1
+    assert lib.gdn_fwd_timed(*gbase, None, None, None) == 1
+    gbase[3] = FAKE
+    assert lib.gdn_fwd_timed(*gbase, None, ev, None) == 1
 
 
 def test_gdn_rejects_on_host(lib):
@@ -86,7 +136,9 @@ def test_gdn_rejects_on_host(lib):
     assert lib.gdn_fwd(*args) == 2  # unsupported K
     args[13] = 128
     args[17] = 10
-    assert lib.gdn_fwd(*args) == 3  # workspace too small
+    assert lib.gdn_fwd_split(*args[:18], -1, None) == 3  # two-stage workspace too small
+    args[8], args[9] = FAKE, 3
+    assert lib.gdn_fwd(*args) == 3  # packed: segment tables do not fit
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
@@ -129,16 +181,16 @@ def test_split_workspace_grows_with_segments(lib):
     """Explicit splitting adds the segment tables, flags, two [segments, H, K, V]
     state buffers and the [segments, H, K, K] transitions."""
     B, T, H, K, V = 1, 8192, 2, 128, 128
-    plain = kda.workspace_size(B, T, H, K, V, segment_chunks=-1)
+    plain = kda.workspace_size(B, T, H, K, V, segment_chunks=-1, path="staged")
     slots = (B * T + 31) // 32 + 1
     for L in (16, 64):
         nv = 1 + (slots + L - 1) // L
-        extra = kda.workspace_size(B, T, H, K, V, segment_chunks=L) - plain
+        extra = kda.workspace_size(B, T, H, K, V, segment_chunks=L, path="staged") - plain
         states = nv * H * K * V * 4
         assert extra >= 2 * states + nv * H * K * K * 4
         assert extra < 2 * states + nv * H * K * K * 4 + 4096
     # automatic: 2 heads x 4 column blocks is far too few workgroups, so it splits
-    assert kda.workspace_size(B, T, H, K, V) > plain
+    assert kda.workspace_size(B, T, H, K, V, path="staged") > plain
 
 
 def _kda_bwd_call(lib, **over):
@@ -170,7 +222,7 @@ def test_kda_bwd_rejects_on_host(lib, over, code):
 
 
 def test_kda_bwd_needs_the_larger_workspace(lib):
-    fwd = kda.workspace_size(1, 16, 1, 128, 128)
+    fwd = kda.workspace_size(1, 16, 1, 128, 128, path="staged")
     bwd = kda.bwd_workspace_size(1, 16, 1, 128, 128)
     assert bwd > fwd > 0
     # enough for the forward pass, not for the backward: rejected before any launch
@@ -206,7 +258,7 @@ def test_chunk_kda_rejects_unsupported_variants(flag, value):
 
 
 def test_fwd_save_needs_the_backward_workspace(lib):
-    fwd = kda.workspace_size(1, 16, 1, 128, 128)
+    fwd = kda.workspace_size(1, 16, 1, 128, 128, path="staged")
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, 0.088, None, None, None, 0, 1, 16, 1,
             128, 128, FAKE, FAKE, fwd, None]
     assert lib.kda_fwd_save(*args) == 3  # enough for kda_fwd only

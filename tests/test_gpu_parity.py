@@ -155,16 +155,17 @@ def test_state_continuation():
         assert_close(f"continuation@{T1} state", to64(S2), to64(S))
 
 
-def test_deterministic_and_fully_written():
+@pytest.mark.parametrize("path", ["fused", "staged"])
+def test_deterministic_and_fully_written(path):
     """Two runs are bitwise identical, including when the output, state and
     workspace buffers start out filled with NaN (no element is left unwritten)."""
     w = inputs.kda_workload(2, 250, 3, 128, 128, seed=3900, init_std=0.05)
-    o1, S1 = gpu_run(w)
+    o1, S1 = gpu_run(w, path=path)
     nan_o = torch.full_like(o1, float("nan"))
     nan_S = torch.full_like(S1, float("nan"))
-    ws = torch.full((kda.workspace_size(2, 250, 3, 128, 128),), 0xFF, dtype=torch.uint8,
-                    device=o1.device)
-    o2, S2 = gpu_run(w, workspace=ws, out=nan_o, final_out=nan_S)
+    ws = torch.full((kda.workspace_size(2, 250, 3, 128, 128, path=path),), 0xFF,
+                    dtype=torch.uint8, device=o1.device)
+    o2, S2 = gpu_run(w, path=path, workspace=ws, out=nan_o, final_out=nan_S)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
@@ -251,37 +252,70 @@ WIDE = [(3, 1000, 48, 128, 128), (5, 700, 40, 64, 64), (2, 1111, 80, 128, 64),
         (3, 513, 48, 64, 128)]
 
 
+@pytest.mark.parametrize("path", ["fused", "staged"])
 @pytest.mark.parametrize("B,T,H,K,V", WIDE, ids=lambda x: str(x))
-def test_wide_recurrence_grids(B, T, H, K, V):
+def test_wide_recurrence_grids(B, T, H, K, V, path):
     w = inputs.kda_workload(B, T, H, K, V, seed=4500 + T + H, dt_bias_value=-6.0,
                             init_std=0.05, name=f"wide_B{B}_T{T}_H{H}_K{K}_V{V}")
-    check_parity(w, heads=[0, H // 2 + 1, H - 1], first_tokens=32)
+    check_parity(w, heads=[0, H // 2 + 1, H - 1], first_tokens=32, path=path)
 
 
-def test_wide_recurrence_packed():
+@pytest.mark.parametrize("path", ["fused", "staged"])
+def test_wide_recurrence_packed(path):
     # 40 packed sequences (one empty, several shorter than a chunk) x 8 heads
     lengths = [(37 * i) % 301 for i in range(40)]
     w = inputs.kda_workload(1, 0, 8, 128, 128, seed=4600, dt_bias_value=-6.0,
                             init_std=0.05, lengths=lengths, name="wide_packed_40x8")
-    check_parity(w, heads=[0, 3, 7], first_tokens=32)
+    check_parity(w, heads=[0, 3, 7], first_tokens=32, path=path)
 
 
-def test_wide_recurrence_gdn():
+@pytest.mark.parametrize("path", ["fused", "staged"])
+def test_wide_recurrence_gdn(path):
     # the scalar-gate variant on the same large-grid path (slow decay)
     w = inputs.gdn_workload(3, 600, 48, 128, 128, seed=4700, init_std=0.05, decay_shift=-6.0,
                             name="wide_gdn_B3_T600_H48")
-    check_parity(w, heads=[0, 20, 47], first_tokens=32)
+    check_parity(w, heads=[0, 20, 47], first_tokens=32, path=path)
 
 
-def test_stages_equal_fused_call():
-    """kda_prep followed by kda_recur (the two ABI stages, as the benchmark times
-    them) gives bitwise the same result as kda_fwd; the same for gdn_prep."""
+@pytest.mark.parametrize("path", ["fused", "staged"])
+def test_full_config_sampled_small(path):
+    """The config-0 workload on both paths (the tiny case, every head)."""
+    check_parity(inputs.config(0), path=path)
+
+
+def test_fused_timed_equals_plain():
+    """kda_fwd_timed / gdn_fwd_timed (the measurement forms of the single-launch
+    pass) give bitwise the plain results and a positive kernel time."""
+    for w in (inputs.kda_workload(2, 300, 3, 128, 128, seed=4900, init_std=0.05),
+              inputs.kda_workload(1, 0, 4, 64, 128, seed=4901, lengths=[70, 0, 33, 1]),
+              inputs.gdn_workload(2, 200, 2, 128, 128, seed=4902, init_std=0.05)):
+        o, S = gpu_run(w)
+        stream = torch.cuda.current_stream()
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for x in ev:
+            x.record(stream)
+        o2, S2 = gpu_run(w, events=ev)
+        assert torch.equal(o, o2) and torch.equal(S, S2)
+        ms = ev[0].elapsed_time(ev[1])
+        say(f"  {w.name} fused: {ms * 1e3:.1f} us")
+        assert 0.0 < ms < 1000.0, ms
+
+
+def staged_ws(w):
+    return torch.empty(kda.workspace_size(w.B, w.T, w.H, w.K, w.V, w.n_seqs, w.kind,
+                                          segment_chunks=-1, path="staged"),
+                       dtype=torch.uint8, device="cuda:0")
+
+
+def test_stages_equal_two_stage_call():
+    """kda_prep followed by kda_recur (the two ABI stages) gives bitwise the same
+    result as the unsplit two-stage call kda_fwd_split(segment_chunks=-1); the
+    same for gdn_prep."""
     for w in (inputs.kda_workload(2, 200, 3, 128, 128, seed=4200, init_std=0.05),
               inputs.gdn_workload(1, 0, 2, 128, 64, seed=4300, lengths=[50, 0, 77])):
-        o, S = gpu_run(w)
+        o, S = gpu_run(w, path="staged", segment_chunks=-1)
         d = w.to("cuda:0")
-        ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.K, w.V, w.n_seqs),
-                         dtype=torch.uint8, device="cuda:0")
+        ws = staged_ws(w)
         if w.kind == "kda":
             kda.kda_prep(d["q"], d["k"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
                          w.lower_bound, ws, d["cu_seqlens"], V=w.V)
@@ -302,10 +336,9 @@ def test_timed_stages_equal_plain_stages():
     for w in (inputs.kda_workload(2, 300, 3, 128, 128, seed=4800, init_std=0.05),
               inputs.kda_workload(1, 0, 4, 64, 128, seed=4801, lengths=[70, 0, 33, 1]),
               inputs.kda_workload(3, 200, 48, 128, 128, seed=4802, init_std=0.05)):
-        o, S = gpu_run(w)
+        o, S = gpu_run(w, path="staged", segment_chunks=-1)
         d = w.to("cuda:0")
-        ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.K, w.V, w.n_seqs),
-                         dtype=torch.uint8, device="cuda:0")
+        ws = staged_ws(w)
         stream = torch.cuda.current_stream()
         ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for n in ("prep", "recur")}

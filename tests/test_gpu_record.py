@@ -201,8 +201,8 @@ def test_prep_record_matches_chunked_oracle(case):
         w = inputs.gdn_workload(B, T, H, K, V, seed, name=case)
     say(f"[record] {case}: B={B} T={T} H={H} K={K}")
     d = w.to("cuda:0")
-    ws = torch.empty(kda.workspace_size(B, T, H, K, V, kind=kind), dtype=torch.uint8,
-                     device="cuda:0")
+    ws = torch.empty(kda.workspace_size(B, T, H, K, V, kind=kind, segment_chunks=-1,
+                                        path="staged"), dtype=torch.uint8, device="cuda:0")
     if kind == "kda":
         kda.kda_prep(d["q"], d["k"], d["g"], d["beta"], d["A_log"], d["dt_bias"],
                      w.lower_bound, ws, V=V)

@@ -1,9 +1,19 @@
-"""GPU parity of sequence splitting (kda_fwd_split / gdn_fwd_split and the
-automatic choice of kda_fwd) against the fp64 oracle, in the regimes of the
-transition bound: a segment that forgets its entering state within a few
-chunks (the transition is skipped and the first pass runs only the decay
-window), one that forgets it within part of the segment, one that keeps it
-(the transition is computed and applied by the scan) and no decay at all."""
+"""GPU parity of sequence splitting against the fp64 oracle, for both forward
+paths:
+
+  staged (kda_fwd_split / gdn_fwd_split): segments run from a zero state, a
+    scan over the segment transitions carries the state across them; a
+    transition whose bound shows it negligible is skipped and the first pass
+    then runs only the decay window;
+  fused (kda_fwd_segmented / gdn_fwd_segmented and the automatic choice of
+    kda_fwd): a segment starts two chunks early from a zero state and keeps
+    that start only if the bound of those two chunks is below 2^-40, else it
+    restarts from the sequence start.
+
+The cases cover the regimes of both bounds: state forgotten within a few
+chunks (default decay), within part of a segment, kept across segments (slow
+decay: the staged scan applies transitions, the fused segments restart) and
+no decay at all."""
 import pytest
 import torch
 
@@ -42,33 +52,58 @@ CASES = [
 ]
 
 
+PATHS = ["fused", "staged"]
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name,make,seg", CASES, ids=[c[0] for c in CASES])
-def test_split_matches_oracle(name, make, seg):
+def test_split_matches_oracle(name, make, seg, path):
     w = make()
-    say(f"[split] {name}: segment_chunks={seg}")
-    check_parity(w, first_tokens=32, segment_chunks=seg)
+    say(f"[split] {name}: path={path} segment_chunks={seg}")
+    check_parity(w, first_tokens=32, segment_chunks=seg, path=path)
 
 
-def test_split_equals_unsplit():
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dt_bias", [-6.0, 0.0])
+def test_split_equals_unsplit(path, dt_bias):
     """Split and unsplit runs agree to rounding (every segment boundary inside
-    the sequence, slow decay so every boundary carries state)."""
-    w = inputs.kda_workload(1, 2500, 2, 128, 128, seed=6600, dt_bias_value=-6.0, init_std=0.05)
-    o1, S1 = gpu_run(w, segment_chunks=-1)
-    o2, S2 = gpu_run(w, segment_chunks=8)
+    the sequence; slow decay: every boundary carries state, default decay: the
+    fused segments keep their zero start)."""
+    w = inputs.kda_workload(1, 2500, 2, 128, 128, seed=6600, dt_bias_value=dt_bias,
+                            init_std=0.05)
+    o1, S1 = gpu_run(w, path=path, segment_chunks=-1)
+    o2, S2 = gpu_run(w, path=path, segment_chunks=8)
     assert_close("o split vs unsplit", to64(o2), to64(o1))
     assert_close("state split vs unsplit", to64(S2), to64(S1))
 
 
-def test_automatic_split_long_sequence():
-    """kda_fwd splits on its own for one long sequence with few heads."""
-    w = inputs.kda_workload(1, 16384, 2, 128, 128, seed=6700, dt_bias_value=-6.0,
-                            init_std=0.05, name="auto_split_T16384_H2")
-    check_parity(w, first_tokens=32)
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("dt_bias", [-6.0, 0.0])
+def test_automatic_split_long_sequence(path, dt_bias):
+    """The automatic choice splits one long sequence with few heads on its own."""
+    w = inputs.kda_workload(1, 16384, 2, 128, 128, seed=6700, dt_bias_value=dt_bias,
+                            init_std=0.05, name=f"auto_split_T16384_H2_dt{dt_bias:g}")
+    check_parity(w, first_tokens=32, path=path)
 
 
-def test_split_deterministic():
+@pytest.mark.parametrize("path", PATHS)
+def test_split_deterministic(path):
     w = inputs.kda_workload(1, 2000, 2, 128, 128, seed=6800, dt_bias_value=-6.0, init_std=0.05)
-    o1, S1 = gpu_run(w, segment_chunks=4)
-    o2, S2 = gpu_run(w, segment_chunks=4)
+    o1, S1 = gpu_run(w, path=path, segment_chunks=4)
+    o2, S2 = gpu_run(w, path=path, segment_chunks=4)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3, 5])
+def test_fused_segments_short_and_warm_up(seg):
+    """Fused segments shorter than, equal to and longer than the two warm-up
+    chunks, on a ragged packed batch, default decay (the zero start is kept)
+    and GDN; every segment's outputs and the final states checked."""
+    lengths = [0, 31, 32, 33, 200, 7, 513, 96]
+    w = inputs.kda_workload(1, 0, 3, 128, 128, seed=6900 + seg, init_std=0.05,
+                            lengths=lengths, name=f"fused_seg{seg}_packed")
+    check_parity(w, first_tokens=32, segment_chunks=seg)
+    w = inputs.gdn_workload(2, 300, 2, 64, 128, seed=6950 + seg, init_std=0.05,
+                            name=f"fused_seg{seg}_gdn")
+    check_parity(w, first_tokens=32, segment_chunks=seg)
