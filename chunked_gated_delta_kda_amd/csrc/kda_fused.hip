@@ -15,19 +15,23 @@
 //   prep waves (K/32): wave p owns channels 32p .. 32p+31 of both 16-token
 //     blocks of a chunk.  Lane m + 16g holds tokens m and 16 + m and the eight
 //     channels 32p + 8g .. +7, i.e. its slice of a 16x16x32 MFMA operand.  Per
-//     chunk, over three iterations: load q, k, g (and beta); the partial sums
-//     of squares of q and k over its channels (phase N); the gate, the
-//     in-block prefix sums, the decayed operands written into the chunk's LDS
-//     record, and partial intra-chunk products over its channels (phase A).
+//     chunk, over two iterations: load q, k, g (and beta); then (phase A) the
+//     gate, the in-block prefix sums, the decayed operands written into the
+//     chunk's LDS record, partial intra-chunk products over its channels and
+//     partial squared norms of q and k (diagonals of MFMA products of the raw
+//     inputs).  q and k are never normalised elementwise: the record holds
+//     the raw rows and the per-token factors 1/||k||, 1/||q|| are applied to
+//     the 16x16 tiles, to V - KG S, to U' and to the output.
 //   compute waves (4): wave w owns V/4 value columns of the [K, V] state in
 //     fp32 MFMA accumulators for the whole segment and runs the recurrence of
 //     kda_recur.hip on the LDS record.  In turn, one of them also finishes a
-//     chunk's record (phase B): the sum of the partial products, the masks and
-//     beta, the in-block inverses by forward substitution, the coupling block
+//     chunk's record (phase B): the norms, the sum of the partial products,
+//     the masks and beta, both in-block inverses at once by forward
+//     substitution (one per half of the wave), the coupling block
 //     T10 = -T11 A10 T00, and Tb and Aqk.
 // One barrier per iteration.  In iteration i the compute waves run chunk i,
-// phase B finishes chunk i+1, phase A fills chunk i+2, phase N covers chunk
-// i+3 and the loads of chunk i+4 are issued; three records are live in LDS.
+// phase B finishes chunk i+1 and phase A fills chunk i+2; three records are
+// live in LDS.
 //
 // Sequence segments.  A (sequence, head) pair is one chain of chunk steps, so
 // long sequences are cut into segments of L chunks that run in parallel.  A
@@ -64,14 +68,17 @@ struct FusedLayout {
     static constexpr int REC = 0;                                   // [NBUF][R::BYTES]
     static constexpr int PART = REC + NBUF * R::BYTES;              // [2][NPW][6][64] floatx4
     static constexpr int PART_SLOT = NPW * 6 * 64 * 16;
-    static constexpr int NORM = PART + 2 * PART_SLOT;               // [2][NPW][64] float
-    static constexpr int RMAX = NORM + 2 * NPW * 64 * 4;            // [2][NPW][32] float
+    static constexpr int NRM = PART + 2 * PART_SLOT;                // [2][NPW][64] float
+    static constexpr int RMAX = NRM + 2 * NPW * 64 * 4;             // [2][NPW][32] float
     static constexpr int BETA = RMAX + 2 * NPW * 32 * 4;            // [2][32] float
     static constexpr int GTOK = BETA + 2 * 32 * 4;                  // [2][32] float
     static constexpr int TOT = GTOK + 2 * 32 * 4;                   // [NPW][64] float
     static constexpr int AMAT = TOT + NPW * 64 * 4;                 // [2][256] float
-    static constexpr int T00 = AMAT + 2 * 256 * 4;                  // [256] float
-    static constexpr int MISC = T00 + 256 * 4;                      // bound sum
+    // [2][3][256] float: per chunk (slot x & 1) Tb00 row-major, T11^T and A10
+    // in D layout, from phase B for the coupling block the compute waves form
+    static constexpr int CPL = AMAT + 2 * 256 * 4;
+    static constexpr int INVN = CPL + 2 * 3 * 256 * 4;              // [NBUF][64] float
+    static constexpr int MISC = INVN + NBUF * 64 * 4;               // bound sum
     static constexpr int BYTES = MISC + 16;
     static_assert(BYTES <= 160 * 1024, "LDS of one CU");
 };
@@ -118,6 +125,12 @@ __device__ __forceinline__ int opaque_lane() {
 // loads are outstanding (vmcnt 8 / 0; expcnt and lgkmcnt left at their maximum)
 constexpr int VMCNT_8 = 0x0F78;
 constexpr int VMCNT_0 = 0x0F70;
+
+// element i (runtime, 0..3) of v
+__device__ __forceinline__ float pick(floatx4 v, int i) {
+    const float lo = i & 1 ? v[1] : v[0], hi = i & 1 ? v[3] : v[2];
+    return i & 2 ? hi : lo;
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -218,7 +231,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         if (!is_cw) {
             const float* dp = a.dt_bias + (int64_t)h * K + 32 * p + 8 * g;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dt[e] = dp[e];
+            for (int e = 0; e < 8; ++e) dt[e] = dp[e] * LOG2E;  // the gate works in log2 units
         }
     }
 
@@ -240,7 +253,10 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
     // the warm-up chunks' bound is complete at iteration out_from (phase B of
     // the last one ran an iteration earlier); every wave reads the same value
     auto failed_bound = [&](int it) __attribute__((always_inline)) {
-        return !exact && it == out_from && !(misc[0] < a.bound_limit);
+        if (exact || it != out_from) return false;
+        // the LDS read stays here (not hoisted into every iteration)
+        asm volatile("" ::: "memory");
+        return !(misc[0] < a.bound_limit);
     };
 
         // ---------------------------------------------------------- prep waves
@@ -251,51 +267,24 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             (void)lr; (void)lg;
             const int64_t ct0 = chunk_t0(x);
             const int64_t r0 = ct0 * a.H + h;  // the chunk's first (token, head) row
-            const uint16_t* qb = a.q + r0 * K;
-            const uint16_t* kb = a.k + r0 * K;
-            const uint16_t* gb = GDN ? nullptr : a.g_kda + r0 * K;
-            const float* gdb = GDN ? a.g_gdn + r0 : nullptr;
-            const uint16_t* bt = a.beta + r0;
+            // uniform bases and 32-bit lane byte offsets (one address add per load)
+            const char* qb = reinterpret_cast<const char*>(a.q + r0 * K);
+            const char* kb = reinterpret_cast<const char*>(a.k + r0 * K);
+            const char* gb = GDN ? nullptr : reinterpret_cast<const char*>(a.g_kda + r0 * K);
+            const char* gdb = GDN ? reinterpret_cast<const char*>(a.g_gdn + r0) : nullptr;
+            const char* bt = reinterpret_cast<const char*>(a.beta + r0);
             const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
-            const int cb = 32 * p + 8 * g;
+            const uint32_t cb = 32 * p + 8 * g;
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 // padding rows re-read the chunk's first row
-                const int r = 16 * b + m < nvalid ? (16 * b + m) * a.H : 0;
-                d.q[b] = *reinterpret_cast<const u32x4*>(qb + r * K + cb);
-                d.k[b] = *reinterpret_cast<const u32x4*>(kb + r * K + cb);
-                if constexpr (!GDN) d.g[b] = *reinterpret_cast<const u32x4*>(gb + r * K + cb);
-                else d.gd[b] = gdb[r];
-                d.braw[b] = bt[r];
-            }
-        };
-        auto phase_n = [&](const PIn& d, int x) __attribute__((always_inline)) {
-            const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
-            (void)lr; (void)lg;
-            float sq[2], sk[2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                sq[b] = 0.f;
-                sk[b] = 0.f;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float q0 = bf_lo(d.q[b][u]), q1 = bf_hi(d.q[b][u]);
-                    const float k0 = bf_lo(d.k[b][u]), k1 = bf_hi(d.k[b][u]);
-                    sq[b] = fmaf(q0, q0, fmaf(q1, q1, sq[b]));
-                    sk[b] = fmaf(k0, k0, fmaf(k1, k1, sk[b]));
-                }
-                sq[b] += __shfl_xor(sq[b], 16, 64);
-                sq[b] += __shfl_xor(sq[b], 32, 64);
-                sk[b] += __shfl_xor(sk[b], 16, 64);
-                sk[b] += __shfl_xor(sk[b], 32, 64);
-            }
-            if (g == 0) {
-                float* nb = reinterpret_cast<float*>(lds + L::NORM) + ((x & 1) * NPW + p) * 64;
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    nb[16 * b + m] = sq[b];
-                    nb[32 + 16 * b + m] = sk[b];
-                }
+                const uint32_t r = 16 * b + m < nvalid ? (uint32_t)(16 * b + m) * (uint32_t)a.H : 0u;
+                const uint32_t off = (r * K + cb) * 2u;
+                d.q[b] = *reinterpret_cast<const u32x4*>(qb + off);
+                d.k[b] = *reinterpret_cast<const u32x4*>(kb + off);
+                if constexpr (!GDN) d.g[b] = *reinterpret_cast<const u32x4*>(gb + off);
+                else d.gd[b] = *reinterpret_cast<const float*>(gdb + r * 4u);
+                d.braw[b] = *reinterpret_cast<const uint16_t*>(bt + r * 2u);
             }
         };
         auto phase_a = [&](const PIn& d, int x) __attribute__((always_inline)) {
@@ -305,20 +294,11 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
             const int64_t ct0 = chunk_t0(x);
             const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
-            float vmask[2], iq[2], ik[2], bsig[2];
-            const float* nb = reinterpret_cast<const float*>(lds + L::NORM) + slot * NPW * 64;
+            float vmask[2], bsig[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 const bool valid = 16 * b + m < nvalid;
                 vmask[b] = valid ? 1.f : 0.f;
-                float sq = 0.f, sk = 0.f;
-#pragma unroll
-                for (int pp = 0; pp < NPW; ++pp) {
-                    sq += nb[pp * 64 + 16 * b + m];
-                    sk += nb[pp * 64 + 32 + 16 * b + m];
-                }
-                iq[b] = rsq_hw(sq + NORM_EPS) * vmask[b];
-                ik[b] = rsq_hw(sk + NORM_EPS) * vmask[b];
                 const float braw = __uint_as_float((uint32_t)d.braw[b] << 16);
                 bsig[b] = valid ? (GDN ? braw : sigmoid_f(braw)) : 0.f;
             }
@@ -345,35 +325,37 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             } else {
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    // log2 a = max(lb log2 e, -rate log2(e) max(y, 0) - rate log2(1 + 2^(-|y| log2 e)))
+                    // with y' = (g + dt_bias) log2 e:
+                    // log2 a = max(lb log2 e, -rate max(y', 0) - rate log2(1 + 2^-|y'|))
                     const float lb2 = a.lower_bound * LOG2E * vmask[b];
-                    const float c1v = -rate * LOG2E * vmask[b], c2v = -rate * vmask[b];
-                    rmax[b] = -INFINITY;
+                    const float c1v = -rate * vmask[b];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const float x2[2] = {bf_lo(d.g[b][u]), bf_hi(d.g[b][u])};
 #pragma unroll
                         for (int hh = 0; hh < 2; ++hh) {
                             const int e = 2 * u + hh;
-                            const float y = x2[hh] + dt[e];
-                            const float t = exp2_hw(-fabsf(y) * LOG2E);
-                            const float la = fmaxf(lb2, fmaf(c1v, fmaxf(y, 0.f), c2v * log2_hw(1.f + t)));
-                            rmax[b] = fmaxf(rmax[b], la);
-                            G[b][e] = la;
+                            const float y = fmaf(x2[hh], LOG2E, dt[e]);
+                            const float t = exp2_hw(-fabsf(y));
+                            G[b][e] = fmaxf(lb2, c1v * (fmaxf(y, 0.f) + log2_hw(1.f + t)));
                         }
+                    }
+                }
+                // the bound of a warm-up chunk: max over this wave's channels of
+                // each token's log2 decay (before the prefix sums overwrite G)
+                if (x < out_from) {
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        rmax[b] = G[b][0];
+#pragma unroll
+                        for (int e = 1; e < 8; ++e) rmax[b] = fmaxf(rmax[b], G[b][e]);
+                        rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 16, 64));
+                        rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 32, 64));
                     }
                 }
                 row_scan16_n<16>(&G[0][0]);
             }
-            // the bound: max over this wave's channels of each token's log2 decay
-            if constexpr (!GDN) {
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 16, 64));
-                    rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 32, 64));
-                }
-            }
-            if (g == 0) {
+            if (x < out_from && g == 0) {
                 float* rm = reinterpret_cast<float*>(lds + L::RMAX) + (slot * NPW + p) * 32;
                 rm[m] = rmax[0];
                 rm[16 + m] = rmax[1];
@@ -443,10 +425,10 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                 float qn[8], kn[8];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    qn[2 * u] = bf_lo(d.q[b][u]) * iq[b];
-                    qn[2 * u + 1] = bf_hi(d.q[b][u]) * iq[b];
-                    kn[2 * u] = bf_lo(d.k[b][u]) * ik[b];
-                    kn[2 * u + 1] = bf_hi(d.k[b][u]) * ik[b];
+                    qn[2 * u] = bf_lo(d.q[b][u]);
+                    qn[2 * u + 1] = bf_hi(d.q[b][u]);
+                    kn[2 * u] = bf_lo(d.k[b][u]);
+                    kn[2 * u + 1] = bf_hi(d.k[b][u]);
                 }
                 float kg[8], qg[8], kgl[8], qgl[8], kil[8], kdl[8], kd[8];
                 float gl_tok = 1.f, gend_tok = 1.f;
@@ -485,15 +467,21 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     *reinterpret_cast<u32x4*>(rec + R::NKG + ((b * KS + p) * 64 + lane) * 16) = w;
                 }
                 *reinterpret_cast<bf16x8*>(rec + R::QG + ((b * KS + p) * 64 + lane) * 16) = pack8(qg);
-                // KdT[t][g'][m'][e'] = Kd[tok(g', e')][rho(t, m')], 16-byte units swizzled
+                // KdT[t][g'][m'][e'] = Kd[tok(g', e')][rho(t, m')], 16-byte units
+                // swizzled by st_unit.  Channel 32p + 8g + e is row 4g + (e & 3) of
+                // tile t = 2p + (e >> 2) and token m (block b) is element 4b + (m & 3)
+                // of unit 16 (4t + (m >> 2)) + row; st_unit XORs (m >> 2) & 3 into
+                // the row's low bits, so the element index is
+                //   1024 p + 128 (m >> 2) + 32 g + (m & 3) + 8 ((e & 3) ^ ((m >> 2) & 3))
+                //   + 512 (e >> 2) + 4 b:
+                // four lane addresses (one per e & 3) and constant offsets.
                 {
                     const u32x4 w = __builtin_bit_cast(u32x4, pack8(kd));
+                    const int lb = 1024 * p + 128 * (m >> 2) + 32 * g + (m & 3), sw = (m >> 2) & 3;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const int t = 2 * p + (e >> 2), mm = 4 * g + (e & 3);
-                        const int ee = 4 * b + (m & 3);
-                        const int tr = ((t * 4 + (m >> 2)) * 16 + mm) * EL + ee;
-                        kdt[st_unit(tr / 8) * 8 + tr % 8] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                        uint16_t* kp = kdt + lb + 8 * ((e & 3) ^ sw);
+                        kp[512 * (e >> 2) + 4 * b] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
                     }
                 }
                 const bf16x8 kglf = pack8(kgl), qglf = pack8(qgl);
@@ -526,6 +514,22 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             floatx4* part = reinterpret_cast<floatx4*>(lds + L::PART + slot * L::PART_SLOT) + p * 6 * 64;
 #pragma unroll
             for (int t = 0; t < 6; ++t) part[t * 64 + lane] = P[t];
+            // Squared norms of the raw q and k rows over this wave's channels:
+            // the diagonals of Q Q^T and K K^T from the bf16 inputs (exact
+            // products, fp32 sums).  q and k stay unnormalised everywhere above;
+            // phase B and the recurrence apply 1/||k|| and 1/||q|| per token.
+            float* nr = reinterpret_cast<float*>(lds + L::NRM) + (slot * NPW + p) * 64;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const bf16x8 kr = __builtin_bit_cast(bf16x8, d.k[b]);
+                const bf16x8 qr = __builtin_bit_cast(bf16x8, d.q[b]);
+                const floatx4 dk = mfma32(kr, kr, zero), dq = mfma32(qr, qr, zero);
+                // D[4 g + i][m]: the diagonal is in the lanes of g = m >> 2, element m & 3
+                if (g == (m >> 2)) {
+                    nr[16 * b + m] = pick(dk, m & 3);
+                    nr[32 + 16 * b + m] = pick(dq, m & 3);
+                }
+            }
         };
 
         // ------------------------------------------------------ compute waves
@@ -538,97 +542,140 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
             (void)lr; (void)lg;
             const int64_t ct0 = chunk_t0(x);
-            const uint16_t* vb = a.v + ct0 * vstride + (int64_t)h * V;
+            const char* vb = reinterpret_cast<const char*>(a.v + ct0 * vstride + (int64_t)h * V);
             const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
+            const uint32_t rstride = (uint32_t)a.H * V;
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tk = 16 * bb + 4 * lg + i;
-                    const int off = (tk < nvalid ? tk * a.H * V : 0) + col_of(0, lr);
+                    const uint32_t off =
+                        ((tk < nvalid ? (uint32_t)tk * rstride : 0u) + (uint32_t)col_of(0, lr)) * 2u;
                     if constexpr (CT == 2) d.w[bb][i] = *reinterpret_cast<const uint32_t*>(vb + off);
-                    else d.w[bb][i] = vb[off];
+                    else d.w[bb][i] = *reinterpret_cast<const uint16_t*>(vb + off);
                 }
         };
-        // phase B: finish chunk x's record (duty compute wave)
-        auto phase_b = [&](int x) __attribute__((always_inline)) {
-            const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
-            (void)lr; (void)lg;
-            const int slot = x & 1;
-            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
+        // phase B: finish chunk x's record, split over two compute waves that
+        // run at the same time: B0 the norms and block 0 (A00, Aqk00, T00),
+        // B1 block 1 (A11, Aqk11, T11), the coupling tiles A10 and Aqk10 and
+        // the decay bound.  The coupling block Tb10 = -T11 A10 Tb00 of Tb is
+        // left to the compute waves (from the fp32 tiles in CPL).
+        // The sum of the prep waves' partial products of tile t (fixed order):
+        auto tile = [&](int slot, int t, int lane) __attribute__((always_inline)) {
             const floatx4* part =
                 reinterpret_cast<const floatx4*>(lds + L::PART + slot * L::PART_SLOT);
-            // the sum of the prep waves' partial products of tile t (fixed order)
-            auto tile = [&](int t) __attribute__((always_inline)) {
-                floatx4 r = part[t * 64 + lane];
+            floatx4 r = part[t * 64 + lane];
 #pragma unroll
-                for (int pp = 1; pp < NPW; ++pp) {
-                    const floatx4 y = part[(pp * 6 + t) * 64 + lane];
+            for (int pp = 1; pp < NPW; ++pp) {
+                const floatx4 y = part[(pp * 6 + t) * 64 + lane];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) r[i] += y[i];
-                }
-                return r;
-            };
+                for (int i = 0; i < 4; ++i) r[i] += y[i];
+            }
+            return r;
+        };
+        // A[r][m] (into am, row-major, r = 4 g + i) and Aqk[m][r] of block b from
+        // the raw-key partials: A[r][m] = beta_r k^_r . k^_m, decay-weighted for GDN
+        auto build_block = [&](int slot, int b, const floatx4& pa, const floatx4& pq,
+                               const floatx4& ikr, float ikm, float* am, int m, int g)
+            __attribute__((always_inline)) {
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
             const float* gt = reinterpret_cast<const float*>(lds + L::GTOK) + slot * 32;
-            float* am = reinterpret_cast<float*>(lds + L::AMAT);
-            floatx4 aq[2];
+            floatx4 aq;
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const floatx4 pa = tile(b), pq = tile(2 + b);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * g + i;  // row of this element; its column is m
-                    const float br = bs[16 * b + r];
-                    float dec_rm = 1.f, dec_mr = 1.f;
-                    if constexpr (GDN) {
-                        const float gr = gt[16 * b + r], gm = gt[16 * b + m];
-                        dec_rm = r > m ? exp2_hw(gr - gm) : 0.f;
-                        dec_mr = m >= r ? exp2_hw(gm - gr) : 0.f;
-                    }
-                    am[b * 256 + 16 * r + m] = m < r ? br * pa[i] * dec_rm : 0.f;  // A[r][m]
-                    aq[b][i] = r <= m ? pq[i] * dec_mr : 0.f;                     // Aqk[m][r]
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g + i;  // row of this element; its column is m
+                const float br = bs[16 * b + r] * ikr[i] * ikm;
+                float dec_rm = 1.f, dec_mr = 1.f;
+                if constexpr (GDN) {
+                    const float gr = gt[16 * b + r], gm = gt[16 * b + m];
+                    dec_rm = r > m ? exp2_hw(gr - gm) : 0.f;
+                    dec_mr = m >= r ? exp2_hw(gm - gr) : 0.f;
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                am[16 * r + m] = m < r ? br * pa[i] * dec_rm : 0.f;  // A[r][m]
+                aq[i] = r <= m ? pq[i] * dec_mr : 0.f;                // Aqk[m][r]
             }
+            return aq;
+        };
+        auto phase_b0 = [&](int x) __attribute__((always_inline)) {
+            const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
+            const int slot = x & 1;
+            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
+            const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
+            float* am = reinterpret_cast<float*>(lds + L::AMAT);
+            // 1/||k|| (lanes 0..31) and 1/||q|| (lanes 32..63) of the chunk's
+            // tokens from the prep waves' partial squared norms; 0 for padding
+            float* invn = reinterpret_cast<float*>(lds + L::INVN) + (x % 3) * 64;
+            {
+                const float* nr = reinterpret_cast<const float*>(lds + L::NRM) + slot * NPW * 64;
+                float v = nr[lane];
+#pragma unroll
+                for (int pp = 1; pp < NPW; ++pp) v += nr[pp * 64 + lane];
+                const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
+                invn[lane] = (lane & 31) < nvalid ? rsq_hw(v + NORM_EPS) : 0.f;
+            }
+            const floatx4 pa = tile(slot, 0, lane), pq = tile(slot, 2, lane);
             wave_lds_sync();
-            const floatx4 TT0 = tri_inv_row(am, m, g);  // T00[m][4g + i]
-            __builtin_amdgcn_sched_barrier(0);
-            float* t00 = reinterpret_cast<float*>(lds + L::T00);
-            *reinterpret_cast<floatx4*>(t00 + 16 * m + 4 * g) = TT0;
-            const floatx4 TT1 = tri_inv_row(am + 256, m, g);  // T11[m][4g + i]
-            __builtin_amdgcn_sched_barrier(0);
+            const floatx4 ikr = *reinterpret_cast<const floatx4*>(invn + 4 * g);
+            const floatx4 aq = build_block(slot, 0, pa, pq, ikr, invn[m], am, m, g);
             wave_lds_sync();
-            floatx4 T00D, A10;  // D layout: T00[4g + i][m], A10[4g + i][m]
-            const floatx4 p4 = tile(4);
+            float t[16];
+            tri_inv_rows(am, m, t);  // every lane: row m of T00
+            const floatx4 TT0 = pick4(t, g);  // T00[m][4g + i]
+            floatx4 tb;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                T00D[i] = t00[16 * (4 * g + i) + m];
-                A10[i] = bs[16 + 4 * g + i] * p4[i];
-            }
-            // T10^T = -T00^T A10^T T11^T = -M(T00, M(A10, T11^T))
-            const floatx4 T10T = mt(T00D, mt(A10, TT1));
-            const floatx4 p5 = tile(5);
-            floatx4 tb_lo[2], tb_hi[2], aq_lo[2], aq_hi[2];
+            for (int i = 0; i < 4; ++i) tb[i] = TT0[i] * bs[4 * g + i];  // Tb00[m][4g + i]
+            const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<bf16xEL*>(rec + R::AQK + lane * (2 * EL)) = pack_tok(aq, zero);
+            *reinterpret_cast<bf16xEL*>(rec + R::TB + lane * (2 * EL)) = pack_tok(tb, zero);
+            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 768;
+            *reinterpret_cast<floatx4*>(cpl + 16 * m + 4 * g) = tb;  // Tb00 row-major
+        };
+        auto phase_b1 = [&](int x) __attribute__((always_inline)) {
+            const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
+            const int slot = x & 1;
+            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
+            const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
+            float* am = reinterpret_cast<float*>(lds + L::AMAT) + 256;
+            // 1/||k|| of block-1 rows 4 g + i and of columns m of both blocks
+            // (formed here too: phase B0 runs at the same time)
+            const float* nr = reinterpret_cast<const float*>(lds + L::NRM) + slot * NPW * 64;
+            const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
+            floatx4 ikr = *reinterpret_cast<const floatx4*>(nr + 16 + 4 * g);
+            float km1 = nr[16 + m], km0 = nr[m];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float b0 = bs[4 * g + i], b1 = bs[16 + 4 * g + i];
-                tb_lo[0][i] = TT0[i] * b0;    // Tb00
-                tb_hi[0][i] = 0.f;
-                tb_lo[1][i] = -b0 * T10T[i];  // Tb10
-                tb_hi[1][i] = TT1[i] * b1;    // Tb11
-                aq_lo[0][i] = aq[0][i];
-                aq_hi[0][i] = 0.f;
-                aq_lo[1][i] = p5[i];          // Aqk10 (all keys before the query)
-                aq_hi[1][i] = aq[1][i];
+            for (int pp = 1; pp < NPW; ++pp) {
+                const floatx4 y = *reinterpret_cast<const floatx4*>(nr + pp * 64 + 16 + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ikr[i] += y[i];
+                km1 += nr[pp * 64 + 16 + m];
+                km0 += nr[pp * 64 + m];
             }
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                *reinterpret_cast<bf16xEL*>(rec + R::AQK + (b * 64 + lane) * (2 * EL)) =
-                    pack_tok(aq_lo[b], aq_hi[b]);
-                *reinterpret_cast<bf16xEL*>(rec + R::TB + (b * 64 + lane) * (2 * EL)) =
-                    pack_tok(tb_lo[b], tb_hi[b]);
-            }
+            for (int i = 0; i < 4; ++i)
+                ikr[i] = 16 + 4 * g + i < nvalid ? rsq_hw(ikr[i] + NORM_EPS) : 0.f;
+            const float ikm1 = 16 + m < nvalid ? rsq_hw(km1 + NORM_EPS) : 0.f;
+            const float ikm0 = m < nvalid ? rsq_hw(km0 + NORM_EPS) : 0.f;
+            const floatx4 pa = tile(slot, 1, lane), pq = tile(slot, 3, lane);
+            const floatx4 aq = build_block(slot, 1, pa, pq, ikr, ikm1, am, m, g);
+            const floatx4 p4 = tile(slot, 4, lane), p5 = tile(slot, 5, lane);
+            floatx4 a10;  // A10[4g + i][m] = beta_{16+4g+i} k^_{16+4g+i} . k^_m
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a10[i] = bs[16 + 4 * g + i] * ikr[i] * ikm0 * p4[i];
+            wave_lds_sync();
+            float t[16];
+            tri_inv_rows(am, m, t);  // every lane: row m of T11
+            const floatx4 TT1 = pick4(t, g);  // T11[m][4g + i]
+            bf16x4 tb11;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tb11[i] = (bf16)(TT1[i] * bs[16 + 4 * g + i]);
+            // Aqk block 1 = [Aqk10 | Aqk11] (Aqk10: all keys before the query);
+            // Tb block 1 = [Tb10 | Tb11]: the Tb11 half here
+            *reinterpret_cast<bf16xEL*>(rec + R::AQK + (64 + lane) * (2 * EL)) = pack_tok(p5, aq);
+            *reinterpret_cast<bf16x4*>(rec + R::TB + (64 + lane) * (2 * EL) + EL) = tb11;
+            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 768;
+            *reinterpret_cast<floatx4*>(cpl + 256 + 4 * lane) = TT1;
+            *reinterpret_cast<floatx4*>(cpl + 512 + 4 * lane) = a10;
             // the chunk's bound (sum over its tokens of max_c log2 a), warm-up chunks
             if (x < out_from) {
                 const float* rm = reinterpret_cast<const float*>(lds + L::RMAX) + slot * NPW * 32;
@@ -651,6 +698,11 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             const int64_t ct0 = chunk_t0(x);
             const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
             const bool outs = x >= out_from;
+            // 1/||k|| of the lane's tokens 16 bb + 4 lg + i (the record holds the
+            // raw keys and queries; phase B wrote these for the chunk)
+            const float* invn = reinterpret_cast<const float*>(lds + L::INVN) + (x % 3) * 64;
+            const floatx4 ikt[2] = {*reinterpret_cast<const floatx4*>(invn + 4 * lg),
+                                    *reinterpret_cast<const floatx4*>(invn + 16 + 4 * lg)};
             bf16x8 sb[CT][KS];
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
@@ -661,16 +713,14 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                         sb[ct][j][e] = (bf16)S[ct][2 * j][e];
                         sb[ct][j][4 + e] = (bf16)S[ct][2 * j + 1][e];
                     }
+            // Y_b = V_b - KG_b S: the product with the raw keys, then per token
+            // V + (1/||k||) (-K G S)
+            const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
             floatx4 Y[CT][2];
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t w = vin.w[bb][i];
-                    Y[0][bb][i] = bf_lo(w);
-                    if constexpr (CT == 2) Y[1][bb][i] = bf_hi(w);
-                }
-            // Y_b = V_b - KG_b S
+                for (int bb = 0; bb < 2; ++bb) Y[ct][bb] = zero;
 #pragma unroll
             for (int j = 0; j < KS; ++j)
 #pragma unroll
@@ -680,10 +730,18 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) Y[ct][bb] = mfma32(nkg, sb[ct][j], Y[ct][bb]);
                 }
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t w = vin.w[bb][i];
+                    Y[0][bb][i] = fmaf(ikt[bb][i], Y[0][bb][i], bf_lo(w));
+                    if constexpr (CT == 2) Y[1][bb][i] = fmaf(ikt[bb][i], Y[1][bb][i], bf_hi(w));
+                }
             __builtin_amdgcn_sched_barrier(0);
-            // O^T = S^T QG^T (+ U'^T Aqk^T below)
+            // O^T = S^T QG^T (+ U'^T Aqk^T below), raw queries: scaled by
+            // 1/||q|| at the store
             floatx4 OT[CT][2];
-            const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
             if (outs) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
@@ -720,20 +778,37 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     yc[ct][i] = (bf16)Y[ct][0][i];
                     yc[ct][4 + i] = (bf16)Y[ct][1][i];
                 }
+            // Tb's block 1 = [Tb10 | Tb11]: Tb10 = -T11 A10 Tb00 from phase B's
+            // fp32 tiles (the same in every compute wave), Tb11 from the record
+            bf16xEL tb1 = *reinterpret_cast<const bf16xEL*>(buf + R::TB + (64 + lane) * (2 * EL));
+            {
+                const float* cpl = reinterpret_cast<const float*>(lds + L::CPL) + (x & 1) * 768;
+                floatx4 tb00d;  // Tb00[4g + i][m]
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tb00d[i] = cpl[16 * (4 * lg + i) + lr];
+                const floatx4 tt1 = *reinterpret_cast<const floatx4*>(cpl + 256 + 4 * lane);
+                const floatx4 a10 = *reinterpret_cast<const floatx4*>(cpl + 512 + 4 * lane);
+                // M(Tb00, M(A10, T11^T)) = (T11 A10 Tb00)^T: element i is [m][4g + i]
+                const floatx4 c = mt(tb00d, mt(a10, tt1));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tb1[i] = (bf16)(-c[i]);
+            }
             floatx4 U[CT][2];
+            {
+                const bf16xEL tb0 = *reinterpret_cast<const bf16xEL*>(buf + R::TB + lane * (2 * EL));
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const bf16xEL tb =
-                    *reinterpret_cast<const bf16xEL*>(buf + R::TB + (bb * 64 + lane) * (2 * EL));
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) U[ct][bb] = mfma_tok(tb, yc[ct], zero);
+                for (int ct = 0; ct < CT; ++ct) {
+                    U[ct][0] = mfma_tok(tb0, yc[ct], zero);
+                    U[ct][1] = mfma_tok(tb1, yc[ct], zero);
+                }
             }
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    uc[ct][i] = (bf16)U[ct][0][i];
-                    uc[ct][4 + i] = (bf16)U[ct][1][i];
+                    // (1/||k_t||) U'_t: the record's Kd and Aqk hold the raw keys
+                    uc[ct][i] = (bf16)(U[ct][0][i] * ikt[0][i]);
+                    uc[ct][4 + i] = (bf16)(U[ct][1][i] * ikt[1][i]);
                 }
             __builtin_amdgcn_sched_barrier(0);
             // S = Diag(Gam_C) S + KdT U'
@@ -759,28 +834,31 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             for (int ob = 0; ob < 2; ++ob) {
                 if (16 * ob + lr >= nvalid) continue;
                 uint16_t* op = obase + (16 * ob + lr) * a.H * V;
+                const float so = a.scale * invn[32 + 16 * ob + lr];  // scale / ||q||
                 if constexpr (CT == 2) {
                     // tile ct row 4 lg + i is column wcol + 2 (4 lg + i) + ct: the
                     // lane's 8 values are columns wcol + 8 lg .. + 7
                     bf16x8 ov;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        ov[2 * i] = (bf16)(a.scale * OT[0][ob][i]);
-                        ov[2 * i + 1] = (bf16)(a.scale * OT[1][ob][i]);
+                        ov[2 * i] = (bf16)(so * OT[0][ob][i]);
+                        ov[2 * i + 1] = (bf16)(so * OT[1][ob][i]);
                     }
                     *reinterpret_cast<bf16x8*>(op + wcol + 8 * lg) = ov;
                 } else {
                     bf16x4 ov;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) ov[i] = (bf16)(a.scale * OT[0][ob][i]);
+                    for (int i = 0; i < 4; ++i) ov[i] = (bf16)(so * OT[0][ob][i]);
                     *reinterpret_cast<bf16x4*>(op + wcol + 4 * lg) = ov;
                 }
             }
         };
 
     // ------------------------------------------------------- the iterations
-    // Iteration it (from -4): compute chunk it, phase B chunk it+1, phase A
-    // chunk it+2, phase N chunk it+3, loads chunk it+4.  Each role runs its own
+    // Iteration it (from -2): compute chunk it, phase B chunk it+1 and the
+    // loads of v for chunk it+2; the loads of q, k, g and beta for chunk it+4
+    // (chunks 0 and 1 before the loop) and phase A of chunk it+2.  Each role
+    // runs its own
     // copy of the loop (the same iterations and barriers), unrolled by three so
     // that every register ring slot is a constant.
     if (is_cw) {
@@ -789,23 +867,27 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             load_state(exact);
             if (tid == 0) misc[0] = 0.f;  // sum of the warm-up chunks' bounds
             if (n_it <= 0) break;
-            const int n_iter = (n_it + 4 + 2) / 3 * 3;
+            const int n_iter = (n_it + 2 + 2) / 3 * 3;
             VIn vin[3];
             bool restart = false;
             for (int k3 = 0; k3 < n_iter && !restart; k3 += 3) {
                 static_for<0, 3>([&](auto u) __attribute__((always_inline)) {
                     if (restart) return;
-                    const int it = k3 + u - 4;
+                    const int it = k3 + u - 2;
                     if (failed_bound(it)) {
                         restart = true;
                         return;
                     }
-                    constexpr int sv = (u + 1) % 3, sc = (u + 2) % 3;
+                    // ring slot of chunk y: y mod 3
+                    constexpr int sv = u, sc = (u + 1) % 3;
                     // unconditional (a valid chunk re-read at the ends): a load
                     // issued on some paths only makes the compiler's in-order
                     // wait counts cover the loads just issued as well
-                    load_v(vin[sv], min(max(it + 2, 0), n_it - 1));
-                    if (it + 1 >= 0 && it + 1 < n_it && wave == (it + 1) % NCW) phase_b(it + 1);
+                    load_v(vin[sv], min(it + 2, n_it - 1));
+                    if (it + 1 >= 0 && it + 1 < n_it) {
+                        if (wave == (it + 1) % NCW) phase_b0(it + 1);
+                        else if (wave == (it + 3) % NCW) phase_b1(it + 1);
+                    }
                     if (it >= 0 && it < n_it) compute(it, vin[sc]);
                     __syncthreads();
                 });
@@ -828,24 +910,26 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         for (int attempt = 0; attempt < 2; ++attempt) {
             begin_attempt(attempt);
             if (n_it <= 0) break;
-            const int n_iter = (n_it + 4 + 2) / 3 * 3;
+            const int n_iter = (n_it + 2 + 2) / 3 * 3;
             // nothing in flight on entry (a restarted attempt leaves loads of
             // the abandoned one): the loop's wait counts hold on every path
             __builtin_amdgcn_s_waitcnt(VMCNT_0);
             PIn pin[3];
+            load_in(pin[0], 0);
+            load_in(pin[1], min(1, n_it - 1));
             bool restart = false;
             for (int k3 = 0; k3 < n_iter && !restart; k3 += 3) {
                 static_for<0, 3>([&](auto u) __attribute__((always_inline)) {
                     if (restart) return;
-                    const int it = k3 + u - 4;
+                    const int it = k3 + u - 2;
                     if (failed_bound(it)) {
                         restart = true;
                         return;
                     }
-                    constexpr int sl = u, sn = (u + 2) % 3, sa = (u + 1) % 3;
+                    constexpr int sa = u, sl = (u + 2) % 3;  // ring slot of chunk y: y mod 3
+                    // two chunks ahead: the loads have two iterations to land
                     load_in(pin[sl], min(it + 4, n_it - 1));  // unconditional (see load_v)
-                    if (it + 3 >= 0 && it + 3 < n_it) phase_n(pin[sn], it + 3);
-                    if (it + 2 >= 0 && it + 2 < n_it) phase_a(pin[sa], it + 2);
+                    if (it + 2 < n_it) phase_a(pin[sa], it + 2);
                     else touch(pin[sa]);
                     __syncthreads();
                 });

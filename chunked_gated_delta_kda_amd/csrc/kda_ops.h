@@ -12,11 +12,13 @@ namespace ops {
 constexpr int ROW_SHR1 = 0x111, ROW_SHR2 = 0x112, ROW_SHR4 = 0x114, ROW_SHR8 = 0x118;
 
 
+// Inclusive prefix sum over the 16 lanes of each row.  A source lane before
+// the row start reads 0 (bound_ctrl), so every step is one v_add_f32_dpp.
 __device__ __forceinline__ float row_scan16(float x) {
-    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR1, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR2, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR4, 0xf, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR8, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR1, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR2, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR4, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0.f, x, ROW_SHR8, 0xf, 0xf, true);
     return x;
 }
 
@@ -25,13 +27,13 @@ __device__ __forceinline__ float row_scan16(float x) {
 template <int N>
 __device__ __forceinline__ void row_scan16_n(float* x) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR1, 0xf, 0xf, false);
+    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR1, 0xf, 0xf, true);
 #pragma unroll
-    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR2, 0xf, 0xf, false);
+    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR2, 0xf, 0xf, true);
 #pragma unroll
-    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR4, 0xf, 0xf, false);
+    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR4, 0xf, 0xf, true);
 #pragma unroll
-    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR8, 0xf, 0xf, false);
+    for (int i = 0; i < N; ++i) x[i] += __builtin_amdgcn_update_dpp(0.f, x[i], ROW_SHR8, 0xf, 0xf, true);
 }
 
 __device__ __forceinline__ float lane_val(float x, int src) { return __shfl(x, src, 64); }
@@ -87,6 +89,54 @@ __device__ __forceinline__ floatx4 tri_inv_row(const float* a, int m, int g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         r[i] = g == 0 ? t[i] : g == 1 ? t[4 + i] : g == 2 ? t[8 + i] : t[12 + i];
+    return r;
+}
+
+// Row m of T = (I + A)^-1 (as tri_inv_row) into t[0..15], for a matrix whose
+// LDS address may differ between lanes (two matrices inverted at once by two
+// lane groups).  Each step reads the next row one step ahead of its use.
+__device__ __forceinline__ void tri_inv_rows(const float* a, int m, float (&t)[16]) {
+    float s[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        t[j] = j == m ? 1.f : 0.f;
+        s[j] = 0.f;
+    }
+    auto read_row = [&](auto kc, float (&row)[16]) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        static_for<0, (k + 3) / 4>([&](auto q) __attribute__((always_inline)) {
+            const floatx4 v = *reinterpret_cast<const floatx4*>(a + 16 * k + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) row[4 * q + e] = v[e];
+        });
+    };
+    float ra[16];
+    read_row(std::integral_constant<int, 15>{}, ra);
+    static_for<0, 15>([&](auto kk) __attribute__((always_inline)) {
+        constexpr int k = 15 - kk;
+        float na[16];
+        if constexpr (k > 1) read_row(std::integral_constant<int, k - 1>{}, na);
+        if constexpr (k < 15) t[k] = k < m ? -s[k] : t[k];
+#pragma unroll
+        for (int j = 0; j < k; ++j) s[j] = fmaf(t[k], ra[j], s[j]);
+        if constexpr (k > 1) {
+#pragma unroll
+            for (int j = 0; j < k - 1; ++j) ra[j] = na[j];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    t[0] = 0 < m ? -s[0] : t[0];
+}
+
+// t[4 g + i], i = 0..3, for a runtime g in 0..3
+__device__ __forceinline__ floatx4 pick4(const float (&t)[16], int g) {
+    floatx4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = g & 1 ? t[4 + i] : t[i];
+        const float hi = g & 1 ? t[12 + i] : t[8 + i];
+        r[i] = g & 2 ? hi : lo;
+    }
     return r;
 }
 
