@@ -738,7 +738,6 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     Y[0][bb][i] = fmaf(ikt[bb][i], Y[0][bb][i], bf_lo(w));
                     if constexpr (CT == 2) Y[1][bb][i] = fmaf(ikt[bb][i], Y[1][bb][i], bf_hi(w));
                 }
-            __builtin_amdgcn_sched_barrier(0);
             // O^T = S^T QG^T (+ U'^T Aqk^T below), raw queries: scaled by
             // 1/||q|| at the store
             floatx4 OT[CT][2];
@@ -757,7 +756,6 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                         for (int ct = 0; ct < CT; ++ct) OT[ct][ob] = mfma32(sb[ct][j], qg, OT[ct][ob]);
                     }
             }
-            __builtin_amdgcn_sched_barrier(0);
             // decay the state
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
@@ -768,7 +766,6 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
 #pragma unroll
                     for (int i = 0; i < 4; ++i) S[ct][t][i] *= gc[i];
             }
-            __builtin_amdgcn_sched_barrier(0);
             // U' = Tb Y over the chunk's tokens
             bf16xEL yc[CT], uc[CT];
 #pragma unroll
@@ -810,7 +807,6 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     uc[ct][i] = (bf16)(U[ct][0][i] * ikt[0][i]);
                     uc[ct][4 + i] = (bf16)(U[ct][1][i] * ikt[1][i]);
                 }
-            __builtin_amdgcn_sched_barrier(0);
             // S = Diag(Gam_C) S + KdT U'
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
@@ -819,7 +815,6 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) S[ct][t] = mfma_tok(kdt, uc[ct], S[ct][t]);
             }
-            __builtin_amdgcn_sched_barrier(0);
             if (!outs) return;
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob) {
