@@ -369,7 +369,7 @@ FusedPlan plan_fused(int32_t B, int32_t T, int32_t H, int32_t N, bool varlen, in
 size_t fused_workspace_bytes(const FusedPlan& p, int32_t N, bool varlen) {
     if (!varlen) return ALIGN;
     const size_t nv = (size_t)p.n_virt;
-    return meta_bytes(N) + align_up(sizeof(int32_t) * (2 * (nv + 1) + nv + ((size_t)N + 1)));
+    return meta_bytes(N) + align_up(sizeof(int32_t) * (2 * (nv + 1) + nv + ((size_t)N + 1) + nv));
 }
 
 // Argument checks of the single-launch pass (its workspace instead of the
@@ -435,13 +435,15 @@ int run_fused(const Common& c, int32_t N, kda::FusedArgs f, bool gdn, hipStream_
         int32_t* vchunk_off = vseq_start + (nv + 1);
         int32_t* final_map = vchunk_off + (nv + 1);
         int32_t* vfirst = final_map + nv;
+        int32_t* order = vfirst + (N + 1);
         kda::launch_seq_table(c.cu, N, c.T, (int64_t)c.B * c.T, seq_start, chunk_off, stream);
         kda::launch_seg_table(seq_start, chunk_off, N, fp.L, nv, vseq_start, vchunk_off,
-                              final_map, vfirst, stream);
+                              final_map, vfirst, stream, order);
         f.seq_start = seq_start;
         f.vseq_start = vseq_start;
         f.vfirst = vfirst;
         f.final_map = final_map;
+        f.order = order;
         f.n_segs = nv;
         groups = (int64_t)nv * c.H;
     }

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
 
     // ---------------------------------------------------------------- segment
     const int h = blockIdx.x % a.H;
-    const int vseg = blockIdx.x / a.H;
+    int vseg = blockIdx.x / a.H;
     int n, fslot;
     int64_t tseq0, tseq1;  // the sequence's tokens
     int c0, c1;            // the segment's chunks (within the sequence)
@@ -170,6 +170,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
     } else {
         const int nseg = min(a.vfirst[a.n_seqs], a.n_segs);
         if (vseg >= nseg) return;
+        // dispatch rank -> segment (longest first), kept inside the table
+        if (a.order) vseg = min(max(a.order[vseg], 0), nseg - 1);
         int lo = 0, hi = a.n_seqs;  // vfirst[lo] <= vseg < vfirst[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;

@@ -134,6 +134,7 @@ struct FusedArgs {
     const int32_t* vseq_start;  // packed: [n_segs + 1] first token of each segment
     const int32_t* vfirst;      // packed: [n_seqs + 1] first segment of each sequence
     const int32_t* final_map;   // packed: [n_segs] sequence whose final state a segment ends
+    const int32_t* order;       // packed: [n_segs] segment of each dispatch rank (or null)
     int32_t warm_chunks;        // warm-up chunks before a segment that starts mid-sequence
     float bound_limit;          // log2: a warm-up whose transitions are below this suffices
     int64_t tok_limit;          // tokens in the batch
@@ -177,9 +178,11 @@ void launch_bwd_chunk(const BwdArgs& a, int K, int V, bool gdn, int n_slots, hip
 void launch_bwd_reduce(const float* part_dt, const float* part_alog, int32_t n_slots,
                        int32_t H, int32_t K, float* ddt_bias, float* dA_log, hipStream_t stream);
 
+// order (optional, [n_virt_max]): the segments longest first, for dispatch
 void launch_seg_table(const int32_t* seq_start, const int32_t* chunk_off, int32_t n_seqs,
                       int32_t L, int32_t n_virt_max, int32_t* vseq_start, int32_t* vchunk_off,
-                      int32_t* final_map, int32_t* vfirst, hipStream_t stream);
+                      int32_t* final_map, int32_t* vfirst, hipStream_t stream,
+                      int32_t* order = nullptr);
 void launch_split_scan(const SplitScanArgs& a, int K, hipStream_t stream);
 void launch_seq_table(const int32_t* cu, int32_t n_seqs, int32_t T, int64_t total_tokens,
                       int32_t* seq_start, int32_t* chunk_off, hipStream_t stream);

@@ -25,6 +25,9 @@ namespace kda {
 
 namespace {
 
+constexpr int SEG_ORDER_BUCKETS = 1024;  // segment lengths (chunk steps) told apart
+constexpr int SEG_WARM_CHUNKS = 2;       // the fused pass's warm-up (kda_api.hip)
+
 __device__ __forceinline__ int32_t block_scan_add(int32_t v, int32_t* buf) {
     const int tid = threadIdx.x;
     buf[tid] = v;
@@ -55,8 +58,10 @@ __global__ __launch_bounds__(256) void kda_seg_table_kernel(const int32_t* seq_s
                                                             int32_t n_virt_max,
                                                             int32_t* vseq_start,
                                                             int32_t* vchunk_off,
-                                                            int32_t* final_map, int32_t* vfirst) {
+                                                            int32_t* final_map, int32_t* vfirst,
+                                                            int32_t* order) {
     __shared__ int32_t buf[256];
+    __shared__ int32_t hist[SEG_ORDER_BUCKETS];
     const int tid = threadIdx.x;
     int32_t carry = 0;
     for (int base = 0; base < n_seqs; base += 256) {
@@ -93,13 +98,48 @@ __global__ __launch_bounds__(256) void kda_seg_table_kernel(const int32_t* seq_s
         if (v < n_virt_max) final_map[v] = -1;
     }
     if (tid == 0) vfirst[n_seqs] = min(carry, n_virt_max);
+    if (!order) return;
+
+    // Dispatch order of the segments, longest first (list scheduling of
+    // unequal jobs onto the compute units).  A segment's length in chunk
+    // steps is its chunks plus the warm-up chunks of a segment that does not
+    // start its sequence (the one after a sequence's last segment starts
+    // one).  Counting sort on that length (clamped to the bucket count);
+    // within a length the order is whatever the atomics give -- a segment's
+    // results do not depend on when it runs.
+    const int32_t nseg = min(carry, n_virt_max);
+    __syncthreads();  // the table above is complete
+    for (int i = tid; i < SEG_ORDER_BUCKETS; i += 256) hist[i] = 0;
+    __syncthreads();
+    auto bucket = [&](int v) {
+        int32_t len = max(vchunk_off[v + 1] - vchunk_off[v], 0);
+        if (v > 0 && final_map[v - 1] < 0) len += SEG_WARM_CHUNKS;
+        return SEG_ORDER_BUCKETS - 1 - min(len, SEG_ORDER_BUCKETS - 1);
+    };
+    for (int v = tid; v < nseg; v += 256) atomicAdd(&hist[bucket(v)], 1);
+    __syncthreads();
+    constexpr int PER = SEG_ORDER_BUCKETS / 256;
+    int32_t cnt[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        cnt[j] = hist[PER * tid + j];
+        sum += cnt[j];
+    }
+    int32_t run = block_scan_add(sum, buf) - sum;  // exclusive prefix of this thread's buckets
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        hist[PER * tid + j] = run;
+        run += cnt[j];
+    }
+    __syncthreads();
+    for (int v = tid; v < nseg; v += 256) order[atomicAdd(&hist[bucket(v)], 1)] = v;
 }
 
 void launch_seg_table(const int32_t* seq_start, const int32_t* chunk_off, int32_t n_seqs,
                       int32_t L, int32_t n_virt_max, int32_t* vseq_start, int32_t* vchunk_off,
-                      int32_t* final_map, int32_t* vfirst, hipStream_t stream) {
+                      int32_t* final_map, int32_t* vfirst, hipStream_t stream, int32_t* order) {
     hipLaunchKernelGGL(kda_seg_table_kernel, dim3(1), dim3(256), 0, stream, seq_start, chunk_off,
-                       n_seqs, L, n_virt_max, vseq_start, vchunk_off, final_map, vfirst);
+                       n_seqs, L, n_virt_max, vseq_start, vchunk_off, final_map, vfirst, order);
 }
 
 // The scan over the segments of one (sequence, head, 32 value columns):

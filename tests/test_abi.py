@@ -53,13 +53,14 @@ def test_workspace_size_formula(lib):
     # L = max(8, ceil(slots H / 512)) chunks, at most N + ceil(slots / L) of them)
     L = max(8, -(-slots * H // 512))
     nv = N + -(-slots // L)
-    fused = meta + al(4 * (2 * (nv + 1) + nv + N + 1))
+    # sequence tables, segment tables and the longest-first dispatch order
+    fused = meta + al(4 * (2 * (nv + 1) + nv + N + 1 + nv))
     assert kda.workspace_size(B, T, H, 128, 128) == fused
     assert fused < 4096 < want
     L = 16
     nv = N + -(-slots // L)
     assert kda.workspace_size(B, T, H, 128, 128, segment_chunks=L) == \
-        meta + al(4 * (2 * (nv + 1) + nv + N + 1))
+        meta + al(4 * (2 * (nv + 1) + nv + N + 1 + nv))
     for path in ("fused", "staged"):
         assert kda.workspace_size(1, 100, 1, 96, 128, path=path) == 0  # unsupported K
         assert kda.workspace_size(0, 100, 1, 128, 128, path=path) == 0
