@@ -19,7 +19,7 @@ _STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED"
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_fwd", "gdn_fwd", "kda_fwd_workspace_size", "gdn_fwd_workspace_size",
            "kda_fwd_segmented_workspace_size", "kda_fwd_segmented", "gdn_fwd_segmented",
-           "kda_fwd_timed", "gdn_fwd_timed",
+           "kda_fwd_timed", "gdn_fwd_timed", "kda_fwd_noalloc",
            "kda_fwd_split_workspace_size", "kda_fwd_split", "gdn_fwd_split", "kda_prep",
            "gdn_prep", "kda_recur", "kda_prep_timed", "kda_recur_timed", "kda_decode", "gdn_decode", "kda_bwd_workspace_size",
            "kda_bwd", "gdn_bwd", "kda_fwd_save", "gdn_fwd_save", "kda_bwd_saved",
@@ -69,6 +69,8 @@ def load(path: Path | str | None = None):
     lib.kda_fwd_segmented.argtypes = lib.kda_fwd_split.argtypes
     lib.gdn_fwd_segmented.restype = ctypes.c_int
     lib.gdn_fwd_segmented.argtypes = lib.gdn_fwd_split.argtypes
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_fwd_noalloc.argtypes = lib.kda_fwd.argtypes[:19] + [vp]
     lib.kda_fwd_timed.restype = ctypes.c_int
     lib.kda_fwd_timed.argtypes = lib.kda_fwd.argtypes + [vp, vp]
     lib.gdn_fwd_timed.restype = ctypes.c_int
@@ -267,6 +269,36 @@ def kda_fwd(q, k, v, g, beta, A_log, dt_bias, lower_bound=-5.0, scale=None, init
     if st != 0:
         raise LibKdaError(st, status_str(st))
     return a["o"], a["final"]
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20  # KDA_NOALLOC_SCRATCH_BYTES of include/kda.h
+
+
+def kda_fwd_noalloc(q, k, v, g, beta, A_log, dt_bias, out, final_out=None, lower_bound=-5.0,
+                    scale=None, initial_state=None, cu_seqlens=None):
+    """kda_fwd through kda_fwd_noalloc: allocates nothing (no workspace, no
+    outputs: ``out`` [B,T,H,V] bf16 and ``final_out`` [N,H,K,V] fp32 or None
+    are written in place).  Packed batches keep their tables in the library's
+    per-GPU scratch array; calls overlapping in time on one GPU race on it."""
+    torch = _torch()
+    B, T, H, K, V, N, scale = _shapes(q, k, v, beta, scale, initial_state, cu_seqlens)
+    dev = q.device
+    _need(out, "out", torch.bfloat16, (B, T, H, V), dev)
+    if final_out is not None:
+        _need(final_out, "final_out", torch.float32, (N, H, K, V), dev)
+    _kda_gate_checks(g, A_log, dt_bias, B, T, H, K, dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = load().kda_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                                _ptr(dt_bias), float(lower_bound), float(scale),
+                                _ptr(initial_state), _ptr(final_out), _ptr(cu_seqlens), N, B, T,
+                                H, K, V, _ptr(out), stream)
+    if st == 3 and cu_seqlens is not None:
+        raise LibKdaError(st, f"the packed batch's tables need more than the "
+                              f"{NOALLOC_SCRATCH_BYTES} bytes of the library's scratch array; "
+                              f"use kda_fwd with a workspace")
+    if st != 0:
+        raise LibKdaError(st, status_str(st))
+    return out, final_out
 
 
 def gdn_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,

@@ -4,10 +4,18 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_common.h"
 #include "kda_launch.h"
+
+// Scratch of kda_fwd_noalloc: the packed-sequence and segment tables of the
+// single-launch pass, in a device array of the library instead of a caller
+// workspace.  Every GPU the library runs on holds its own copy until the
+// process ends; every call on that GPU shares it (the tables are rewritten
+// in full by each call before they are read).
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -663,6 +671,29 @@ int run_decode(kda::DecodeArgs& d, int32_t N, int32_t H, int32_t K, int32_t V, b
 
 }  // namespace
 
+namespace {
+
+// Device address of `scratch` on each device, resolved once per device (the
+// array's name in host code is only a stand-in for the symbol).
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return KDA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t kda_fwd_split_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
@@ -771,6 +802,36 @@ int kda_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint1
     return kda_fwd_fused(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
                          final_state, cu_seqlens, num_seqs, B, T, H, K, V, o, workspace,
                          workspace_bytes, 0, stream, nullptr, nullptr);
+}
+
+int kda_fwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                    const uint16_t* beta, const float* A_log, const float* dt_bias,
+                    float lower_bound, float scale, const float* initial_state,
+                    float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                    int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* stream) {
+    // Every check of kda_fwd first, on the host, with the scratch standing
+    // in as the workspace (a packed batch whose tables need more than the
+    // array gets KDA_ERR_WORKSPACE); only then the array's device address.
+    {
+        Common c{q, k, v, beta, initial_state, final_state, cu_seqlens, cu_seqlens != nullptr,
+                 num_seqs, B, T, H, K, V, o, reinterpret_cast<void*>(ALIGN),
+                 KDA_NOALLOC_SCRATCH_BYTES, scale, 0};
+        int st = check_kda_gate(T, g, A_log, dt_bias, lower_bound);
+        if (st != KDA_OK) return st;
+        int32_t N = 0;
+        st = check_fused(c, N);
+        if (st != KDA_OK) return st;
+    }
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (cu_seqlens != nullptr) {
+        const int st = scratch_on_current_device(&ws);
+        if (st != KDA_OK) return st;
+        ws_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    }
+    return kda_fwd_fused(q, k, v, g, beta, A_log, dt_bias, lower_bound, scale, initial_state,
+                         final_state, cu_seqlens, num_seqs, B, T, H, K, V, o, ws, ws_bytes, 0,
+                         stream, nullptr, nullptr);
 }
 
 int kda_fwd_segmented(const uint16_t* q, const uint16_t* k, const uint16_t* v,

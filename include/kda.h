@@ -161,6 +161,27 @@ int kda_fwd_timed(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
                   int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* workspace,
                   size_t workspace_bytes, void* stream, void* start_event, void* stop_event);
 
+/* kda_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same pass and results as kda_fwd, with no workspace argument.  A packed
+ * batch keeps its sequence and segment tables (what kda_fwd puts in the
+ * workspace) in a device array of the library, KDA_NOALLOC_SCRATCH_BYTES per
+ * GPU, held until the process ends; a fixed-length batch needs none.  The
+ * call allocates nothing; the caller passes every input and output.
+ * Errors: those of kda_fwd, and KDA_ERR_WORKSPACE (before any HIP call) for
+ * a packed batch whose tables need more than the array (at most
+ * num_seqs + ceil(tokens / 32 + num_seqs) / L segments, L >= 8, about 16
+ * bytes per segment and 12 per sequence: far beyond a million tokens).
+ * The array is shared by every call on a GPU: calls that overlap in time on
+ * one GPU (other streams, other host threads) race on it and must be
+ * serialised by the caller; calls in stream order are safe. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int kda_fwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                    const uint16_t* beta, const float* A_log, const float* dt_bias,
+                    float lower_bound, float scale, const float* initial_state,
+                    float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+                    int32_t T, int32_t H, int32_t K, int32_t V, uint16_t* o, void* stream);
+
 int gdn_fwd_timed(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
                   const uint16_t* beta, float scale, const float* initial_state,
                   float* final_state, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,

@@ -305,3 +305,18 @@ def test_prep_grid_limit_checked_on_host(lib):
     st = lib.kda_prep(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, None, 0, 1, 1 << 24, 8192, 64,
                       64, FAKE, 1 << 62, None)
     assert st == 1
+
+
+def test_noalloc_rejects_on_host(lib):
+    """kda_fwd_noalloc: the checks of kda_fwd, and a packed batch whose tables
+    exceed the library's scratch array rejected before any HIP call."""
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -5.0, 0.088, None, None, FAKE, 1 << 20, 1,
+            1 << 24, 4, 128, 128, FAKE, None]
+    assert lib.kda_fwd_noalloc(*args) == 3  # 2^20 sequences: tables far beyond 4 MiB
+    args[12], args[14] = 2, 64  # a small packed batch: the checks of kda_fwd
+    args[3] = None
+    assert lib.kda_fwd_noalloc(*args) == 1  # null g
+    args[3] = FAKE
+    args[16] = 96
+    assert lib.kda_fwd_noalloc(*args) == 2  # unsupported K
+
