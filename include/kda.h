@@ -169,9 +169,9 @@ int kda_fwd_timed(const uint16_t* q, const uint16_t* k, const uint16_t* v, const
  * GPU, held until the process ends; a fixed-length batch needs none.  The
  * call allocates nothing; the caller passes every input and output.
  * Errors: those of kda_fwd, and KDA_ERR_WORKSPACE (before any HIP call) for
- * a packed batch whose tables need more than the array (at most
- * num_seqs + ceil(tokens / 32 + num_seqs) / L segments, L >= 8, about 16
- * bytes per segment and 12 per sequence: far beyond a million tokens).
+ * a packed batch whose tables need more than the array: about 28 bytes per
+ * sequence (the size kda_fwd_workspace_size gives), so up to about 149,000
+ * packed sequences of any lengths.
  * The array is shared by every call on a GPU: calls that overlap in time on
  * one GPU (other streams, other host threads) race on it and must be
  * serialised by the caller; calls in stream order are safe. */
