@@ -343,19 +343,28 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                         }
                     }
                 }
-                // the bound of a warm-up chunk: max over this wave's channels of
-                // each token's log2 decay (before the prefix sums overwrite G)
-                if (x < out_from) {
+                // the bound (used for warm-up chunks): max over this wave's
+                // channels of each token's log2 decay, from G before the prefix
+                // sums.  Unconditional: a branch around the scan keeps the compiler
+                // from fusing the scan's last DPP step (16 extra moves per chunk).
 #pragma unroll
-                    for (int b = 0; b < 2; ++b) {
-                        rmax[b] = G[b][0];
+                for (int b = 0; b < 2; ++b) {
+                    rmax[b] = G[b][0];
 #pragma unroll
-                        for (int e = 1; e < 8; ++e) rmax[b] = fmaxf(rmax[b], G[b][e]);
-                        rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 16, 64));
-                        rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 32, 64));
-                    }
+                    for (int e = 1; e < 8; ++e) rmax[b] = fmaxf(rmax[b], G[b][e]);
                 }
                 row_scan16_n<16>(&G[0][0]);
+                // the scan's results used here: later uses inside lane-masked
+                // blocks would otherwise pull its last step there, unfused
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(G[b][e]));
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 16, 64));
+                    rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 32, 64));
+                }
             }
             if (x < out_from && g == 0) {
                 float* rm = reinterpret_cast<float*>(lds + L::RMAX) + (slot * NPW + p) * 32;
