@@ -24,11 +24,12 @@
 //     the 16x16 tiles, to V - KG S, to U' and to the output.
 //   compute waves (4): wave w owns V/4 value columns of the [K, V] state in
 //     fp32 MFMA accumulators for the whole segment and runs the recurrence of
-//     kda_recur.hip on the LDS record.  In turn, one of them also finishes a
-//     chunk's record (phase B): the norms, the sum of the partial products,
-//     the masks and beta, both in-block inverses at once by forward
-//     substitution (one per half of the wave), the coupling block
-//     T10 = -T11 A10 T00, and Tb and Aqk.
+//     kda_recur.hip on the LDS record.  In turn, two of them also finish a
+//     chunk's record (phase B, one 16-token block each): the norms, the sum
+//     of the prep waves' partial products, the masks and beta, the in-block
+//     inverse by forward substitution, and the block's Tb and Aqk tiles.  The
+//     coupling block Tb10 = -T11 A10 Tb00 is formed by every compute wave at
+//     its next step from fp32 tiles the two left in LDS.
 // One barrier per iteration.  In iteration i the compute waves run chunk i,
 // phase B finishes chunk i+1 and phase A fills chunk i+2; three records are
 // live in LDS.
@@ -289,7 +290,10 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                 d.braw[b] = *reinterpret_cast<const uint16_t*>(bt + r * 2u);
             }
         };
-        auto phase_a = [&](const PIn& d, int x) __attribute__((always_inline)) {
+        // `issue_loads` runs between the decay scan and the rest: the next
+        // chunks' loads leave the wave after its first long run of arithmetic,
+        // not at the barrier where every wave of the CU issues at once
+        auto phase_a = [&](const PIn& d, int x, auto&& issue_loads) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
             (void)lr; (void)lg;
             const int slot = x & 1;
@@ -366,6 +370,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 32, 64));
                 }
             }
+            issue_loads();
             if (x < out_from && g == 0) {
                 float* rm = reinterpret_cast<float*>(lds + L::RMAX) + (slot * NPW + p) * 32;
                 rm[m] = rmax[0];
@@ -934,9 +939,16 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     }
                     constexpr int sa = u, sl = (u + 2) % 3;  // ring slot of chunk y: y mod 3
                     // two chunks ahead: the loads have two iterations to land
-                    load_in(pin[sl], min(it + 4, n_it - 1));  // unconditional (see load_v)
-                    if (it + 2 < n_it) phase_a(pin[sa], it + 2);
-                    else touch(pin[sa]);
+                    // unconditional (see load_v)
+                    auto loads = [&]() __attribute__((always_inline)) {
+                        load_in(pin[sl], min(it + 4, n_it - 1));
+                    };
+                    if (it + 2 < n_it) {
+                        phase_a(pin[sa], it + 2, loads);
+                    } else {
+                        loads();
+                        touch(pin[sa]);
+                    }
                     __syncthreads();
                 });
             }
