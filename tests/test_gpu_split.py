@@ -14,6 +14,7 @@ The cases cover the regimes of both bounds: state forgotten within a few
 chunks (default decay), within part of a segment, kept across segments (slow
 decay: the staged scan applies transitions, the fused segments restart) and
 no decay at all."""
+import numpy as np
 import pytest
 import torch
 
@@ -107,3 +108,31 @@ def test_fused_segments_short_and_warm_up(seg):
     w = inputs.gdn_workload(2, 300, 2, 64, 128, seed=6950 + seg, init_std=0.05,
                             name=f"fused_seg{seg}_gdn")
     check_parity(w, first_tokens=32, segment_chunks=seg)
+
+
+@pytest.mark.parametrize("seg", [None, 1])
+def test_fused_many_packed_sequences(seg):
+    """Three hundred packed sequences of 0..70 tokens (zeros included): many
+    more segments than compute units, most of them one or two chunks, so the
+    segment table, its longest-first order and the per-sequence final states
+    are exercised at scale; KDA and GDN."""
+    rng = np.random.default_rng(7100)
+    lengths = rng.integers(0, 71, size=300).tolist()
+    lengths[:3] = [0, 0, 1]
+    w = inputs.kda_workload(1, 0, 2, 64, 64, seed=7101, init_std=0.05, lengths=lengths,
+                            name="fused_many_packed_kda")
+    kw = {} if seg is None else {"segment_chunks": seg}
+    check_parity(w, first_tokens=32, **kw)
+    w = inputs.gdn_workload(1, 0, 2, 64, 64, seed=7102, init_std=0.05, lengths=lengths,
+                            name="fused_many_packed_gdn")
+    check_parity(w, first_tokens=32, **kw)
+
+
+def test_fused_segments_beyond_sort_buckets():
+    """Segments of 1100 chunks: more than the 1024 length buckets of the
+    longest-first sort (the longest share its last bucket), on two sequences
+    of over 33,000 tokens around a short one."""
+    lengths = [33000, 5, 34000]
+    w = inputs.kda_workload(1, 0, 1, 64, 64, seed=7200, init_std=0.05, lengths=lengths,
+                            name="fused_long_segments")
+    check_parity(w, first_tokens=32, segment_chunks=1100)
