@@ -75,10 +75,11 @@ struct FusedLayout {
     static constexpr int GTOK = BETA + 2 * 32 * 4;                  // [2][32] float
     static constexpr int TOT = GTOK + 2 * 32 * 4;                   // [NPW][64] float
     static constexpr int AMAT = TOT + NPW * 64 * 4;                 // [2][256] float
-    // [2][3][256] float: per chunk (slot x & 1) Tb00 row-major, T11^T and A10
-    // in D layout, from phase B for the coupling block the compute waves form
+    // [2][2][256] float: per chunk (slot x & 1) Tb00 row-major and
+    // (T11 A10)^T in D layout, from phase B for the coupling block the
+    // compute waves form
     static constexpr int CPL = AMAT + 2 * 256 * 4;
-    static constexpr int INVN = CPL + 2 * 3 * 256 * 4;              // [NBUF][64] float
+    static constexpr int INVN = CPL + 2 * 2 * 256 * 4;              // [NBUF][64] float
     static constexpr int MISC = INVN + NBUF * 64 * 4;               // bound sum
     static constexpr int BYTES = MISC + 16;
     static_assert(BYTES <= 160 * 1024, "LDS of one CU");
@@ -574,9 +575,10 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         };
         // phase B: finish chunk x's record, split over two compute waves that
         // run at the same time: B0 the norms and block 0 (A00, Aqk00, T00),
-        // B1 block 1 (A11, Aqk11, T11), the coupling tiles A10 and Aqk10 and
-        // the decay bound.  The coupling block Tb10 = -T11 A10 Tb00 of Tb is
-        // left to the compute waves (from the fp32 tiles in CPL).
+        // B1 block 1 (A11, Aqk11, T11), the coupling tiles A10 and Aqk10, the
+        // product T11 A10 and the decay bound.  The coupling block
+        // Tb10 = -(T11 A10) Tb00 of Tb is left to the compute waves (from the
+        // fp32 tiles in CPL: B0's and B1's results meet only there).
         // The sum of the prep waves' partial products of tile t (fixed order):
         auto tile = [&](int slot, int t, int lane) __attribute__((always_inline)) {
             const floatx4* part =
@@ -644,7 +646,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
             *reinterpret_cast<bf16xEL*>(rec + R::AQK + lane * (2 * EL)) = pack_tok(aq, zero);
             *reinterpret_cast<bf16xEL*>(rec + R::TB + lane * (2 * EL)) = pack_tok(tb, zero);
-            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 768;
+            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 512;
             *reinterpret_cast<floatx4*>(cpl + 16 * m + 4 * g) = tb;  // Tb00 row-major
         };
         auto phase_b1 = [&](int x) __attribute__((always_inline)) {
@@ -689,9 +691,10 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             // Tb block 1 = [Tb10 | Tb11]: the Tb11 half here
             *reinterpret_cast<bf16xEL*>(rec + R::AQK + (64 + lane) * (2 * EL)) = pack_tok(p5, aq);
             *reinterpret_cast<bf16x4*>(rec + R::TB + (64 + lane) * (2 * EL) + EL) = tb11;
-            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 768;
-            *reinterpret_cast<floatx4*>(cpl + 256 + 4 * lane) = TT1;
-            *reinterpret_cast<floatx4*>(cpl + 512 + 4 * lane) = a10;
+            // M(A10, T11^T) = (T11 A10)^T in D layout: once here instead of
+            // in every compute wave
+            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 512;
+            *reinterpret_cast<floatx4*>(cpl + 256 + 4 * lane) = mt(a10, TT1);
             // the chunk's bound (sum over its tokens of max_c log2 a), warm-up chunks
             if (x < out_from) {
                 const float* rm = reinterpret_cast<const float*>(lds + L::RMAX) + slot * NPW * 32;
@@ -791,18 +794,17 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     yc[ct][i] = (bf16)Y[ct][0][i];
                     yc[ct][4 + i] = (bf16)Y[ct][1][i];
                 }
-            // Tb's block 1 = [Tb10 | Tb11]: Tb10 = -T11 A10 Tb00 from phase B's
-            // fp32 tiles (the same in every compute wave), Tb11 from the record
+            // Tb's block 1 = [Tb10 | Tb11]: Tb10 = -(T11 A10) Tb00 from phase
+            // B's fp32 tiles (the same in every compute wave), Tb11 from the record
             bf16xEL tb1 = *reinterpret_cast<const bf16xEL*>(buf + R::TB + (64 + lane) * (2 * EL));
             {
-                const float* cpl = reinterpret_cast<const float*>(lds + L::CPL) + (x & 1) * 768;
+                const float* cpl = reinterpret_cast<const float*>(lds + L::CPL) + (x & 1) * 512;
                 floatx4 tb00d;  // Tb00[4g + i][m]
 #pragma unroll
                 for (int i = 0; i < 4; ++i) tb00d[i] = cpl[16 * (4 * lg + i) + lr];
-                const floatx4 tt1 = *reinterpret_cast<const floatx4*>(cpl + 256 + 4 * lane);
-                const floatx4 a10 = *reinterpret_cast<const floatx4*>(cpl + 512 + 4 * lane);
-                // M(Tb00, M(A10, T11^T)) = (T11 A10 Tb00)^T: element i is [m][4g + i]
-                const floatx4 c = mt(tb00d, mt(a10, tt1));
+                const floatx4 ta = *reinterpret_cast<const floatx4*>(cpl + 256 + 4 * lane);
+                // M(Tb00, (T11 A10)^T) = (T11 A10 Tb00)^T: element i is [m][4g + i]
+                const floatx4 c = mt(tb00d, ta);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) tb1[i] = (bf16)(-c[i]);
             }
