@@ -7,7 +7,10 @@ GPU를 위한 선형 어텐션 고성능 CUDA 커널 라이브러리", section "
 forward pass is kda_fwd / gdn_fwd and the backward pass kda_bwd / gdn_bwd of the
 C ABI; when an input needs a gradient the forward pass is kda_fwd_save /
 gdn_fwd_save, which keeps in a workspace what the backward pass would otherwise
-recompute, and the backward pass kda_bwd_saved / gdn_bwd_saved reuses it.
+recompute, and the backward pass kda_bwd_saved / gdn_bwd_saved reuses it.  That
+forward pass is the two-stage one (its records are what the backward pass
+needs), so with a gradient requested o differs from kda_fwd's single-launch o
+by rounding only.
 This module only checks and forwards arguments (no arithmetic of the method
 runs outside the library).
 

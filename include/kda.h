@@ -355,8 +355,10 @@ int gdn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float
             size_t workspace_bytes, void* stream);
 
 /* Training pair: a forward pass that keeps what its backward pass would
- * recompute, and that backward pass.  Same computation as kda_fwd /
- * gdn_fwd and kda_bwd / gdn_bwd (results bit for bit equal to theirs); the
+ * recompute, and that backward pass.  Same computation as the two-stage
+ * forward pass (kda_fwd_split / gdn_fwd_split with no splitting) and
+ * kda_bwd / gdn_bwd (results bit for bit equal to theirs); the single-launch
+ * kda_fwd / gdn_fwd forms the same function in another rounding order.  The
  * pages' training use (cuLA README mirror, section "Usage": o.backward(do)
  * after the forward call) runs the two back to back on the same inputs.
  *

@@ -29,7 +29,7 @@ import torch
 import chunked_gated_delta_kda_amd as kda
 from chunked_gated_delta_kda_amd import inputs
 from oracle import backward as obwd
-from parity_util import say, to64
+from parity_util import assert_close, say, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -257,7 +257,10 @@ def test_bwd_empty_sequence_batch():
 @pytest.mark.parametrize("kind", ["kda", "kda packed", "gdn"])
 def test_saved_pair_equals_recompute(kind):
     """kda_fwd_save + kda_bwd_saved (and the GDN pair) run the same arithmetic as
-    kda_fwd and kda_bwd: outputs, final states and every gradient equal bit for bit."""
+    the two-stage forward pass (kda_fwd_split, no splitting) and kda_bwd: outputs,
+    final states and every gradient equal bit for bit.  The single-launch
+    kda_fwd / gdn_fwd forms the same function in another rounding order: equal
+    to the pair's forward within the forward pass's parity bounds."""
     if kind == "gdn":
         w = inputs.gdn_workload(2, 150, 2, 128, 128, seed=8100, init_std=0.05)
     elif kind == "kda packed":
@@ -270,7 +273,9 @@ def test_saved_pair_equals_recompute(kind):
     do, dfin = do.to(DEV), dfin.to(DEV)
     cu = d["cu_seqlens"]
     if kind == "gdn":
-        o1, s1 = kda.gdn_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, d["initial_state"])
+        o1, s1 = kda.gdn_fwd_split(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale,
+                                   d["initial_state"], segment_chunks=-1)
+        o3, s3 = kda.gdn_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale, d["initial_state"])
         o2, s2, ws = kda.gdn_fwd_save(d["q"], d["k"], d["v"], d["g"], d["beta"], w.scale,
                                       d["initial_state"])
         r1 = kda.gdn_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, w.scale, d["initial_state"],
@@ -279,13 +284,18 @@ def test_saved_pair_equals_recompute(kind):
                                d["initial_state"], dfin)
     else:
         args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"])
-        o1, s1 = kda.kda_fwd(*args, w.lower_bound, w.scale, d["initial_state"], cu_seqlens=cu)
+        o1, s1 = kda.kda_fwd_split(*args, w.lower_bound, w.scale, d["initial_state"],
+                                   cu_seqlens=cu, segment_chunks=-1)
+        o3, s3 = kda.kda_fwd(*args, w.lower_bound, w.scale, d["initial_state"], cu_seqlens=cu)
         o2, s2, ws = kda.kda_fwd_save(*args, w.lower_bound, w.scale, d["initial_state"],
                                       cu_seqlens=cu)
         r1 = kda.kda_bwd(*args, do, w.lower_bound, w.scale, d["initial_state"], dfin, cu)
         r2 = kda.kda_bwd_saved(*args, do, ws, w.lower_bound, w.scale, d["initial_state"], dfin, cu)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert_close("o (single launch vs pair)", o3.double().cpu().numpy(), o2.double().cpu().numpy())
+    assert_close("final_state (single launch vs pair)", s3.double().cpu().numpy(),
+                 s2.double().cpu().numpy())
     for name, t in r1.items():
         if t is not None:
             assert torch.equal(r2[name], t), name
