@@ -595,8 +595,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         // A[r][m] (into am, row-major, r = 4 g + i) and Aqk[m][r] of block b from
         // the raw-key partials: A[r][m] = beta_r k^_r . k^_m, decay-weighted for GDN
         auto build_block = [&](int slot, int b, const floatx4& pa, const floatx4& pq,
-                               const floatx4& ikr, float ikm, float* am, int m, int g)
-            __attribute__((always_inline)) {
+                               const floatx4& ikr, float ikm, float* am, int m, int g,
+                               floatx4& ad) __attribute__((always_inline)) {
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
             const float* gt = reinterpret_cast<const float*>(lds + L::GTOK) + slot * 32;
             floatx4 aq;
@@ -610,10 +610,29 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     dec_rm = r > m ? exp2_hw(gr - gm) : 0.f;
                     dec_mr = m >= r ? exp2_hw(gm - gr) : 0.f;
                 }
-                am[16 * r + m] = m < r ? br * pa[i] * dec_rm : 0.f;  // A[r][m]
-                aq[i] = r <= m ? pq[i] * dec_mr : 0.f;                // Aqk[m][r]
+                ad[i] = m < r ? br * pa[i] * dec_rm : 0.f;  // A[r][m] (D layout)
+                am[16 * r + m] = ad[i];
+                aq[i] = r <= m ? pq[i] * dec_mr : 0.f;     // Aqk[m][r]
             }
             return aq;
+        };
+        // T^T of a block in D layout (T^T[4g + i][m] = T[m][4g + i]) from A in
+        // D layout (ad) and row-major in LDS (am, written and synchronised):
+        // KDA by fp32 forward substitution on the VALU; GDN, whose phase B
+        // and recurrence step are the iteration's critical path (its prep
+        // waves' elementwise work is light), by the fp32 doubling product on
+        // the otherwise idle MFMA unit.
+        auto block_inverse_t = [&](const floatx4& ad, const float* am, int m, int g)
+            __attribute__((always_inline)) {
+            if constexpr (GDN) {
+                const floatx4 atd = *reinterpret_cast<const floatx4*>(am + 16 * m + 4 * g);
+                return tri_inv_mfma_t(ad, atd, m, g);
+            } else {
+                (void)ad;
+                float t[16];
+                tri_inv_rows(am, m, t);  // every lane: row m of T
+                return pick4(t, g);      // T[m][4g + i]
+            }
         };
         auto phase_b0 = [&](int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
@@ -635,11 +654,10 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             const floatx4 pa = tile(slot, 0, lane), pq = tile(slot, 2, lane);
             wave_lds_sync();
             const floatx4 ikr = *reinterpret_cast<const floatx4*>(invn + 4 * g);
-            const floatx4 aq = build_block(slot, 0, pa, pq, ikr, invn[m], am, m, g);
+            floatx4 ad;
+            const floatx4 aq = build_block(slot, 0, pa, pq, ikr, invn[m], am, m, g, ad);
             wave_lds_sync();
-            float t[16];
-            tri_inv_rows(am, m, t);  // every lane: row m of T00
-            const floatx4 TT0 = pick4(t, g);  // T00[m][4g + i]
+            const floatx4 TT0 = block_inverse_t(ad, am, m, g);  // T00[m][4g + i]
             floatx4 tb;
 #pragma unroll
             for (int i = 0; i < 4; ++i) tb[i] = TT0[i] * bs[4 * g + i];  // Tb00[m][4g + i]
@@ -675,15 +693,14 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             const float ikm1 = 16 + m < nvalid ? rsq_hw(km1 + NORM_EPS) : 0.f;
             const float ikm0 = m < nvalid ? rsq_hw(km0 + NORM_EPS) : 0.f;
             const floatx4 pa = tile(slot, 1, lane), pq = tile(slot, 3, lane);
-            const floatx4 aq = build_block(slot, 1, pa, pq, ikr, ikm1, am, m, g);
+            floatx4 ad;
+            const floatx4 aq = build_block(slot, 1, pa, pq, ikr, ikm1, am, m, g, ad);
             const floatx4 p4 = tile(slot, 4, lane), p5 = tile(slot, 5, lane);
             floatx4 a10;  // A10[4g + i][m] = beta_{16+4g+i} k^_{16+4g+i} . k^_m
 #pragma unroll
             for (int i = 0; i < 4; ++i) a10[i] = bs[16 + 4 * g + i] * ikr[i] * ikm0 * p4[i];
             wave_lds_sync();
-            float t[16];
-            tri_inv_rows(am, m, t);  // every lane: row m of T11
-            const floatx4 TT1 = pick4(t, g);  // T11[m][4g + i]
+            const floatx4 TT1 = block_inverse_t(ad, am, m, g);  // T11[m][4g + i]
             bf16x4 tb11;
 #pragma unroll
             for (int i = 0; i < 4; ++i) tb11[i] = (bf16)(TT1[i] * bs[16 + 4 * g + i]);

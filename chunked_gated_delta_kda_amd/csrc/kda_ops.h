@@ -128,6 +128,27 @@ __device__ __forceinline__ void tri_inv_rows(const float* a, int m, float (&t)[1
     t[0] = 0 < m ? -s[0] : t[0];
 }
 
+// T^T for T = (I + A)^-1, A strictly lower-triangular 16 x 16, in fp32 on
+// MFMA: the product (I - A)(I + A^2)(I + A^4)(I + A^8), exact in exact
+// arithmetic because A^16 = 0 (the doubling form of the inverse).  ad / atd
+// are A and A^T in D layout (lane n + 16 g, element i: row 4 g + i, column
+// n); the result is T^T in D layout, i.e. element i = T[n][4 g + i].  Eight
+// products M(P, Q) = P^T Q (32 v_mfma_f32_16x16x4_f32, four deep).  With
+// near-parallel keys the partial products grow to ~10^3 before they
+// cancel, so the result carries ~10^3 fp32 ulps (~1e-4 relative), below
+// the bf16 rounding of the stored Tb.
+__device__ __forceinline__ floatx4 tri_inv_mfma_t(floatx4 ad, floatx4 atd, int m, int g) {
+    floatx4 eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eye[i] = 4 * g + i == m ? 1.f : 0.f;
+    const floatx4 a2 = mt(atd, ad), a2t = mt(ad, atd);  // A^2, (A^2)^T
+    const floatx4 a4 = mt(a2t, a2), a4t = mt(a2, a2t);  // A^4, (A^4)^T
+    const floatx4 a8t = mt(a4, a4t);                    // (A^8)^T
+    const floatx4 x1 = mt(eye - atd, eye + a2);         // (I - A)(I + A^2)
+    const floatx4 x2 = mt(eye + a4t, x1);               // (I + A^4) X1
+    return mt(x2, eye + a8t);                           // ((I + A^8) X2)^T
+}
+
 // t[4 g + i], i = 0..3, for a runtime g in 0..3
 __device__ __forceinline__ floatx4 pick4(const float (&t)[16], int g) {
     floatx4 r;

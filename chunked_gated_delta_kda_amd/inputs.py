@@ -150,9 +150,14 @@ def kda_workload(B, T, H, K, V, seed, *, g_std=0.1, g_mean=0.0, A_log_std=0.01,
 
 
 def gdn_workload(B, T, H, K, V, seed, *, init_std=None, lengths=None, decay_shift=0.0,
-                 name="gdn"):
+                 beta_mean=0.0, beta_value=None, g_value=None, key_cos=None, key_pool=None,
+                 q_equals_k=False, name="gdn"):
     """GDN inputs: q,k,v ~N(0,1) bf16; g fp32 [B,T,H] = clamp(-softplus(N(0,1) + shift), -5, 0);
-    beta = sigmoid(N(0,1)) rounded to bf16; initial_state ~N(0, init_std) or None."""
+    beta = sigmoid(N(beta_mean, 1)) rounded to bf16; initial_state ~N(0, init_std) or None.
+
+    Stress variants as for kda_workload (drawn after everything above):
+    ``beta_value`` (a constant probability), ``g_value`` (a constant log
+    decay), ``key_cos``, ``key_pool`` and ``q_equals_k``."""
     gen = torch.Generator().manual_seed(seed)
     cu = None
     if lengths is not None:
@@ -165,8 +170,22 @@ def gdn_workload(B, T, H, K, V, seed, *, init_std=None, lengths=None, decay_shif
     v = _normal(gen, (B, T, H, V)).to(torch.bfloat16)
     g = torch.clamp(-torch.nn.functional.softplus(_normal(gen, (B, T, H)) + decay_shift),
                     -5.0, 0.0)
-    beta = torch.sigmoid(_normal(gen, (B, T, H))).to(torch.bfloat16)
+    beta = torch.sigmoid(_normal(gen, (B, T, H), 1.0, beta_mean)).to(torch.bfloat16)
     h0 = None if init_std is None else _normal(gen, (N, H, K, V), init_std)
+    if beta_value is not None:
+        beta = torch.full((B, T, H), float(beta_value)).to(torch.bfloat16)
+    if g_value is not None:
+        g = torch.full((B, T, H), float(g_value), dtype=torch.float32)
+    if key_cos is not None:
+        u = _normal(gen, (1, 1, H, K))
+        z = _normal(gen, (B, T, H, K))
+        k = (u * float(key_cos) ** 0.5 + z * (1.0 - float(key_cos)) ** 0.5).to(torch.bfloat16)
+    if key_pool is not None:
+        pool = _normal(gen, (H, int(key_pool), K))
+        idx = torch.randint(0, int(key_pool), (B, T, H), generator=gen)
+        k = pool[torch.arange(H)[None, None, :], idx].to(torch.bfloat16)
+    if q_equals_k:
+        q = k.clone()
     return Workload("gdn", name, q, k, v, g, beta, None, None, -5.0, K ** -0.5, h0, cu)
 
 

@@ -72,6 +72,29 @@ def test_retrieval_repeated_keys(pool):
     assert_close("o vs scale * v", to64(o), w.scale * w.v.double().numpy())
 
 
+@pytest.mark.parametrize("cos", [0.8, 0.95])
+def test_gdn_correlated_keys(cos):
+    """The correlated-key stress for GDN (its block inverses run as the fp32
+    doubling product on MFMA): keys of a head share a direction, beta ~0.88,
+    slow decay, so A has entries near 1 and the product's partial sums grow
+    far above the O(1) inverse before they cancel."""
+    w = inputs.gdn_workload(2, 320, 3, 128, 128, seed=3450 + int(round(cos * 100)),
+                            decay_shift=-6.0, beta_mean=2.0, key_cos=cos, init_std=0.05,
+                            name=f"gdn_corr_keys_{cos}")
+    check_parity(w, first_tokens=32)
+
+
+@pytest.mark.parametrize("pool", [4, 8])
+def test_gdn_retrieval_repeated_keys(pool):
+    """The retrieval invariant for GDN: beta = 1, no decay (g = 0), q = k drawn
+    from `pool` vectors per head; then o_t = scale * v_t."""
+    w = inputs.gdn_workload(1, 512, 4, 128, 128, seed=3550 + pool, beta_value=1.0, g_value=0.0,
+                            key_pool=pool, q_equals_k=True, init_std=0.05,
+                            name=f"gdn_retrieval_pool{pool}")
+    o, _ = check_parity(w)
+    assert_close("o vs scale * v", to64(o), w.scale * w.v.double().numpy())
+
+
 def test_lower_bound_other_than_default():
     w = inputs.kda_workload(1, 200, 2, 128, 128, seed=3150, g_mean=4.0, g_std=1.0,
                             lower_bound=-1.5, init_std=0.05, name="lower_bound_-1.5")
