@@ -24,12 +24,13 @@
 //     the 16x16 tiles, to V - KG S, to U' and to the output.
 //   compute waves (4): wave w owns V/4 value columns of the [K, V] state in
 //     fp32 MFMA accumulators for the whole segment and runs the recurrence of
-//     kda_recur.hip on the LDS record.  In turn, two of them also finish a
-//     chunk's record (phase B, one 16-token block each): the norms, the sum
-//     of the prep waves' partial products, the masks and beta, the in-block
-//     inverse by forward substitution, and the block's Tb and Aqk tiles.  The
-//     coupling block Tb10 = -T11 A10 Tb00 is formed by every compute wave at
-//     its next step from fp32 tiles the two left in LDS.
+//     kda_recur.hip on the LDS record.  Each of them also finishes a quarter
+//     of the next chunk's record (phase B, in four parts that rotate over the
+//     waves): two parts form a block's A (sums of the prep waves' partial
+//     products, beta, norms), its inverse and Tb; the other two the norms,
+//     the Aqk tiles and the decay bound.  The coupling block
+//     Tb10 = -(T11 A10) Tb00 is formed by every compute wave at its next
+//     step from fp32 tiles the two inverse parts left in LDS.
 // One barrier per iteration.  In iteration i the compute waves run chunk i,
 // phase B finishes chunk i+1 and phase A fills chunk i+2; three records are
 // live in LDS.
@@ -573,12 +574,14 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     else d.w[bb][i] = *reinterpret_cast<const uint16_t*>(vb + off);
                 }
         };
-        // phase B: finish chunk x's record, split over two compute waves that
-        // run at the same time: B0 the norms and block 0 (A00, Aqk00, T00),
-        // B1 block 1 (A11, Aqk11, T11), the coupling tiles A10 and Aqk10, the
-        // product T11 A10 and the decay bound.  The coupling block
+        // phase B: finish chunk x's record in four parts, one per compute wave,
+        // that run at the same time: P0 block 0 (A00, T00, Tb00), P1 block 1
+        // (A11, T11, Tb11, the coupling tile A10 and the product T11 A10), P2
+        // the chunk's norms and Aqk00, P3 Aqk11, Aqk10 and the decay bound.
+        // The two substitutions, the long chains, sit on SIMDs two apart; the
+        // light parts keep them free of everything else.  The coupling block
         // Tb10 = -(T11 A10) Tb00 of Tb is left to the compute waves (from the
-        // fp32 tiles in CPL: B0's and B1's results meet only there).
+        // fp32 tiles in CPL: P0's and P1's results meet only there).
         // The sum of the prep waves' partial products of tile t (fixed order):
         auto tile = [&](int slot, int t, int lane) __attribute__((always_inline)) {
             const floatx4* part =
@@ -592,27 +595,58 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             }
             return r;
         };
-        // A[r][m] (into am, row-major, r = 4 g + i) and Aqk[m][r] of block b from
-        // the raw-key partials: A[r][m] = beta_r k^_r . k^_m, decay-weighted for GDN
-        auto build_block = [&](int slot, int b, const floatx4& pa, const floatx4& pq,
-                               const floatx4& ikr, float ikm, float* am, int m, int g,
-                               floatx4& ad) __attribute__((always_inline)) {
+        // 1/||k|| of chunk token s (lane-varying) and of block b's rows
+        // 4 g + i, from the prep waves' partial squared norms; 0 for padding
+        auto token_norm = [&](int slot, int s, int nvalid) __attribute__((always_inline)) {
+            const float* nr = reinterpret_cast<const float*>(lds + L::NRM) + slot * NPW * 64;
+            float v = nr[s];
+#pragma unroll
+            for (int pp = 1; pp < NPW; ++pp) v += nr[pp * 64 + s];
+            return s < nvalid ? rsq_hw(v + NORM_EPS) : 0.f;
+        };
+        auto row_norms = [&](int slot, int b, int nvalid, int g) __attribute__((always_inline)) {
+            const float* nr = reinterpret_cast<const float*>(lds + L::NRM) + slot * NPW * 64;
+            floatx4 ikr = *reinterpret_cast<const floatx4*>(nr + 16 * b + 4 * g);
+#pragma unroll
+            for (int pp = 1; pp < NPW; ++pp) {
+                const floatx4 y = *reinterpret_cast<const floatx4*>(nr + pp * 64 + 16 * b + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ikr[i] += y[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ikr[i] = 16 * b + 4 * g + i < nvalid ? rsq_hw(ikr[i] + NORM_EPS) : 0.f;
+            return ikr;
+        };
+        // A[r][m] of block b (r = 4 g + i) into am (row-major) and ad (D
+        // layout): beta_r k^_r . k^_m from the raw-key partials, decay-weighted
+        // for GDN
+        auto build_a = [&](int slot, int b, const floatx4& pa, const floatx4& ikr, float ikm,
+                           float* am, int m, int g, floatx4& ad) __attribute__((always_inline)) {
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
             const float* gt = reinterpret_cast<const float*>(lds + L::GTOK) + slot * 32;
-            floatx4 aq;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;  // row of this element; its column is m
                 const float br = bs[16 * b + r] * ikr[i] * ikm;
-                float dec_rm = 1.f, dec_mr = 1.f;
-                if constexpr (GDN) {
-                    const float gr = gt[16 * b + r], gm = gt[16 * b + m];
-                    dec_rm = r > m ? exp2_hw(gr - gm) : 0.f;
-                    dec_mr = m >= r ? exp2_hw(gm - gr) : 0.f;
-                }
-                ad[i] = m < r ? br * pa[i] * dec_rm : 0.f;  // A[r][m] (D layout)
+                float dec = 1.f;
+                if constexpr (GDN) dec = r > m ? exp2_hw(gt[16 * b + r] - gt[16 * b + m]) : 0.f;
+                ad[i] = m < r ? br * pa[i] * dec : 0.f;
                 am[16 * r + m] = ad[i];
-                aq[i] = r <= m ? pq[i] * dec_mr : 0.f;     // Aqk[m][r]
+            }
+        };
+        // Aqk[m][r] of block b (raw q . k; the norms are applied by the
+        // recurrence), decay-weighted for GDN
+        auto build_aq = [&](int slot, int b, const floatx4& pq, int m, int g)
+            __attribute__((always_inline)) {
+            const float* gt = reinterpret_cast<const float*>(lds + L::GTOK) + slot * 32;
+            floatx4 aq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g + i;
+                float dec = 1.f;
+                if constexpr (GDN) dec = m >= r ? exp2_hw(gt[16 * b + m] - gt[16 * b + r]) : 0.f;
+                aq[i] = r <= m ? pq[i] * dec : 0.f;
             }
             return aq;
         };
@@ -634,14 +668,65 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                 return pick4(t, g);      // T[m][4g + i]
             }
         };
-        auto phase_b0 = [&](int x) __attribute__((always_inline)) {
+        // Phase B, part 0: block 0's A00, T00 and Tb00
+        auto phase_p0 = [&](int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
             const int slot = x & 1;
             unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
             float* am = reinterpret_cast<float*>(lds + L::AMAT);
+            const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
+            const floatx4 ikr = row_norms(slot, 0, nvalid, g);
+            const float ikm = token_norm(slot, m, nvalid);
+            const floatx4 pa = tile(slot, 0, lane);
+            floatx4 ad;
+            build_a(slot, 0, pa, ikr, ikm, am, m, g, ad);
+            wave_lds_sync();
+            const floatx4 TT0 = block_inverse_t(ad, am, m, g);  // T00[m][4g + i]
+            floatx4 tb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tb[i] = TT0[i] * bs[4 * g + i];  // Tb00[m][4g + i]
+            const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<bf16xEL*>(rec + R::TB + lane * (2 * EL)) = pack_tok(tb, zero);
+            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 512;
+            *reinterpret_cast<floatx4*>(cpl + 16 * m + 4 * g) = tb;  // Tb00 row-major
+        };
+        // Phase B, part 1: block 1's A11, T11, Tb11 and the product T11 A10
+        auto phase_p1 = [&](int x) __attribute__((always_inline)) {
+            const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
+            const int slot = x & 1;
+            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
+            const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
+            float* am = reinterpret_cast<float*>(lds + L::AMAT) + 256;
+            const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
+            const floatx4 ikr = row_norms(slot, 1, nvalid, g);
+            const float ikm1 = token_norm(slot, 16 + m, nvalid), ikm0 = token_norm(slot, m, nvalid);
+            const floatx4 pa = tile(slot, 1, lane), p4 = tile(slot, 4, lane);
+            floatx4 ad;
+            build_a(slot, 1, pa, ikr, ikm1, am, m, g, ad);
+            floatx4 a10;  // A10[4g + i][m] = beta_{16+4g+i} k^_{16+4g+i} . k^_m
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a10[i] = bs[16 + 4 * g + i] * ikr[i] * ikm0 * p4[i];
+            wave_lds_sync();
+            const floatx4 TT1 = block_inverse_t(ad, am, m, g);  // T11[m][4g + i]
+            bf16x4 tb11;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tb11[i] = (bf16)(TT1[i] * bs[16 + 4 * g + i]);
+            // Tb block 1 = [Tb10 | Tb11]: the Tb11 half here
+            *reinterpret_cast<bf16x4*>(rec + R::TB + (64 + lane) * (2 * EL) + EL) = tb11;
+            // M(A10, T11^T) = (T11 A10)^T in D layout: once here instead of
+            // in every compute wave
+            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 512;
+            *reinterpret_cast<floatx4*>(cpl + 256 + 4 * lane) = mt(a10, TT1);
+        };
+        // Phase B, part 2: the chunk's 1/||k|| and 1/||q|| (for the recurrence)
+        // and Aqk's block 0
+        auto phase_p2 = [&](int x) __attribute__((always_inline)) {
+            const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
+            const int slot = x & 1;
+            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
             // 1/||k|| (lanes 0..31) and 1/||q|| (lanes 32..63) of the chunk's
-            // tokens from the prep waves' partial squared norms; 0 for padding
+            // tokens; 0 for padding
             float* invn = reinterpret_cast<float*>(lds + L::INVN) + (x % 3) * 64;
             {
                 const float* nr = reinterpret_cast<const float*>(lds + L::NRM) + slot * NPW * 64;
@@ -651,67 +736,20 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                 const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
                 invn[lane] = (lane & 31) < nvalid ? rsq_hw(v + NORM_EPS) : 0.f;
             }
-            const floatx4 pa = tile(slot, 0, lane), pq = tile(slot, 2, lane);
-            wave_lds_sync();
-            const floatx4 ikr = *reinterpret_cast<const floatx4*>(invn + 4 * g);
-            floatx4 ad;
-            const floatx4 aq = build_block(slot, 0, pa, pq, ikr, invn[m], am, m, g, ad);
-            wave_lds_sync();
-            const floatx4 TT0 = block_inverse_t(ad, am, m, g);  // T00[m][4g + i]
-            floatx4 tb;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tb[i] = TT0[i] * bs[4 * g + i];  // Tb00[m][4g + i]
+            const floatx4 aq = build_aq(slot, 0, tile(slot, 2, lane), m, g);
             const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
             *reinterpret_cast<bf16xEL*>(rec + R::AQK + lane * (2 * EL)) = pack_tok(aq, zero);
-            *reinterpret_cast<bf16xEL*>(rec + R::TB + lane * (2 * EL)) = pack_tok(tb, zero);
-            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 512;
-            *reinterpret_cast<floatx4*>(cpl + 16 * m + 4 * g) = tb;  // Tb00 row-major
         };
-        auto phase_b1 = [&](int x) __attribute__((always_inline)) {
+        // Phase B, part 3: Aqk's block 1 and the decay bound of warm-up chunks
+        auto phase_p3 = [&](int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
             const int slot = x & 1;
             unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
-            float* am = reinterpret_cast<float*>(lds + L::AMAT) + 256;
-            // 1/||k|| of block-1 rows 4 g + i and of columns m of both blocks
-            // (formed here too: phase B0 runs at the same time)
-            const float* nr = reinterpret_cast<const float*>(lds + L::NRM) + slot * NPW * 64;
-            const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
-            floatx4 ikr = *reinterpret_cast<const floatx4*>(nr + 16 + 4 * g);
-            float km1 = nr[16 + m], km0 = nr[m];
-#pragma unroll
-            for (int pp = 1; pp < NPW; ++pp) {
-                const floatx4 y = *reinterpret_cast<const floatx4*>(nr + pp * 64 + 16 + 4 * g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ikr[i] += y[i];
-                km1 += nr[pp * 64 + 16 + m];
-                km0 += nr[pp * 64 + m];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ikr[i] = 16 + 4 * g + i < nvalid ? rsq_hw(ikr[i] + NORM_EPS) : 0.f;
-            const float ikm1 = 16 + m < nvalid ? rsq_hw(km1 + NORM_EPS) : 0.f;
-            const float ikm0 = m < nvalid ? rsq_hw(km0 + NORM_EPS) : 0.f;
-            const floatx4 pa = tile(slot, 1, lane), pq = tile(slot, 3, lane);
-            floatx4 ad;
-            const floatx4 aq = build_block(slot, 1, pa, pq, ikr, ikm1, am, m, g, ad);
-            const floatx4 p4 = tile(slot, 4, lane), p5 = tile(slot, 5, lane);
-            floatx4 a10;  // A10[4g + i][m] = beta_{16+4g+i} k^_{16+4g+i} . k^_m
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a10[i] = bs[16 + 4 * g + i] * ikr[i] * ikm0 * p4[i];
-            wave_lds_sync();
-            const floatx4 TT1 = block_inverse_t(ad, am, m, g);  // T11[m][4g + i]
-            bf16x4 tb11;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tb11[i] = (bf16)(TT1[i] * bs[16 + 4 * g + i]);
-            // Aqk block 1 = [Aqk10 | Aqk11] (Aqk10: all keys before the query);
-            // Tb block 1 = [Tb10 | Tb11]: the Tb11 half here
-            *reinterpret_cast<bf16xEL*>(rec + R::AQK + (64 + lane) * (2 * EL)) = pack_tok(p5, aq);
-            *reinterpret_cast<bf16x4*>(rec + R::TB + (64 + lane) * (2 * EL) + EL) = tb11;
-            // M(A10, T11^T) = (T11 A10)^T in D layout: once here instead of
-            // in every compute wave
-            float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 512;
-            *reinterpret_cast<floatx4*>(cpl + 256 + 4 * lane) = mt(a10, TT1);
+            const floatx4 aq = build_aq(slot, 1, tile(slot, 3, lane), m, g);
+            // Aqk block 1 = [Aqk10 | Aqk11] (Aqk10: all keys before the query)
+            *reinterpret_cast<bf16xEL*>(rec + R::AQK + (64 + lane) * (2 * EL)) =
+                pack_tok(tile(slot, 5, lane), aq);
             // the chunk's bound (sum over its tokens of max_c log2 a), warm-up chunks
             if (x < out_from) {
                 const float* rm = reinterpret_cast<const float*>(lds + L::RMAX) + slot * NPW * 32;
@@ -915,8 +953,12 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     // wait counts cover the loads just issued as well
                     load_v(vin[sv], min(it + 2, n_it - 1));
                     if (it + 1 >= 0 && it + 1 < n_it) {
-                        if (wave == (it + 1) % NCW) phase_b0(it + 1);
-                        else if (wave == (it + 3) % NCW) phase_b1(it + 1);
+                        // parts 0 and 1 (the substitutions) on SIMDs two apart
+                        const int part = (wave - (it + 1)) & (NCW - 1);
+                        if (part == 0) phase_p0(it + 1);
+                        else if (part == 2) phase_p1(it + 1);
+                        else if (part == 1) phase_p2(it + 1);
+                        else phase_p3(it + 1);
                     }
                     if (it >= 0 && it < n_it) compute(it, vin[sc]);
                     __syncthreads();
