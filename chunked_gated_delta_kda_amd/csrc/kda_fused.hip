@@ -656,18 +656,14 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         // and recurrence step are the iteration's critical path (its prep
         // waves' elementwise work is light), by the fp32 doubling product on
         // the otherwise idle MFMA unit.
-        auto block_inverse_t = [&](const floatx4& ad, const float* am, int m, int g)
-            __attribute__((always_inline)) {
-            if constexpr (GDN) {
-                const floatx4 atd = *reinterpret_cast<const floatx4*>(am + 16 * m + 4 * g);
-                return tri_inv_mfma_t(ad, atd, m, g);
-            } else {
-                (void)ad;
-                float t[16];
-                tri_inv_rows(am, m, t);  // every lane: row m of T
-                return pick4(t, g);      // T[m][4g + i]
-            }
-        };
+        // T^T of a block in D layout (T^T[4g + i][m] = T[m][4g + i]) from A in
+        // D layout (ad) and row-major in LDS (am, written and synchronised;
+        // overwritten here): the two 8 x 8 diagonal blocks by substitution on
+        // the VALU, the coupling of the two on fp32 MFMA (28 fmas and eight
+        // MFMAs per lane instead of the 16 x 16 substitution's 120 fmas; the
+        // iteration is bound by the SIMDs' issue, not by MFMA latency)
+        auto block_inverse_t = [&](const floatx4& ad, float* am, int m, int g)
+            __attribute__((always_inline)) { return tri_inv_split_t(am, ad, m, g); };
         // Phase B, part 0: block 0's A00, T00 and Tb00
         auto phase_p0 = [&](int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;

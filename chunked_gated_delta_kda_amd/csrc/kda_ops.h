@@ -128,25 +128,66 @@ __device__ __forceinline__ void tri_inv_rows(const float* a, int m, float (&t)[1
     t[0] = 0 < m ? -s[0] : t[0];
 }
 
-// T^T for T = (I + A)^-1, A strictly lower-triangular 16 x 16, in fp32 on
-// MFMA: the product (I - A)(I + A^2)(I + A^4)(I + A^8), exact in exact
-// arithmetic because A^16 = 0 (the doubling form of the inverse).  ad / atd
-// are A and A^T in D layout (lane n + 16 g, element i: row 4 g + i, column
-// n); the result is T^T in D layout, i.e. element i = T[n][4 g + i].  Eight
-// products M(P, Q) = P^T Q (32 v_mfma_f32_16x16x4_f32, four deep).  With
-// near-parallel keys the partial products grow to ~10^3 before they
-// cancel, so the result carries ~10^3 fp32 ulps (~1e-4 relative), below
-// the bf16 rounding of the stored Tb.
-__device__ __forceinline__ floatx4 tri_inv_mfma_t(floatx4 ad, floatx4 atd, int m, int g) {
-    floatx4 eye;
+// T^T in D layout (element i = T[m][4 g + i]) for T = (I + A)^-1, A
+// strictly lower-triangular 16 x 16, given row-major in LDS at `a` (which
+// this overwrites) and in D layout in `ad`.  With D = diag(T0, T1) the
+// inverses of the two diagonal 8 x 8 blocks and E the lower-left 8 x 8 block
+// of A, T = D - D E D.  T0 and T1 come from fp32 forward substitution, both
+// at once (lanes 0-7 rows of T0, lanes 8-15 rows of T1: seven steps, 28 fmas
+// per lane); D is transposed through LDS; D E D is two D-layout products on
+// fp32 MFMA (eight v_mfma_f32_16x16x4_f32).
+__device__ __forceinline__ floatx4 tri_inv_split_t(float* a, floatx4 ad, int m, int g) {
+    const int h = m >> 3, mm = m & 7;
+    float t[8], s[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) eye[i] = 4 * g + i == m ? 1.f : 0.f;
-    const floatx4 a2 = mt(atd, ad), a2t = mt(ad, atd);  // A^2, (A^2)^T
-    const floatx4 a4 = mt(a2t, a2), a4t = mt(a2, a2t);  // A^4, (A^4)^T
-    const floatx4 a8t = mt(a4, a4t);                    // (A^8)^T
-    const floatx4 x1 = mt(eye - atd, eye + a2);         // (I - A)(I + A^2)
-    const floatx4 x2 = mt(eye + a4t, x1);               // (I + A^4) X1
-    return mt(x2, eye + a8t);                           // ((I + A^8) X2)^T
+    for (int j = 0; j < 8; ++j) {
+        t[j] = j == mm ? 1.f : 0.f;
+        s[j] = 0.f;
+    }
+    const float* ab = a + 136 * h;  // row 8h, column 8h of A
+    auto read_row = [&](auto kc, float (&row)[8]) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        static_for<0, (k + 3) / 4>([&](auto q) __attribute__((always_inline)) {
+            const floatx4 v = *reinterpret_cast<const floatx4*>(ab + 16 * k + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) row[4 * q + e] = v[e];
+        });
+    };
+    float ra[8];
+    read_row(std::integral_constant<int, 7>{}, ra);
+    static_for<0, 7>([&](auto kk) __attribute__((always_inline)) {
+        constexpr int k = 7 - kk;
+        float na[8];
+        if constexpr (k > 1) read_row(std::integral_constant<int, k - 1>{}, na);
+        if constexpr (k < 7) t[k] = k < mm ? -s[k] : t[k];
+#pragma unroll
+        for (int j = 0; j < k; ++j) s[j] = fmaf(t[k], ra[j], s[j]);
+        if constexpr (k > 1) {
+#pragma unroll
+            for (int j = 0; j < k - 1; ++j) ra[j] = na[j];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    t[0] = 0 < mm ? -s[0] : t[0];
+    // D's rows over A (its reads are done: LDS accesses of a wave run in order)
+    if (g == 0) {
+        *reinterpret_cast<floatx4*>(a + 8 * m) = floatx4{t[0], t[1], t[2], t[3]};
+        *reinterpret_cast<floatx4*>(a + 8 * m + 4) = floatx4{t[4], t[5], t[6], t[7]};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    floatx4 dd, y, e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        dd[i] = (r >> 3) == h ? a[8 * r + mm] : 0.f;                        // D[r][m]
+        y[i] = (g >> 1) == h ? ((g & 1) ? t[4 + i] : t[i]) : 0.f;          // D[m][r]
+        e[i] = (r >= 8 && m < 8) ? ad[i] : 0.f;                             // E[r][m]
+    }
+    const floatx4 x = mt(e, y);   // E^T D^T
+    const floatx4 z = mt(dd, x);  // D^T E^T D^T = (D E D)^T
+    return y - z;
 }
 
 // t[4 g + i], i = 0..3, for a runtime g in 0..3
