@@ -66,11 +66,11 @@ struct FusedLayout {
     static constexpr int CT = V / 64;   // 16-column state tiles per compute wave
     static constexpr int NT = 64 * (NPW + NCW);
     static constexpr int NBUF = 3;      // chunk records in LDS
-    // byte offsets
-    static constexpr int REC = 0;                                   // [NBUF][R::BYTES]
-    static constexpr int PART = REC + NBUF * R::BYTES;              // [2][NPW][6][64] floatx4
-    static constexpr int PART_SLOT = NPW * 6 * 64 * 16;
-    static constexpr int NRM = PART + 2 * PART_SLOT;                // [2][NPW][64] float
+    // byte offsets: the small tables and the partial products first, so that
+    // every access to them is a lane offset plus an instruction immediate
+    // (LDS instructions encode offsets below 64 KB); the records last (their
+    // accesses start from a per-record base anyway)
+    static constexpr int NRM = 0;                                   // [2][NPW][64] float
     static constexpr int RMAX = NRM + 2 * NPW * 64 * 4;             // [2][NPW][32] float
     static constexpr int BETA = RMAX + 2 * NPW * 32 * 4;            // [2][32] float
     static constexpr int GTOK = BETA + 2 * 32 * 4;                  // [2][32] float
@@ -82,7 +82,11 @@ struct FusedLayout {
     static constexpr int CPL = AMAT + 2 * 256 * 4;
     static constexpr int INVN = CPL + 2 * 2 * 256 * 4;              // [NBUF][64] float
     static constexpr int MISC = INVN + NBUF * 64 * 4;               // bound sum
-    static constexpr int BYTES = MISC + 16;
+    static constexpr int PART = MISC + 16;                          // [2][NPW][6][64] floatx4
+    static constexpr int PART_SLOT = NPW * 6 * 64 * 16;
+    static constexpr int REC = PART + 2 * PART_SLOT;                // [NBUF][R::BYTES]
+    static constexpr int BYTES = REC + NBUF * R::BYTES;
+    static_assert(PART % 16 == 0 && REC % 16 == 0, "16-byte LDS accesses");
     static_assert(BYTES <= 160 * 1024, "LDS of one CU");
 };
 
@@ -122,6 +126,15 @@ __device__ __forceinline__ int opaque_lane() {
     int l = (int)(threadIdx.x & 63);
     asm volatile("" : "+v"(l));
     return l;
+}
+
+// A wave-uniform value the compiler cannot see through: record and slot
+// indices derived from the chunk number stay plain products, instead of
+// being strength-reduced into loop-carried addresses whose displacements
+// (negative) no LDS instruction can encode, which costs an add per access.
+__device__ __forceinline__ int opaque_uniform(int v) {
+    asm volatile("" : "+s"(v));
+    return v;
 }
 
 // s_waitcnt immediates that wait until at most eight (none) vector memory
@@ -298,8 +311,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         auto phase_a = [&](const PIn& d, int x, auto&& issue_loads) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
             (void)lr; (void)lg;
-            const int slot = x & 1;
-            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
+            const int slot = opaque_uniform(x & 1);
+            unsigned char* rec = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             const int64_t ct0 = chunk_t0(x);
             const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
             float vmask[2], bsig[2];
@@ -667,8 +680,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         // Phase B, part 0: block 0's A00, T00 and Tb00
         auto phase_p0 = [&](int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
-            const int slot = x & 1;
-            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
+            const int slot = opaque_uniform(x & 1);
+            unsigned char* rec = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
             float* am = reinterpret_cast<float*>(lds + L::AMAT);
             const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
@@ -690,8 +703,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         // Phase B, part 1: block 1's A11, T11, Tb11 and the product T11 A10
         auto phase_p1 = [&](int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
-            const int slot = x & 1;
-            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
+            const int slot = opaque_uniform(x & 1);
+            unsigned char* rec = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
             float* am = reinterpret_cast<float*>(lds + L::AMAT) + 256;
             const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
@@ -719,11 +732,11 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         // and Aqk's block 0
         auto phase_p2 = [&](int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
-            const int slot = x & 1;
-            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
+            const int slot = opaque_uniform(x & 1);
+            unsigned char* rec = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             // 1/||k|| (lanes 0..31) and 1/||q|| (lanes 32..63) of the chunk's
             // tokens; 0 for padding
-            float* invn = reinterpret_cast<float*>(lds + L::INVN) + (x % 3) * 64;
+            float* invn = reinterpret_cast<float*>(lds + L::INVN) + opaque_uniform(x % 3) * 64;
             {
                 const float* nr = reinterpret_cast<const float*>(lds + L::NRM) + slot * NPW * 64;
                 float v = nr[lane];
@@ -739,8 +752,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         // Phase B, part 3: Aqk's block 1 and the decay bound of warm-up chunks
         auto phase_p3 = [&](int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4;
-            const int slot = x & 1;
-            unsigned char* rec = lds + L::REC + (x % 3) * R::BYTES;
+            const int slot = opaque_uniform(x & 1);
+            unsigned char* rec = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
             const floatx4 aq = build_aq(slot, 1, tile(slot, 3, lane), m, g);
             // Aqk block 1 = [Aqk10 | Aqk11] (Aqk10: all keys before the query)
@@ -764,13 +777,13 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         auto compute = [&](int x, const VIn& vin) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
             (void)lr; (void)lg;
-            const unsigned char* buf = lds + L::REC + (x % 3) * R::BYTES;
+            const unsigned char* buf = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             const int64_t ct0 = chunk_t0(x);
             const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
             const bool outs = x >= out_from;
             // 1/||k|| of the lane's tokens 16 bb + 4 lg + i (the record holds the
             // raw keys and queries; phase B wrote these for the chunk)
-            const float* invn = reinterpret_cast<const float*>(lds + L::INVN) + (x % 3) * 64;
+            const float* invn = reinterpret_cast<const float*>(lds + L::INVN) + opaque_uniform(x % 3) * 64;
             const floatx4 ikt[2] = {*reinterpret_cast<const floatx4*>(invn + 4 * lg),
                                     *reinterpret_cast<const floatx4*>(invn + 16 + 4 * lg)};
             bf16x8 sb[CT][KS];
@@ -849,7 +862,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             // B's fp32 tiles (the same in every compute wave), Tb11 from the record
             bf16xEL tb1 = *reinterpret_cast<const bf16xEL*>(buf + R::TB + (64 + lane) * (2 * EL));
             {
-                const float* cpl = reinterpret_cast<const float*>(lds + L::CPL) + (x & 1) * 512;
+                const float* cpl = reinterpret_cast<const float*>(lds + L::CPL) + opaque_uniform(x & 1) * 512;
                 floatx4 tb00d;  // Tb00[4g + i][m]
 #pragma unroll
                 for (int i = 0; i < 4; ++i) tb00d[i] = cpl[16 * (4 * lg + i) + lr];
