@@ -889,11 +889,13 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     uc[ct][i] = (bf16)(U[ct][0][i] * ikt[0][i]);
                     uc[ct][4 + i] = (bf16)(U[ct][1][i] * ikt[1][i]);
                 }
-            // S = Diag(Gam_C) S + KdT U'
+            // S = Diag(Gam_C) S + KdT U'.  Unit t * 64 + lane of KdT sits at
+            // st_unit(t * 64 + lane) = t * 64 + (lane ^ g): one lane offset,
+            // the tile's as an instruction immediate
+            const unsigned char* kdtl = buf + R::KDT + (lane ^ lg) * 16;
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
-                const bf16xEL kdt = *reinterpret_cast<const bf16xEL*>(
-                    buf + R::KDT + st_unit(t * 64 + lane) * 16);
+                const bf16xEL kdt = *reinterpret_cast<const bf16xEL*>(kdtl + t * 1024);
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) S[ct][t] = mfma_tok(kdt, uc[ct], S[ct][t]);
             }
@@ -906,11 +908,13 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                 for (int ct = 0; ct < CT; ++ct) OT[ct][ob] = mfma_tok(uc[ct], aqk, OT[ct][ob]);
             }
             // OT[ct][ob][i] = O[token 16 ob + lr][column of tile ct, tile row 4 lg + i]
-            uint16_t* obase = a.o + ct0 * vstride + (int64_t)h * V;
+            // (a wave-uniform base and 32-bit lane offsets, as for the loads)
+            char* obase = reinterpret_cast<char*>(a.o + ct0 * vstride + (int64_t)h * V);
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob) {
                 if (16 * ob + lr >= nvalid) continue;
-                uint16_t* op = obase + (16 * ob + lr) * a.H * V;
+                uint16_t* op = reinterpret_cast<uint16_t*>(
+                    obase + (uint32_t)(16 * ob + lr) * (uint32_t)(a.H * V) * 2u);
                 const float so = a.scale * invn[32 + 16 * ob + lr];  // scale / ||q||
                 if constexpr (CT == 2) {
                     // tile ct row 4 lg + i is column wcol + 2 (4 lg + i) + ct: the
