@@ -642,9 +642,16 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;  // row of this element; its column is m
                 const float br = bs[16 * b + r] * ikr[i] * ikm;
-                float dec = 1.f;
-                if constexpr (GDN) dec = r > m ? exp2_hw(gt[16 * b + r] - gt[16 * b + m]) : 0.f;
-                ad[i] = m < r ? br * pa[i] * dec : 0.f;
+                if constexpr (GDN) {
+                    // formed before the mask: used on one side of the select,
+                    // the decay's exp is otherwise sunk into a branch per
+                    // element, each waiting on its own LDS reads
+                    float v = br * pa[i] * exp2_hw(gt[16 * b + r] - gt[16 * b + m]);
+                    asm volatile("" : "+v"(v));
+                    ad[i] = m < r ? v : 0.f;
+                } else {
+                    ad[i] = m < r ? br * pa[i] : 0.f;
+                }
                 am[16 * r + m] = ad[i];
             }
         };
