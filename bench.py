@@ -55,6 +55,9 @@ def source_digest(names=None) -> str:
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(p.name.encode())
         h.update(" ".join(text.split()).encode())
+        if p.suffix == ".hip":  # and the flags it is compiled with
+            from chunked_gated_delta_kda_amd.build import source_flags
+            h.update(" ".join(source_flags(p.name)).encode())
     return h.hexdigest()[:16]
 
 
