@@ -35,11 +35,12 @@ VGPR_FORM = {"kda_api.hip", "kda_prep.hip", "kda_recur.hip", "kda_fused.hip", "k
              "kda_split.hip"}
 
 
-# Sources scheduled with the compiler's iterative ILP strategy: the
-# single-launch kernel's SIMDs are issue-bound with two waves each, and this
-# schedule measured 2-2.5% faster on every workload (same results, bit for
-# bit) than the default occupancy-driven one.
-ILP_SCHED = {"kda_fused.hip"}
+# Sources scheduled with the compiler's iterative ILP strategy instead of the
+# default occupancy-driven one (same results, bit for bit): the single-launch
+# kernel's SIMDs are issue-bound with two waves each, and it measured 2-2.5%
+# faster on every workload; the chunk-preparation kernel 3.6% faster.  On the
+# recurrence, split and gradient kernels it measured within the spread.
+ILP_SCHED = {"kda_fused.hip", "kda_prep.hip"}
 
 
 def source_flags(src: str) -> list:
