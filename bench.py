@@ -93,10 +93,11 @@ def design_bytes(w):
     return dict(kda_prep=mb["kda_prep"] + rec, kda_recur=mb["kda_recur"] + rec)
 
 
-def fused_design_bytes(w, seg_chunks, warm=2):
+def fused_design_bytes(w, seg_chunks, warm=1):
     """Bytes the single-launch kernel moves by its own design: the method's
     bytes plus the warm-up re-reads (q, k, g, beta, v of `warm` chunks before
-    every segment that starts inside its sequence).  Fixed-length batches only
+    every segment that starts inside its sequence; one when the first
+    attempt's bound holds).  Fixed-length batches only
     (seg_chunks: the segment length the launch uses)."""
     mb = method_bytes(w)
     nc = (w.T + C - 1) // C

@@ -322,13 +322,16 @@ int run(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, hipStream_t strea
 // shorter than FUSED_MIN_CHUNKS; a request < 0 keeps whole sequences, > 0
 // sets L.  A segment that starts mid-sequence warms up over FUSED_WARM_CHUNKS
 // chunks from a zero state, exact to 2^FUSED_BOUND_LIMIT of the entering
-// state or else restarted from the sequence start (see kda_fused.hip).
+// state (fp32 rounding of the state), else over FUSED_WARM_RETRY chunks, else
+// it restarts from the sequence start (see kda_fused.hip).  A failed attempt
+// costs only its warm-up and pipeline-fill iterations.
 constexpr int32_t FUSED_MIN_CHUNKS = 8;
-constexpr int32_t FUSED_WARM_CHUNKS = 2;
+constexpr int32_t FUSED_WARM_CHUNKS = 1;
+constexpr int32_t FUSED_WARM_RETRY = 4;
 // The plan targets MI355X's 256 compute units.  It is a constant, not a
 // device query, so that the workspace size is a pure function of the sizes.
 constexpr int64_t FUSED_CUS = 256;
-constexpr float FUSED_BOUND_LIMIT = -40.f;
+constexpr float FUSED_BOUND_LIMIT = -24.f;
 
 struct FusedPlan {
     int32_t L;             // chunks per segment
@@ -427,6 +430,7 @@ int run_fused(const Common& c, int32_t N, kda::FusedArgs f, bool gdn, hipStream_
     f.n_seqs = N;
     f.packed = c.varlen;
     f.warm_chunks = FUSED_WARM_CHUNKS;
+    f.warm_chunks_retry = FUSED_WARM_RETRY;
     f.bound_limit = FUSED_BOUND_LIMIT;
     f.tok_limit = (int64_t)c.B * c.T;
     int64_t groups;

@@ -42,10 +42,12 @@
 // transitions: for one token ||(I - b k^ k^T) Diag(a)||_2 <= max(1, |1 - b|)
 // max_c a_c (at most max_c a_c for 0 <= b <= 2), so the state entering the
 // segment reaches its first token scaled by at most 2^(the sum over the
-// warm-up's tokens of log2 of that factor).  Below 2^bound_limit (2^-40, far
-// under fp32 rounding of the state) the zero start is exact to that bound;
-// otherwise the segment restarts from the sequence start and its initial
-// state.  The FlashQLA summary (section "핵심 기능") describes switching on
+// warm-up's tokens of log2 of that factor).  Below 2^bound_limit (2^-24: the
+// fp32 rounding of the state) the zero start is exact to that bound.
+// Otherwise the segment tries again with a longer warm-up, and if that
+// fails too, from the sequence start and its initial state.  The bound is
+// known when the warm-up ends, so a failed attempt costs only its warm-up
+// and the pipeline's two fill iterations.  The FlashQLA summary (section "핵심 기능") describes switching on
 // intra-card parallelism when the gate's decay allows it; this is that test,
 // made per segment.
 #include <hip/hip_ext.h>
@@ -254,16 +256,18 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
     }
 
     float* const misc = reinterpret_cast<float*>(lds + L::MISC);
-    const int W = a.warm_chunks;
 
     // An attempt computes chunks x0 .. c1 - 1 of the sequence, with outputs
-    // from c0 on; attempt 0 starts W chunks early from a zero state (exact
-    // when that is the sequence start), attempt 1 (after a failed bound)
-    // from the sequence start and its initial state.
+    // from c0 on; attempts 0 and 1 (each after a failed bound) start
+    // warm_chunks and warm_chunks_retry chunks early from a zero state (exact
+    // when that is the sequence start), attempt 2 from the sequence start and
+    // its initial state.
+    constexpr int N_ATTEMPTS = 3;
     int x0 = 0, n_it = 0, out_from = 0;
     bool exact = true;
     auto begin_attempt = [&](int attempt) __attribute__((always_inline)) {
-        x0 = attempt == 0 ? max(0, c0 - W) : 0;  // first chunk computed
+        const int w = attempt == 0 ? a.warm_chunks : attempt == 1 ? a.warm_chunks_retry : c0;
+        x0 = max(0, c0 - w);                     // first chunk computed
         exact = x0 == 0;
         n_it = c1 - x0;                          // chunks computed
         out_from = c0 - x0;                      // first chunk (relative) with outputs
@@ -365,7 +369,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                 // the bound (used for warm-up chunks): max over this wave's
                 // channels of each token's log2 decay, from G before the prefix
                 // sums.  Unconditional: a branch around the scan keeps the compiler
-                // from fusing the scan's last DPP step (16 extra moves per chunk).
+                // from fusing the scan's last DPP step (16 extra moves per chunk);
+                // the reduction over the lane's row groups below is not.
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
                     rmax[b] = G[b][0];
@@ -379,17 +384,21 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(G[b][e]));
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 16, 64));
-                    rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 32, 64));
-                }
             }
             issue_loads();
-            if (x < out_from && g == 0) {
-                float* rm = reinterpret_cast<float*>(lds + L::RMAX) + (slot * NPW + p) * 32;
-                rm[m] = rmax[0];
-                rm[16 + m] = rmax[1];
+            if (x < out_from) {  // only warm-up chunks need the bound
+                if constexpr (!GDN) {
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 16, 64));
+                        rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 32, 64));
+                    }
+                }
+                if (g == 0) {
+                    float* rm = reinterpret_cast<float*>(lds + L::RMAX) + (slot * NPW + p) * 32;
+                    rm[m] = rmax[0];
+                    rm[16 + m] = rmax[1];
+                }
             }
             // per-channel block decays 2^(block total): ef0 (block 0), ef1 (block 1)
             float ef0[8], ef1[8];
@@ -576,6 +585,19 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             const char* vb = reinterpret_cast<const char*>(a.v + ct0 * vstride + (int64_t)h * V);
             const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
             const uint32_t rstride = (uint32_t)a.H * V;
+            if (nvalid == C) {
+                // a whole chunk: one lane offset, the rows' bases wave-uniform
+                const uint32_t off = ((uint32_t)(4 * lg) * rstride + (uint32_t)col_of(0, lr)) * 2u;
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const char* rb = vb + (size_t)((16 * bb + i) * rstride) * 2u;
+                        if constexpr (CT == 2) d.w[bb][i] = *reinterpret_cast<const uint32_t*>(rb + off);
+                        else d.w[bb][i] = *reinterpret_cast<const uint16_t*>(rb + off);
+                    }
+                return;
+            }
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -943,25 +965,27 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         };
 
     // ------------------------------------------------------- the iterations
-    // Iteration it (from -2): compute chunk it, phase B chunk it+1 and the
-    // loads of v for chunk it+2; the loads of q, k, g and beta for chunk it+4
-    // (chunks 0 and 1 before the loop) and phase A of chunk it+2.  Each role
-    // runs its own
-    // copy of the loop (the same iterations and barriers), unrolled by three so
-    // that every register ring slot is a constant.
+    // Iteration it (from -2 to n_it - 1): compute chunk it, phase B chunk it+1
+    // and the loads of v for chunk it+2; the loads of q, k, g and beta for
+    // chunk it+4 (chunks 0 and 1 before the loop) and phase A of chunk it+2.
+    // Each role runs its own copy of the loop (the same iterations and
+    // barriers), unrolled by three so that every register ring slot is a
+    // constant; both leave it after iteration n_it - 1.
     if (is_cw) {
-        for (int attempt = 0; attempt < 2; ++attempt) {
+        for (int attempt = 0; attempt < N_ATTEMPTS; ++attempt) {
             begin_attempt(attempt);
             load_state(exact);
             if (tid == 0) misc[0] = 0.f;  // sum of the warm-up chunks' bounds
             if (n_it <= 0) break;
             const int n_iter = (n_it + 2 + 2) / 3 * 3;
             VIn vin[3];
-            bool restart = false;
-            for (int k3 = 0; k3 < n_iter && !restart; k3 += 3) {
+            bool restart = false, done = false;
+            for (int k3 = 0; k3 < n_iter && !restart && !done; k3 += 3) {
                 static_for<0, 3>([&](auto u) __attribute__((always_inline)) {
-                    if (restart) return;
+                    if (restart || done) return;
                     const int it = k3 + u - 2;
+                    done = it >= n_it;  // the unrolled tail: no work, no barrier
+                    if (done) return;
                     if (failed_bound(it)) {
                         restart = true;
                         return;
@@ -999,7 +1023,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                         fp[tile_channel(t, 4 * lg + i) * V + col_of(ct, lr)] = S[ct][t][i];
         }
     } else {
-        for (int attempt = 0; attempt < 2; ++attempt) {
+        for (int attempt = 0; attempt < N_ATTEMPTS; ++attempt) {
             begin_attempt(attempt);
             if (n_it <= 0) break;
             const int n_iter = (n_it + 2 + 2) / 3 * 3;
@@ -1009,11 +1033,13 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             PIn pin[3];
             load_in(pin[0], 0);
             load_in(pin[1], min(1, n_it - 1));
-            bool restart = false;
-            for (int k3 = 0; k3 < n_iter && !restart; k3 += 3) {
+            bool restart = false, done = false;
+            for (int k3 = 0; k3 < n_iter && !restart && !done; k3 += 3) {
                 static_for<0, 3>([&](auto u) __attribute__((always_inline)) {
-                    if (restart) return;
+                    if (restart || done) return;
                     const int it = k3 + u - 2;
+                    done = it >= n_it;  // as in the compute waves' loop
+                    if (done) return;
                     if (failed_bound(it)) {
                         restart = true;
                         return;

@@ -136,6 +136,7 @@ struct FusedArgs {
     const int32_t* final_map;   // packed: [n_segs] sequence whose final state a segment ends
     const int32_t* order;       // packed: [n_segs] segment of each dispatch rank (or null)
     int32_t warm_chunks;        // warm-up chunks before a segment that starts mid-sequence
+    int32_t warm_chunks_retry;  // the second attempt's warm-up (after a failed bound)
     float bound_limit;          // log2: a warm-up whose transitions are below this suffices
     int64_t tok_limit;          // tokens in the batch
 };

@@ -26,7 +26,7 @@ namespace kda {
 namespace {
 
 constexpr int SEG_ORDER_BUCKETS = 1024;  // segment lengths (chunk steps) told apart
-constexpr int SEG_WARM_CHUNKS = 2;       // the fused pass's warm-up (kda_api.hip)
+constexpr int SEG_WARM_CHUNKS = 1;       // the fused pass's first warm-up (kda_api.hip)
 
 __device__ __forceinline__ int32_t block_scan_add(int32_t v, int32_t* buf) {
     const int tid = threadIdx.x;

@@ -98,11 +98,12 @@ size_t kda_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_
  * kernel; here they are wave roles of one workgroup.  When the (sequence,
  * head) pairs are fewer than the compute units, sequences are cut into
  * segments that run in parallel; a segment that starts mid-sequence begins
- * two chunks early from a zero state and keeps that start only if those
- * chunks' transitions provably scale the true entering state by less than
- * 2^-40 (for one token ||(I - b k^ k^T) Diag(a)||_2 <= max_c a_c), else it
- * restarts from the sequence start: the result is the unsplit one up to
- * rounding and that bound.  The FlashQLA summary (section "핵심 기능")
+ * one chunk early from a zero state and keeps that start only if that
+ * chunk's transitions provably scale the true entering state by less than
+ * 2^-24, the fp32 rounding of the state (for one token
+ * ||(I - b k^ k^T) Diag(a)||_2 <= max_c a_c); else it tries four chunks
+ * early, and else it restarts from the sequence start: the result is the
+ * unsplit one up to rounding and that bound.  The FlashQLA summary (section "핵심 기능")
  * describes intra-card parallelism switched on when the gate's decay allows
  * it.  o must be 16-byte aligned. */
 int kda_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,

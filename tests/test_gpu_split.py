@@ -6,14 +6,15 @@ paths:
     transition whose bound shows it negligible is skipped and the first pass
     then runs only the decay window;
   fused (kda_fwd_segmented / gdn_fwd_segmented and the automatic choice of
-    kda_fwd): a segment starts two chunks early from a zero state and keeps
-    that start only if the bound of those two chunks is below 2^-40, else it
-    restarts from the sequence start.
+    kda_fwd): a segment starts one chunk early from a zero state and keeps
+    that start only if the bound of that chunk's transitions is below 2^-24;
+    else it tries four chunks early, and else it restarts from the sequence
+    start.
 
-The cases cover the regimes of both bounds: state forgotten within a few
-chunks (default decay), within part of a segment, kept across segments (slow
-decay: the staged scan applies transitions, the fused segments restart) and
-no decay at all."""
+The cases cover the regimes of both bounds: state forgotten within one chunk
+(default decay), within four (the fused segments' second attempt holds),
+within part of a segment, kept across segments (slow decay: the staged scan
+applies transitions, the fused segments restart) and no decay at all."""
 import numpy as np
 import pytest
 import torch
@@ -31,6 +32,12 @@ CASES = [
     ("default decay: transitions negligible",
      lambda: inputs.kda_workload(2, 3000, 2, 128, 128, seed=6100, init_std=0.05,
                                  name="split_fast"), 16),
+    ("faster decay: one warm-up chunk too short, four enough",
+     lambda: inputs.kda_workload(1, 3000, 2, 128, 128, seed=6160, dt_bias_value=-1.0,
+                                 init_std=0.05, name="split_retry"), 16),
+    ("GDN: one warm-up chunk too short, four enough",
+     lambda: inputs.gdn_workload(1, 3000, 2, 128, 128, seed=6510, init_std=0.05,
+                                 decay_shift=-1.5, name="split_gdn_retry"), 16),
     ("medium decay: decay window shorter than the segment",
      lambda: inputs.kda_workload(1, 3000, 2, 128, 128, seed=6150, dt_bias_value=-2.0,
                                  init_std=0.05, name="split_medium"), 16),
@@ -96,10 +103,10 @@ def test_split_deterministic(path):
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
-@pytest.mark.parametrize("seg", [1, 2, 3, 5])
+@pytest.mark.parametrize("seg", [1, 2, 3, 4, 5])
 def test_fused_segments_short_and_warm_up(seg):
-    """Fused segments shorter than, equal to and longer than the two warm-up
-    chunks, on a ragged packed batch, default decay (the zero start is kept)
+    """Fused segments shorter than, equal to and longer than the warm-up
+    chunks of either attempt, on a ragged packed batch, default decay (the zero start is kept)
     and GDN; every segment's outputs and the final states checked."""
     lengths = [0, 31, 32, 33, 200, 7, 513, 96]
     w = inputs.kda_workload(1, 0, 3, 128, 128, seed=6900 + seg, init_std=0.05,
