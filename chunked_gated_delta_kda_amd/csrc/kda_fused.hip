@@ -76,8 +76,7 @@ struct FusedLayout {
     static constexpr int RMAX = NRM + 2 * NPW * 64 * 4;             // [2][NPW][32] float
     static constexpr int BETA = RMAX + 2 * NPW * 32 * 4;            // [2][32] float
     static constexpr int GTOK = BETA + 2 * 32 * 4;                  // [2][32] float
-    static constexpr int TOT = GTOK + 2 * 32 * 4;                   // [NPW][64] float
-    static constexpr int AMAT = TOT + NPW * 64 * 4;                 // [2][256] float
+    static constexpr int AMAT = GTOK + 2 * 32 * 4;                  // [2][256] float
     // [2][2][256] float: per chunk (slot x & 1) Tb00 row-major and
     // (T11 A10)^T in D layout, from phase B for the coupling block the
     // compute waves form
@@ -227,13 +226,25 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4;
         if (exact && a.initial_state) {  // uniform: every load issued before the first wait
             const float* sp = a.initial_state + ((int64_t)n * a.H + h) * K * V;
+            if constexpr (CT == 2) {
+                // the two tiles' columns 2 lr and 2 lr + 1 are adjacent: one
+                // 8-byte load per (tile row, channel)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+                for (int t = 0; t < KT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float2 v = *reinterpret_cast<const float2*>(
+                            sp + tile_channel(t, 4 * lg + i) * V + col_of(0, lr));
+                        S[0][t][i] = v.x;
+                        S[1][t][i] = v.y;
+                    }
+            } else {
 #pragma unroll
                 for (int t = 0; t < KT; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        S[ct][t][i] = sp[tile_channel(t, 4 * lg + i) * V + col_of(ct, lr)];
+                        S[0][t][i] = sp[tile_channel(t, 4 * lg + i) * V + col_of(0, lr)];
+            }
         } else {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
@@ -402,7 +413,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             }
             // per-channel block decays 2^(block total): ef0 (block 0), ef1 (block 1)
             float ef0[8], ef1[8];
-            float* tot = reinterpret_cast<float*>(lds + L::TOT) + p * 64;
+            float glk[2][8];  // KDA: 2^G, the decay from the block start
+            (void)glk;
             if constexpr (GDN) {
                 const float t0 = row_last(Gs[0]), t1 = row_last(Gs[1]);
                 const float e0 = exp2_hw(t0), e1 = exp2_hw(t1);
@@ -412,29 +424,16 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     ef1[e] = e1;
                 }
             } else {
-                if (m == 15) {
+                // the block totals' decays are 2^G of the block's last row
+                // (padding rows add nothing): broadcast from lane 15 of the row
 #pragma unroll
-                    for (int b = 0; b < 2; ++b) {
-                        *reinterpret_cast<floatx4*>(tot + 32 * b + 8 * g) =
-                            floatx4{G[b][0], G[b][1], G[b][2], G[b][3]};
-                        *reinterpret_cast<floatx4*>(tot + 32 * b + 8 * g + 4) =
-                            floatx4{G[b][4], G[b][5], G[b][6], G[b][7]};
-                    }
-                }
-                wave_lds_sync();
-                const float e = exp2_hw(tot[lane]);  // one (block, channel) per lane
-                wave_lds_sync();
-                tot[lane] = e;
-                wave_lds_sync();
+                for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const floatx4 v0 = *reinterpret_cast<const floatx4*>(tot + 8 * g + 4 * hh);
-                    const floatx4 v1 = *reinterpret_cast<const floatx4*>(tot + 32 + 8 * g + 4 * hh);
+                    for (int e = 0; e < 8; ++e) glk[b][e] = exp2_hw(G[b][e]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        ef0[4 * hh + i] = v0[i];
-                        ef1[4 * hh + i] = v1[i];
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    ef0[e] = row_last(glk[0][e]);
+                    ef1[e] = row_last(glk[1][e]);
                 }
             }
             // Gamma_C of this wave's channels, tile order (channel 32p + 8g + e is
@@ -484,7 +483,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                         kil[e] = kn[e];
                         kdl[e] = kn[e] * gend_tok;
                     } else {
-                        gl = exp2_hw(G[b][e]);
+                        gl = glk[b][e];
                         kil[e] = kn[e] * exp2_hw(-G[b][e]);
                         kdl[e] = kil[e] * (b == 0 ? ef0[e] : ef1[e]);
                     }
@@ -967,7 +966,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
     // ------------------------------------------------------- the iterations
     // Iteration it (from -2 to n_it - 1): compute chunk it, phase B chunk it+1
     // and the loads of v for chunk it+2; the loads of q, k, g and beta for
-    // chunk it+4 (chunks 0 and 1 before the loop) and phase A of chunk it+2.
+    // chunk it+3 (chunk 0 before the loop) and phase A of chunk it+2.
     // Each role runs its own copy of the loop (the same iterations and
     // barriers), unrolled by three so that every register ring slot is a
     // constant; both leave it after iteration n_it - 1.
@@ -1015,12 +1014,13 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4;
             float* fp = a.final_state + ((int64_t)fslot * a.H + h) * K * V;
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+            for (int t = 0; t < KT; ++t)
 #pragma unroll
-                for (int t = 0; t < KT; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        fp[tile_channel(t, 4 * lg + i) * V + col_of(ct, lr)] = S[ct][t][i];
+                for (int i = 0; i < 4; ++i) {
+                    float* rp = fp + tile_channel(t, 4 * lg + i) * V + col_of(0, lr);
+                    if constexpr (CT == 2) *reinterpret_cast<float2*>(rp) = float2{S[0][t][i], S[1][t][i]};
+                    else *rp = S[0][t][i];
+                }
         }
     } else {
         for (int attempt = 0; attempt < N_ATTEMPTS; ++attempt) {
@@ -1032,7 +1032,6 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             __builtin_amdgcn_s_waitcnt(VMCNT_0);
             PIn pin[3];
             load_in(pin[0], 0);
-            load_in(pin[1], min(1, n_it - 1));
             bool restart = false, done = false;
             for (int k3 = 0; k3 < n_iter && !restart && !done; k3 += 3) {
                 static_for<0, 3>([&](auto u) __attribute__((always_inline)) {
@@ -1044,11 +1043,14 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                         restart = true;
                         return;
                     }
-                    constexpr int sa = u, sl = (u + 2) % 3;  // ring slot of chunk y: y mod 3
-                    // two chunks ahead: the loads have two iterations to land
+                    constexpr int sa = u, sl = (u + 1) % 3;  // ring slot of chunk y: y mod 3
+                    // one chunk ahead: the loads have the rest of this phase A
+                    // and the barrier to land (two ahead measured no faster in
+                    // the steady state, and the first iteration then waited on
+                    // a burst of both chunks from every workgroup at once);
                     // unconditional (see load_v)
                     auto loads = [&]() __attribute__((always_inline)) {
-                        load_in(pin[sl], min(it + 4, n_it - 1));
+                        load_in(pin[sl], min(it + 3, n_it - 1));
                     };
                     if (it + 2 < n_it) {
                         phase_a(pin[sa], it + 2, loads);
