@@ -213,7 +213,6 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
     const int p = wave - NCW;  // prep wave index (>= 0 for prep waves)
 
     // ---------------------------------------------------- compute-wave state
-    const int64_t vstride = (int64_t)a.H * V;
     floatx4 S[CT][KT];
     // column of tile ct, lane lr: with two tiles per wave, tile ct holds the
     // columns of parity ct, so a lane's pair (2 lr, 2 lr + 1) is contiguous
@@ -276,12 +275,20 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
     constexpr int N_ATTEMPTS = 3;
     int x0 = 0, n_it = 0, out_from = 0;
     bool exact = true;
+    // the attempt's first (token, head) row and its tokens up to the sequence
+    // end: per chunk, a 32-bit token offset from there (the batch holds fewer
+    // than 2^31 tokens)
+    int64_t row0 = 0;
+    int seg_len = 0;
     auto begin_attempt = [&](int attempt) __attribute__((always_inline)) {
         const int w = attempt == 0 ? a.warm_chunks : attempt == 1 ? a.warm_chunks_retry : c0;
         x0 = max(0, c0 - w);                     // first chunk computed
         exact = x0 == 0;
         n_it = c1 - x0;                          // chunks computed
         out_from = c0 - x0;                      // first chunk (relative) with outputs
+        const int64_t t0 = tseq0 + (int64_t)C * x0;
+        row0 = t0 * a.H + h;
+        seg_len = (int)(tseq1 - t0);
     };
     // the warm-up chunks' bound is complete at iteration out_from (phase B of
     // the last one ran an iteration earlier); every wave reads the same value
@@ -293,20 +300,24 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
     };
 
         // ---------------------------------------------------------- prep waves
-        // chunk x (relative to x0): its first token
-        auto chunk_t0 = [&](int x) __attribute__((always_inline)) { return tseq0 + (int64_t)C * (x0 + x); };
+        // chunk x (relative to x0): its valid tokens, and the byte offset of its
+        // first row from the attempt's first row, for rows of `row_bytes`
+        auto nvalid_of = [&](int x) __attribute__((always_inline)) { return min(C, seg_len - C * x); };
+        auto chunk_off = [&](int x, uint32_t row_bytes) __attribute__((always_inline)) {
+            return (uint64_t)(uint32_t)(C * x * a.H) * row_bytes;
+        };
         auto load_in = [&](PIn& d, int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
             (void)lr; (void)lg;
-            const int64_t ct0 = chunk_t0(x);
-            const int64_t r0 = ct0 * a.H + h;  // the chunk's first (token, head) row
             // uniform bases and 32-bit lane byte offsets (one address add per load)
-            const char* qb = reinterpret_cast<const char*>(a.q + r0 * K);
-            const char* kb = reinterpret_cast<const char*>(a.k + r0 * K);
-            const char* gb = GDN ? nullptr : reinterpret_cast<const char*>(a.g_kda + r0 * K);
-            const char* gdb = GDN ? reinterpret_cast<const char*>(a.g_gdn + r0) : nullptr;
-            const char* bt = reinterpret_cast<const char*>(a.beta + r0);
-            const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
+            const uint64_t ok = chunk_off(x, 2u * K), o2 = chunk_off(x, 2u), o4 = chunk_off(x, 4u);
+            const char* qb = reinterpret_cast<const char*>(a.q + row0 * K) + ok;
+            const char* kb = reinterpret_cast<const char*>(a.k + row0 * K) + ok;
+            const char* gb = GDN ? nullptr : reinterpret_cast<const char*>(a.g_kda + row0 * K) + ok;
+            const char* gdb = GDN ? reinterpret_cast<const char*>(a.g_gdn + row0) + o4 : nullptr;
+            const char* bt = reinterpret_cast<const char*>(a.beta + row0) + o2;
+            (void)o4;
+            const int nvalid = nvalid_of(x);
             const uint32_t cb = 32 * p + 8 * g;
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
@@ -328,8 +339,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             (void)lr; (void)lg;
             const int slot = opaque_uniform(x & 1);
             unsigned char* rec = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
-            const int64_t ct0 = chunk_t0(x);
-            const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
+            const int nvalid = nvalid_of(x);
             float vmask[2], bsig[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
@@ -580,9 +590,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         auto load_v = [&](VIn& d, int x) __attribute__((always_inline)) {
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
             (void)lr; (void)lg;
-            const int64_t ct0 = chunk_t0(x);
-            const char* vb = reinterpret_cast<const char*>(a.v + ct0 * vstride + (int64_t)h * V);
-            const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
+            const char* vb = reinterpret_cast<const char*>(a.v + row0 * V) + chunk_off(x, 2u * V);
+            const int nvalid = nvalid_of(x);
             const uint32_t rstride = (uint32_t)a.H * V;
             if (nvalid == C) {
                 // a whole chunk: one lane offset, the rows' bases wave-uniform
@@ -712,7 +721,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             unsigned char* rec = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
             float* am = reinterpret_cast<float*>(lds + L::AMAT);
-            const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
+            const int nvalid = nvalid_of(x);
             const floatx4 ikr = row_norms(slot, 0, nvalid, g);
             const float ikm = token_norm(slot, m, nvalid);
             const floatx4 pa = tile(slot, 0, lane);
@@ -735,7 +744,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             unsigned char* rec = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             const float* bs = reinterpret_cast<const float*>(lds + L::BETA) + slot * 32;
             float* am = reinterpret_cast<float*>(lds + L::AMAT) + 256;
-            const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
+            const int nvalid = nvalid_of(x);
             const floatx4 ikr = row_norms(slot, 1, nvalid, g);
             const float ikm1 = token_norm(slot, 16 + m, nvalid), ikm0 = token_norm(slot, m, nvalid);
             const floatx4 pa = tile(slot, 1, lane), p4 = tile(slot, 4, lane);
@@ -770,7 +779,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                 float v = nr[lane];
 #pragma unroll
                 for (int pp = 1; pp < NPW; ++pp) v += nr[pp * 64 + lane];
-                const int nvalid = (int)min((int64_t)C, tseq1 - chunk_t0(x));
+                const int nvalid = nvalid_of(x);
                 invn[lane] = (lane & 31) < nvalid ? rsq_hw(v + NORM_EPS) : 0.f;
             }
             const floatx4 aq = build_aq(slot, 0, tile(slot, 2, lane), m, g);
@@ -806,8 +815,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
             (void)lr; (void)lg;
             const unsigned char* buf = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
-            const int64_t ct0 = chunk_t0(x);
-            const int nvalid = (int)min((int64_t)C, tseq1 - ct0);
+            const int nvalid = nvalid_of(x);
             const bool outs = x >= out_from;
             // 1/||k|| of the lane's tokens 16 bb + 4 lg + i (the record holds the
             // raw keys and queries; phase B wrote these for the chunk)
@@ -937,7 +945,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             }
             // OT[ct][ob][i] = O[token 16 ob + lr][column of tile ct, tile row 4 lg + i]
             // (a wave-uniform base and 32-bit lane offsets, as for the loads)
-            char* obase = reinterpret_cast<char*>(a.o + ct0 * vstride + (int64_t)h * V);
+            char* obase = reinterpret_cast<char*>(a.o + row0 * V) + chunk_off(x, 2u * V);
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob) {
                 if (16 * ob + lr >= nvalid) continue;
