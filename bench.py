@@ -8,7 +8,8 @@ q/k/v/g/beta, fp32 initial and final states (seeded synthetic inputs,
 chunked_gated_delta_kda_amd.inputs.config(1)).  One step = one full forward
 pass over one batch whose inputs are already resident in HBM.  Several input
 sets are rotated so that no step finds its inputs in the 256 MB last-level
-cache.  Prints one JSON line.
+cache.  The default 500 untimed warm-up steps give the GPU's clock time to
+ramp up before the timed steps.  Prints one JSON line.
 
 Roofline: the method's compulsory bytes (inputs read once, outputs and states
 written once: 6K + 4V + 2 bytes per token-head for KDA, plus the states) over
@@ -525,8 +526,10 @@ def bench_fwd(args, torch, kda, inputs, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first: about 30 ms of work at the default workload, "
+                         "so that the GPU's clock has ramped up (5 steps measured 15%% slower)")
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
