@@ -122,7 +122,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // The lane index as a value the compiler cannot see through: per-lane
 // address arithmetic derived from it is recomputed inside each phase instead
 // of hoisted out of the iteration loop and held in registers for its whole
-// length (which spills).
+// length.  The compute waves use it (hoisting there took them from 222 to
+// 237 VGPRs and measured 3-5% slower); the prep waves, well below the
+// kernel's register count, use the plain lane index and keep those values.
 __device__ __forceinline__ int opaque_lane() {
     int l = (int)(threadIdx.x & 63);
     asm volatile("" : "+v"(l));
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             return (uint64_t)(uint32_t)(C * x * a.H) * row_bytes;
         };
         auto load_in = [&](PIn& d, int x) __attribute__((always_inline)) {
-            const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
+            const int lane = (int)(threadIdx.x & 63), m = lane & 15, g = lane >> 4, lr = m, lg = g;
             (void)lr; (void)lg;
             // uniform bases and 32-bit lane byte offsets (one address add per load)
             const uint64_t ok = chunk_off(x, 2u * K), o2 = chunk_off(x, 2u), o4 = chunk_off(x, 4u);
@@ -335,23 +337,26 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
         // chunks' loads leave the wave after its first long run of arithmetic,
         // not at the barrier where every wave of the CU issues at once
         auto phase_a = [&](const PIn& d, int x, auto&& issue_loads) __attribute__((always_inline)) {
-            const int lane = opaque_lane(), m = lane & 15, g = lane >> 4, lr = m, lg = g;
+            const int lane = (int)(threadIdx.x & 63), m = lane & 15, g = lane >> 4, lr = m, lg = g;
             (void)lr; (void)lg;
             const int slot = opaque_uniform(x & 1);
             unsigned char* rec = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             const int nvalid = nvalid_of(x);
-            float vmask[2], bsig[2];
+            float vmask[2];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const bool valid = 16 * b + m < nvalid;
-                vmask[b] = valid ? 1.f : 0.f;
-                const float braw = __uint_as_float((uint32_t)d.braw[b] << 16);
-                bsig[b] = valid ? (GDN ? braw : sigmoid_f(braw)) : 0.f;
-            }
-            if (p == 0 && g == 0) {
-                float* bs = reinterpret_cast<float*>(lds + L::BETA) + slot * 32;
-                bs[m] = bsig[0];
-                bs[16 + m] = bsig[1];
+            for (int b = 0; b < 2; ++b) vmask[b] = 16 * b + m < nvalid ? 1.f : 0.f;
+            if (p == 0) {  // beta of the chunk's tokens (one prep wave)
+                float bsig[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const float braw = __uint_as_float((uint32_t)d.braw[b] << 16);
+                    bsig[b] = vmask[b] > 0.f ? (GDN ? braw : sigmoid_f(braw)) : 0.f;
+                }
+                if (g == 0) {
+                    float* bs = reinterpret_cast<float*>(lds + L::BETA) + slot * 32;
+                    bs[m] = bsig[0];
+                    bs[16 + m] = bsig[1];
+                }
             }
             // log2 decays and their in-block prefix sums (padding rows add 0)
             float G[2][8], rmax[2];
@@ -509,12 +514,9 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                         kd[e] = kdl[e];
                     }
                 }
-                {  // -KG: the sign bits of the packed bf16 flipped (exact)
-                    u32x4 w = __builtin_bit_cast(u32x4, pack8(kg));
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) w[u] ^= 0x80008000u;
-                    *reinterpret_cast<u32x4*>(rec + R::NKG + ((b * KS + p) * 64 + lane) * 16) = w;
-                }
+                // KG itself in the record's nKG slot: the recurrence negates it in
+                // the FMA that adds V (a source modifier, no instruction)
+                *reinterpret_cast<bf16x8*>(rec + R::NKG + ((b * KS + p) * 64 + lane) * 16) = pack8(kg);
                 *reinterpret_cast<bf16x8*>(rec + R::QG + ((b * KS + p) * 64 + lane) * 16) = pack8(qg);
                 // KdT[t][g'][m'][e'] = Kd[tok(g', e')][rho(t, m')], 16-byte units
                 // swizzled by st_unit.  Channel 32p + 8g + e is row 4g + (e & 3) of
@@ -832,8 +834,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                         sb[ct][j][e] = (bf16)S[ct][2 * j][e];
                         sb[ct][j][4 + e] = (bf16)S[ct][2 * j + 1][e];
                     }
-            // Y_b = V_b - KG_b S: the product with the raw keys, then per token
-            // V + (1/||k||) (-K G S)
+            // Y_b = V_b - KG_b S: the product with the raw keys (the record's
+            // nKG slot holds +KG in this pass), then per token V - (1/||k||) K G S
             const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
             floatx4 Y[CT][2];
 #pragma unroll
@@ -844,18 +846,18 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             for (int j = 0; j < KS; ++j)
 #pragma unroll
                 for (int bb = 0; bb < 2; ++bb) {
-                    const bf16x8 nkg = *reinterpret_cast<const bf16x8*>(
+                    const bf16x8 kgo = *reinterpret_cast<const bf16x8*>(
                         buf + R::NKG + ((bb * KS + j) * 64 + lane) * 16);
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) Y[ct][bb] = mfma32(nkg, sb[ct][j], Y[ct][bb]);
+                    for (int ct = 0; ct < CT; ++ct) Y[ct][bb] = mfma32(kgo, sb[ct][j], Y[ct][bb]);
                 }
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t w = vin.w[bb][i];
-                    Y[0][bb][i] = fmaf(ikt[bb][i], Y[0][bb][i], bf_lo(w));
-                    if constexpr (CT == 2) Y[1][bb][i] = fmaf(ikt[bb][i], Y[1][bb][i], bf_hi(w));
+                    Y[0][bb][i] = fmaf(-ikt[bb][i], Y[0][bb][i], bf_lo(w));
+                    if constexpr (CT == 2) Y[1][bb][i] = fmaf(-ikt[bb][i], Y[1][bb][i], bf_hi(w));
                 }
             // O^T = S^T QG^T (+ U'^T Aqk^T below), raw queries: scaled by
             // 1/||q|| at the store
