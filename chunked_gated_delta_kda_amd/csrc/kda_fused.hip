@@ -824,6 +824,21 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             const float* invn = reinterpret_cast<const float*>(lds + L::INVN) + opaque_uniform(x % 3) * 64;
             const floatx4 ikt[2] = {*reinterpret_cast<const floatx4*>(invn + 4 * lg),
                                     *reinterpret_cast<const floatx4*>(invn + 16 + 4 * lg)};
+            // (first: its fp32 MFMA chain depends on phase B's tiles only)
+            // Tb's block 1 = [Tb10 | Tb11]: Tb10 = -(T11 A10) Tb00 from phase
+            // B's fp32 tiles (the same in every compute wave), Tb11 from the record
+            bf16xEL tb1 = *reinterpret_cast<const bf16xEL*>(buf + R::TB + (64 + lane) * (2 * EL));
+            {
+                const float* cpl = reinterpret_cast<const float*>(lds + L::CPL) + opaque_uniform(x & 1) * 512;
+                floatx4 tb00d;  // Tb00[4g + i][m]
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tb00d[i] = cpl[16 * (4 * lg + i) + lr];
+                const floatx4 ta = *reinterpret_cast<const floatx4*>(cpl + 256 + 4 * lane);
+                // M(Tb00, (T11 A10)^T) = (T11 A10 Tb00)^T: element i is [m][4g + i]
+                const floatx4 c = mt(tb00d, ta);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tb1[i] = (bf16)(-c[i]);
+            }
             bf16x8 sb[CT][KS];
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
@@ -896,20 +911,6 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     yc[ct][i] = (bf16)Y[ct][0][i];
                     yc[ct][4 + i] = (bf16)Y[ct][1][i];
                 }
-            // Tb's block 1 = [Tb10 | Tb11]: Tb10 = -(T11 A10) Tb00 from phase
-            // B's fp32 tiles (the same in every compute wave), Tb11 from the record
-            bf16xEL tb1 = *reinterpret_cast<const bf16xEL*>(buf + R::TB + (64 + lane) * (2 * EL));
-            {
-                const float* cpl = reinterpret_cast<const float*>(lds + L::CPL) + opaque_uniform(x & 1) * 512;
-                floatx4 tb00d;  // Tb00[4g + i][m]
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tb00d[i] = cpl[16 * (4 * lg + i) + lr];
-                const floatx4 ta = *reinterpret_cast<const floatx4*>(cpl + 256 + 4 * lane);
-                // M(Tb00, (T11 A10)^T) = (T11 A10 Tb00)^T: element i is [m][4g + i]
-                const floatx4 c = mt(tb00d, ta);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tb1[i] = (bf16)(-c[i]);
-            }
             floatx4 U[CT][2];
             {
                 const bf16xEL tb0 = *reinterpret_cast<const bf16xEL*>(buf + R::TB + lane * (2 * EL));
