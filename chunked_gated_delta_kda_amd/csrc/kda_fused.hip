@@ -31,6 +31,16 @@
 //     the Aqk tiles and the decay bound.  The coupling block
 //     Tb10 = -(T11 A10) Tb00 is formed by every compute wave at its next
 //     step from fp32 tiles the two inverse parts left in LDS.
+//   phase-B waves (4, scalar gate only): the scalar gate's phase A is light
+//     and its compute waves, carrying phase B too, set the pace; with phase B
+//     on four waves of its own (same parts, same rotation) each SIMD runs
+//     three waves at up to 168 registers each.  To fit, the scalar gate's
+//     recurrence forms S's bf16 operand one 32-channel slice at a time and
+//     its prep waves issue each block's partial products as soon as that
+//     block's operands exist.  (The per-channel gate, whose prep waves are as
+//     long as its compute waves, measured 10% slower with the third wave: at
+//     168 registers its prep waves no longer keep their loads in flight
+//     across the decayed products.)
 // One barrier per iteration.  In iteration i the compute waves run chunk i,
 // phase B finishes chunk i+1 and phase A fills chunk i+2; three records are
 // live in LDS.
@@ -60,13 +70,16 @@ namespace kda {
 
 namespace {
 
-template <int K, int V>
+template <int K, int V, bool GDN>
 struct FusedLayout {
     using R = Rec<K>;
     static constexpr int NPW = K / 32;  // prep waves
     static constexpr int NCW = 4;       // compute waves
+    // phase-B waves: the scalar gate runs phase B on waves of its own (three
+    // waves per SIMD); the per-channel gate on the compute waves
+    static constexpr int NBW = GDN ? NCW : 0;
     static constexpr int CT = V / 64;   // 16-column state tiles per compute wave
-    static constexpr int NT = 64 * (NPW + NCW);
+    static constexpr int NT = 64 * (NPW + NCW + NBW);
     static constexpr int NBUF = 3;      // chunk records in LDS
     // byte offsets: the small tables and the partial products first, so that
     // every access to them is a lane offset plus an instruction immediate
@@ -163,10 +176,10 @@ __device__ __forceinline__ float row_last(float x) {
 }  // namespace
 
 template <int K, int V, bool GDN>
-__global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs a) {
-    using L = FusedLayout<K, V>;
+__global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kernel(FusedArgs a) {
+    using L = FusedLayout<K, V, GDN>;
     using R = Rec<K>;
-    constexpr int NPW = L::NPW, NCW = L::NCW, CT = L::CT;
+    constexpr int NPW = L::NPW, NCW = L::NCW, NBW = L::NBW, CT = L::CT;
     constexpr int KS = K / 32, KT = K / 16;
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::BYTES];
 
@@ -212,7 +225,8 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, m = lane & 15, g = lane >> 4;
     const bool is_cw = wave < NCW;
-    const int p = wave - NCW;  // prep wave index (>= 0 for prep waves)
+    const bool is_bw = NBW > 0 && wave >= NCW && wave < NCW + NBW;
+    const int p = wave - NCW - NBW;  // prep wave index (>= 0 for prep waves)
 
     // ---------------------------------------------------- compute-wave state
     floatx4 S[CT][KT];
@@ -260,7 +274,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
     float rate = 0.f, dt[8];
     if constexpr (!GDN) {
         rate = exp2_hw(a.A_log[h] * LOG2E);
-        if (!is_cw) {
+        if (p >= 0) {
             const float* dp = a.dt_bias + (int64_t)h * K + 32 * p + 8 * g;
 #pragma unroll
             for (int e = 0; e < 8; ++e) dt[e] = dp[e] * LOG2E;  // the gate works in log2 units
@@ -550,7 +564,34 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     kcp1 = kglf;
                     qcp1 = qglf;
                 }
+                // With phase-B waves (168 registers a wave) this block's
+                // partial products over the wave's 32 channels (D = X Y^T) and
+                // its rows' squared norms, as soon as its operands exist (the
+                // block's operands then die early); otherwise all at the end,
+                // below:
+                //   0: A00 (in-block K Ki^T)  1: A11  2: Aqk00^T (Ki Q^T)  3: Aqk11^T
+                //   4: A10 (KG1 Kd0^T)        5: Aqk10^T (Kd0 QG1^T)
+                if constexpr (NBW > 0) {
+                    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+                    floatx4* part = reinterpret_cast<floatx4*>(lds + L::PART + slot * L::PART_SLOT) + p * 6 * 64;
+                    part[b * 64 + lane] = mfma32(ink[b], ini[b], zero);
+                    part[(2 + b) * 64 + lane] = mfma32(ini[b], inq[b], zero);
+                    if (b == 1) {
+                        part[4 * 64 + lane] = mfma32(kcp1, kd0f, zero);
+                        part[5 * 64 + lane] = mfma32(kd0f, qcp1, zero);
+                    }
+                    // squared norms of the raw rows: diagonals of Q Q^T and K K^T
+                    float* nr = reinterpret_cast<float*>(lds + L::NRM) + (slot * NPW + p) * 64;
+                    const bf16x8 kr = __builtin_bit_cast(bf16x8, d.k[b]);
+                    const bf16x8 qr = __builtin_bit_cast(bf16x8, d.q[b]);
+                    const floatx4 dk = mfma32(kr, kr, zero), dq = mfma32(qr, qr, zero);
+                    if (g == (m >> 2)) {
+                        nr[16 * b + m] = pick(dk, m & 3);
+                        nr[32 + 16 * b + m] = pick(dq, m & 3);
+                    }
+                }
             }
+            if constexpr (NBW > 0) return;
             // partial products over this wave's 32 channels (D = X Y^T):
             //   0: A00 (in-block K Ki^T)  1: A11  2: Aqk00^T (Ki Q^T)  3: Aqk11^T
             //   4: A10 (KG1 Kd0^T)        5: Aqk10^T (Kd0 QG1^T)
@@ -839,58 +880,102 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) tb1[i] = (bf16)(-c[i]);
             }
-            bf16x8 sb[CT][KS];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int j = 0; j < KS; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        sb[ct][j][e] = (bf16)S[ct][2 * j][e];
-                        sb[ct][j][4 + e] = (bf16)S[ct][2 * j + 1][e];
-                    }
-            // Y_b = V_b - KG_b S: the product with the raw keys (the record's
-            // nKG slot holds +KG in this pass), then per token V - (1/||k||) K G S
+            // Y_b = V_b - KG_b S and O^T = S^T QG^T
             const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-            floatx4 Y[CT][2];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int bb = 0; bb < 2; ++bb) Y[ct][bb] = zero;
-#pragma unroll
-            for (int j = 0; j < KS; ++j)
-#pragma unroll
-                for (int bb = 0; bb < 2; ++bb) {
-                    const bf16x8 kgo = *reinterpret_cast<const bf16x8*>(
-                        buf + R::NKG + ((bb * KS + j) * 64 + lane) * 16);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) Y[ct][bb] = mfma32(kgo, sb[ct][j], Y[ct][bb]);
-                }
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t w = vin.w[bb][i];
-                    Y[0][bb][i] = fmaf(-ikt[bb][i], Y[0][bb][i], bf_lo(w));
-                    if constexpr (CT == 2) Y[1][bb][i] = fmaf(-ikt[bb][i], Y[1][bb][i], bf_hi(w));
-                }
-            // O^T = S^T QG^T (+ U'^T Aqk^T below), raw queries: scaled by
-            // 1/||q|| at the store
-            floatx4 OT[CT][2];
-            if (outs) {
+            floatx4 Y[CT][2], OT[CT][2];
+            if constexpr (NBW > 0) {
+                // with phase-B waves (168 registers a wave): one 32-channel slice
+                // of S at a time, its bf16 operand formed just before its products
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                    for (int ob = 0; ob < 2; ++ob) OT[ct][ob] = zero;
+                    for (int bb = 0; bb < 2; ++bb) Y[ct][bb] = OT[ct][bb] = zero;
+#pragma unroll
+                for (int j = 0; j < KS; ++j) {
+                    bf16x8 sb[CT];
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            sb[ct][e] = (bf16)S[ct][2 * j][e];
+                            sb[ct][4 + e] = (bf16)S[ct][2 * j + 1][e];
+                        }
+#pragma unroll
+                    for (int bb = 0; bb < 2; ++bb) {
+                        const bf16x8 kgo = *reinterpret_cast<const bf16x8*>(
+                            buf + R::NKG + ((bb * KS + j) * 64 + lane) * 16);
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct) Y[ct][bb] = mfma32(kgo, sb[ct], Y[ct][bb]);
+                    }
+                    if (outs) {
+#pragma unroll
+                        for (int ob = 0; ob < 2; ++ob) {
+                            const bf16x8 qg = *reinterpret_cast<const bf16x8*>(
+                                buf + R::QG + ((ob * KS + j) * 64 + lane) * 16);
+#pragma unroll
+                            for (int ct = 0; ct < CT; ++ct) OT[ct][ob] = mfma32(sb[ct], qg, OT[ct][ob]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t w = vin.w[bb][i];
+                        Y[0][bb][i] = fmaf(-ikt[bb][i], Y[0][bb][i], bf_lo(w));
+                        if constexpr (CT == 2) Y[1][bb][i] = fmaf(-ikt[bb][i], Y[1][bb][i], bf_hi(w));
+                    }
+            } else {
+                bf16x8 sb[CT][KS];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < KS; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            sb[ct][j][e] = (bf16)S[ct][2 * j][e];
+                            sb[ct][j][4 + e] = (bf16)S[ct][2 * j + 1][e];
+                        }
+                // Y_b = V_b - KG_b S: the product with the raw keys (the record's
+                // nKG slot holds +KG in this pass), then per token V - (1/||k||) K G S
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int bb = 0; bb < 2; ++bb) Y[ct][bb] = zero;
 #pragma unroll
                 for (int j = 0; j < KS; ++j)
 #pragma unroll
-                    for (int ob = 0; ob < 2; ++ob) {
-                        const bf16x8 qg = *reinterpret_cast<const bf16x8*>(
-                            buf + R::QG + ((ob * KS + j) * 64 + lane) * 16);
+                    for (int bb = 0; bb < 2; ++bb) {
+                        const bf16x8 kgo = *reinterpret_cast<const bf16x8*>(
+                            buf + R::NKG + ((bb * KS + j) * 64 + lane) * 16);
 #pragma unroll
-                        for (int ct = 0; ct < CT; ++ct) OT[ct][ob] = mfma32(sb[ct][j], qg, OT[ct][ob]);
+                        for (int ct = 0; ct < CT; ++ct) Y[ct][bb] = mfma32(kgo, sb[ct][j], Y[ct][bb]);
                     }
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t w = vin.w[bb][i];
+                        Y[0][bb][i] = fmaf(-ikt[bb][i], Y[0][bb][i], bf_lo(w));
+                        if constexpr (CT == 2) Y[1][bb][i] = fmaf(-ikt[bb][i], Y[1][bb][i], bf_hi(w));
+                    }
+                // O^T = S^T QG^T (+ U'^T Aqk^T below), raw queries: scaled by
+                // 1/||q|| at the store
+                if (outs) {
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int ob = 0; ob < 2; ++ob) OT[ct][ob] = zero;
+#pragma unroll
+                    for (int j = 0; j < KS; ++j)
+#pragma unroll
+                        for (int ob = 0; ob < 2; ++ob) {
+                            const bf16x8 qg = *reinterpret_cast<const bf16x8*>(
+                                buf + R::QG + ((ob * KS + j) * 64 + lane) * 16);
+#pragma unroll
+                            for (int ct = 0; ct < CT; ++ct) OT[ct][ob] = mfma32(sb[ct][j], qg, OT[ct][ob]);
+                        }
+                }
             }
             // decay the state
 #pragma unroll
@@ -974,6 +1059,16 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
             }
         };
 
+    // phase B of chunk x, part (w - x) mod 4 on wave w of its role: parts 0
+    // and 1 (the substitutions) on SIMDs two apart
+    auto phase_b = [&](int w, int x) __attribute__((always_inline)) {
+        const int part = (w - x) & (NCW - 1);
+        if (part == 0) phase_p0(x);
+        else if (part == 2) phase_p1(x);
+        else if (part == 1) phase_p2(x);
+        else phase_p3(x);
+    };
+
     // ------------------------------------------------------- the iterations
     // Iteration it (from -2 to n_it - 1): compute chunk it, phase B chunk it+1
     // and the loads of v for chunk it+2; the loads of q, k, g and beta for
@@ -1006,14 +1101,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     // issued on some paths only makes the compiler's in-order
                     // wait counts cover the loads just issued as well
                     load_v(vin[sv], min(it + 2, n_it - 1));
-                    if (it + 1 >= 0 && it + 1 < n_it) {
-                        // parts 0 and 1 (the substitutions) on SIMDs two apart
-                        const int part = (wave - (it + 1)) & (NCW - 1);
-                        if (part == 0) phase_p0(it + 1);
-                        else if (part == 2) phase_p1(it + 1);
-                        else if (part == 1) phase_p2(it + 1);
-                        else phase_p3(it + 1);
-                    }
+                    if (NBW == 0 && it + 1 >= 0 && it + 1 < n_it) phase_b(wave, it + 1);
                     if (it >= 0 && it < n_it) compute(it, vin[sc]);
                     __syncthreads();
                 });
@@ -1032,6 +1120,30 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
                     if constexpr (CT == 2) *reinterpret_cast<float2*>(rp) = float2{S[0][t][i], S[1][t][i]};
                     else *rp = S[0][t][i];
                 }
+        }
+    } else if (is_bw) {
+        // phase-B waves (scalar gate): the same iterations and barriers
+        for (int attempt = 0; attempt < N_ATTEMPTS; ++attempt) {
+            begin_attempt(attempt);
+            if (n_it <= 0) break;
+            const int n_iter = (n_it + 2 + 2) / 3 * 3;
+            bool restart = false, done = false;
+            for (int k3 = 0; k3 < n_iter && !restart && !done; k3 += 3) {
+                static_for<0, 3>([&](auto u) __attribute__((always_inline)) {
+                    if (restart || done) return;
+                    const int it = k3 + u - 2;
+                    done = it >= n_it;
+                    if (done) return;
+                    if (failed_bound(it)) {
+                        restart = true;
+                        return;
+                    }
+                    if (it + 1 >= 0 && it + 1 < n_it) phase_b(wave - NCW, it + 1);
+                    __syncthreads();
+                });
+            }
+            if (!restart) break;
+            __syncthreads();
         }
     } else {
         for (int attempt = 0; attempt < N_ATTEMPTS; ++attempt) {
@@ -1081,7 +1193,7 @@ __global__ __launch_bounds__(64 * (K / 32 + 4)) void kda_fused_kernel(FusedArgs 
 template <int K, int V, bool GDN>
 static void launch_fused_t(const FusedArgs& a, int n_groups, hipStream_t stream,
                            const LaunchEvents* ev) {
-    using Lay = FusedLayout<K, V>;
+    using Lay = FusedLayout<K, V, GDN>;
     const dim3 grid((unsigned)n_groups), block(Lay::NT);
     if (ev)
         hipExtLaunchKernelGGL((kda_fused_kernel<K, V, GDN>), grid, block, 0, stream, ev->start,
