@@ -136,6 +136,16 @@ def test_gdn_small():
     check_parity(w, first_tokens=32)
 
 
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_gdn_head_dims_slow_decay(K, V):
+    # the scalar-gate single launch at every head-dimension pair (its workgroup
+    # has phase-B waves of their own: K/32 + 8 waves); slow decay, so the
+    # initial state and the earlier chunks reach the last tokens
+    w = inputs.gdn_workload(2, 300, 3, K, V, seed=3300 + K + V, init_std=0.05,
+                            decay_shift=-6.0, name=f"gdn_slow_K{K}_V{V}")
+    check_parity(w, first_tokens=32)
+
+
 def test_gdn_slow_decay_varlen():
     w = inputs.gdn_workload(1, 0, 3, 128, 128, seed=3500, init_std=0.05, decay_shift=-6.0,
                             lengths=[100, 1, 0, 64, 77])
