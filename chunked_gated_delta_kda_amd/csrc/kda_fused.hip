@@ -391,7 +391,10 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
                     // with y' = (g + dt_bias) log2 e:
-                    // log2 a = max(lb log2 e, -rate max(y', 0) - rate log2(1 + 2^-|y'|))
+                    // log2 a = max(lb log2 e, -rate log2(1 + 2^y')).  Where 2^y'
+                    // overflows the product is -inf (the floor binds), or NaN
+                    // for a padding row (factor -0), which the max drops (IEEE
+                    // maxNum returns the number): padding rows get 0
                     const float lb2 = a.lower_bound * LOG2E * vmask[b];
                     const float c1v = -rate * vmask[b];
 #pragma unroll
@@ -401,21 +404,9 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
                         for (int hh = 0; hh < 2; ++hh) {
                             const int e = 2 * u + hh;
                             const float y = fmaf(x2[hh], LOG2E, dt[e]);
-                            const float t = exp2_hw(-fabsf(y));
-                            G[b][e] = fmaxf(lb2, c1v * (fmaxf(y, 0.f) + log2_hw(1.f + t)));
+                            G[b][e] = fmaxf(lb2, c1v * log2_hw(1.f + exp2_hw(y)));
                         }
                     }
-                }
-                // the bound (used for warm-up chunks): max over this wave's
-                // channels of each token's log2 decay, from G before the prefix
-                // sums.  Unconditional: a branch around the scan keeps the compiler
-                // from fusing the scan's last DPP step (16 extra moves per chunk);
-                // the reduction over the lane's row groups below is not.
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    rmax[b] = G[b][0];
-#pragma unroll
-                    for (int e = 1; e < 8; ++e) rmax[b] = fmaxf(rmax[b], G[b][e]);
                 }
                 row_scan16_n<16>(&G[0][0]);
                 // the scan's results used here: later uses inside lane-masked
@@ -428,6 +419,19 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
             issue_loads();
             if (x < out_from) {  // only warm-up chunks need the bound
                 if constexpr (!GDN) {
+                    // the bound: max over this wave's channels of each token's
+                    // log2 decay (the differences of the prefix sums; the row's
+                    // first lane reads 0), then over the lane's row groups
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        rmax[b] = -INFINITY;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float prev =
+                                __builtin_amdgcn_update_dpp(0.f, G[b][e], ROW_SHR1, 0xf, 0xf, true);
+                            rmax[b] = fmaxf(rmax[b], G[b][e] - prev);
+                        }
+                    }
 #pragma unroll
                     for (int b = 0; b < 2; ++b) {
                         rmax[b] = fmaxf(rmax[b], __shfl_xor(rmax[b], 16, 64));
@@ -1101,7 +1105,8 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
                     // issued on some paths only makes the compiler's in-order
                     // wait counts cover the loads just issued as well
                     load_v(vin[sv], min(it + 2, n_it - 1));
-                    if (NBW == 0 && it + 1 >= 0 && it + 1 < n_it) phase_b(wave, it + 1);
+                    // (the last chunk's phase B runs on the prep waves, idle by then)
+                    if (NBW == 0 && it + 1 >= 0 && it + 1 < n_it - 1) phase_b(wave, it + 1);
                     if (it >= 0 && it < n_it) compute(it, vin[sc]);
                     __syncthreads();
                 });
@@ -1180,6 +1185,11 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
                     } else {
                         loads();
                         touch(pin[sa]);
+                        if (NBW == 0 && it + 1 == n_it - 1) {
+                            // all four parts over the K/32 prep waves
+#pragma unroll
+                            for (int w = 0; w < NCW; w += NPW) phase_b(p + w, it + 1);
+                        }
                     }
                     __syncthreads();
                 });
