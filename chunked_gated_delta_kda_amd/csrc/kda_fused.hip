@@ -37,7 +37,9 @@
 //     three waves at up to 168 registers each.  To fit, the scalar gate's
 //     recurrence forms S's bf16 operand one 32-channel slice at a time and
 //     its prep waves issue each block's partial products as soon as that
-//     block's operands exist.  (The per-channel gate, whose prep waves are as
+//     block's operands exist, and the coupling block Tb10 is formed once, by
+//     the wave of part 2 after parts 0 and 1 signal through LDS flags, and
+//     read from the record by the compute waves.  (The per-channel gate, whose prep waves are as
 //     long as its compute waves, measured 10% slower with the third wave: at
 //     168 registers its prep waves no longer keep their loads in flight
 //     across the decayed products.)
@@ -173,6 +175,20 @@ __device__ __forceinline__ float row_last(float x) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1f0));
 }
 
+// An LDS flag set by one wave and awaited by another within an iteration
+// (bounded: a wait that runs out proceeds, so no path can hang).
+__device__ __forceinline__ void flag_set(int* f, int v) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void flag_wait(int* f, int v) {
+    for (int n = 0; n < (1 << 22); ++n) {
+        if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == v) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 }  // namespace
 
 template <int K, int V, bool GDN>
@@ -282,6 +298,7 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
     }
 
     float* const misc = reinterpret_cast<float*>(lds + L::MISC);
+    int* const flags = reinterpret_cast<int*>(lds + L::MISC) + 1;  // [2]: parts 0, 1 done (phase-B waves)
 
     // An attempt computes chunks x0 .. c1 - 1 of the sequence, with outputs
     // from c0 on; attempts 0 and 1 (each after a failed bound) start
@@ -783,6 +800,7 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
             *reinterpret_cast<bf16xEL*>(rec + R::TB + lane * (2 * EL)) = pack_tok(tb, zero);
             float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 512;
             *reinterpret_cast<floatx4*>(cpl + 16 * m + 4 * g) = tb;  // Tb00 row-major
+            if constexpr (NBW > 0) flag_set(flags, x + 1);
         };
         // Phase B, part 1: block 1's A11, T11, Tb11 and the product T11 A10
         auto phase_p1 = [&](int x) __attribute__((always_inline)) {
@@ -811,6 +829,7 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
             // in every compute wave
             float* cpl = reinterpret_cast<float*>(lds + L::CPL) + slot * 512;
             *reinterpret_cast<floatx4*>(cpl + 256 + 4 * lane) = mt(a10, TT1);
+            if constexpr (NBW > 0) flag_set(flags + 1, x + 1);
         };
         // Phase B, part 2: the chunk's 1/||k|| and 1/||q|| (for the recurrence)
         // and Aqk's block 0
@@ -832,6 +851,23 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
             const floatx4 aq = build_aq(slot, 0, tile(slot, 2, lane), m, g);
             const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
             *reinterpret_cast<bf16xEL*>(rec + R::AQK + lane * (2 * EL)) = pack_tok(aq, zero);
+            if constexpr (NBW > 0) {
+                // Tb10 = -(T11 A10) Tb00 once, into the record (the compute
+                // waves, which set the pace here, read it), after parts 0 and
+                // 1 have left their fp32 tiles
+                flag_wait(flags, x + 1);
+                flag_wait(flags + 1, x + 1);
+                const float* cpl = reinterpret_cast<const float*>(lds + L::CPL) + slot * 512;
+                floatx4 tb00d;  // Tb00[4g + i][m]
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tb00d[i] = cpl[16 * (4 * g + i) + m];
+                const floatx4 ta = *reinterpret_cast<const floatx4*>(cpl + 256 + 4 * lane);
+                const floatx4 c = mt(tb00d, ta);
+                bf16x4 t10;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t10[i] = (bf16)(-c[i]);
+                *reinterpret_cast<bf16x4*>(rec + R::TB + (64 + lane) * (2 * EL)) = t10;
+            }
         };
         // Phase B, part 3: Aqk's block 1 and the decay bound of warm-up chunks
         auto phase_p3 = [&](int x) __attribute__((always_inline)) {
@@ -873,7 +909,7 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
             // Tb's block 1 = [Tb10 | Tb11]: Tb10 = -(T11 A10) Tb00 from phase
             // B's fp32 tiles (the same in every compute wave), Tb11 from the record
             bf16xEL tb1 = *reinterpret_cast<const bf16xEL*>(buf + R::TB + (64 + lane) * (2 * EL));
-            {
+            if constexpr (NBW == 0) {
                 const float* cpl = reinterpret_cast<const float*>(lds + L::CPL) + opaque_uniform(x & 1) * 512;
                 floatx4 tb00d;  // Tb00[4g + i][m]
 #pragma unroll
@@ -1084,7 +1120,10 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
         for (int attempt = 0; attempt < N_ATTEMPTS; ++attempt) {
             begin_attempt(attempt);
             load_state(exact);
-            if (tid == 0) misc[0] = 0.f;  // sum of the warm-up chunks' bounds
+            if (tid == 0) {
+                misc[0] = 0.f;  // sum of the warm-up chunks' bounds
+                flags[0] = flags[1] = 0;
+            }
             if (n_it <= 0) break;
             const int n_iter = (n_it + 2 + 2) / 3 * 3;
             VIn vin[3];
