@@ -502,9 +502,12 @@ BwdLayout bwd_part(const Common& c, int32_t N, const WsLayout& w) {
 }
 
 // kda_prep with the reverse-pass records, then the forward sweep that keeps
-// every chunk's entering state and V - KG S: with outputs (mode
-// RECUR_FWD_STORE, a forward pass whose backward pass follows) or without
-// (RECUR_STORE, inside the backward pass).
+// every chunk's entering state and V - KG S: with outputs (a forward pass
+// whose backward pass follows) or without (inside the backward pass).  KDA of
+// fixed length with V = 128: the single-launch kernel's storing variant (it
+// forms its own chunk operands in LDS, so the sweep reads only q, k, v, g and
+// beta); otherwise the recurrence over the records (modes RECUR_FWD_STORE /
+// RECUR_STORE).
 int run_fwd_states(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, bool outputs,
                    hipStream_t stream) {
     if (c.ws_bytes < bwd_workspace_bytes(c.B, c.T, c.H, c.K, c.V, N, c.varlen))
@@ -515,6 +518,25 @@ int run_fwd_states(const Common& c, int32_t N, kda::PrepArgs p, bool gdn, bool o
     p.brec = bl.brec;  // kda_prep also writes the reverse-pass records
     int st = run_prep(c, N, p, gdn, stream);
     if (st != KDA_OK) return st;
+    Common cf = c;
+    cf.split = 0;  // the single launch's own segment plan (the backward asks for none)
+    if (!outputs) {
+        cf.o = nullptr;
+        cf.final_state = nullptr;
+    }
+    Common probe = cf;  // the single launch's own checks (alignment, grid size)
+    if (!probe.o) probe.o = const_cast<uint16_t*>(probe.q);  // only checked, not written
+    int32_t nf = 0;
+    if (!c.varlen && !gdn && c.V == 128 && check_fused(probe, nf) == KDA_OK) {
+        kda::FusedArgs f{};
+        f.g_kda = p.g_kda;
+        f.A_log = p.A_log;
+        f.dt_bias = p.dt_bias;
+        f.lower_bound = p.lower_bound;
+        f.chunk_state = bl.hs;
+        f.chunk_u = bl.zt;
+        return run_fused(cf, N, f, gdn, stream);
+    }
     (void)hipGetLastError();
     kda::RecurArgs r{};
     r.v = c.v;

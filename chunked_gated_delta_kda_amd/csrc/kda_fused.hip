@@ -191,7 +191,12 @@ __device__ __forceinline__ void flag_wait(int* f, int v) {
 
 }  // namespace
 
-template <int K, int V, bool GDN>
+// STORE (KDA, two column tiles a wave): the variant that also keeps, for
+// every chunk with outputs, the bf16 state entering it and its V - KG S (the
+// quantities the backward pass reads), with the outputs optional (a.o may be
+// null).  GDN's twelve waves have 168 registers each, too few for the stores
+// without spilling.
+template <int K, int V, bool GDN, bool STORE>
 __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kernel(FusedArgs a) {
     using L = FusedLayout<K, V, GDN>;
     using R = Rec<K>;
@@ -900,6 +905,38 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
             const unsigned char* buf = lds + L::REC + opaque_uniform(x % 3) * R::BYTES;
             const int nvalid = nvalid_of(x);
             const bool outs = x >= out_from;
+            const bool want_o = outs && (!STORE || a.o != nullptr);
+            // the entering state, rounded to bf16 as for the products below,
+            // into chunk_state [slots, H, K, V], first (only the fp32 state is
+            // live yet).  A lane holds columns 2 lr, 2 lr + 1 of its channels;
+            // the lanes of a pair swap one word per two channels, so that each
+            // writes four adjacent columns of one channel: 8-byte stores, half
+            // as many as with the lane's own pairs
+            if constexpr (STORE && CT == 2) {
+                if (outs) {
+                    const int64_t sslot = (int64_t)n * ((a.T + C - 1) / C) + x0 + x;
+                    char* sbase = reinterpret_cast<char*>(a.chunk_state + (sslot * a.H + h) * K * V);
+                    const bool odd = lr & 1;
+                    const uint32_t cpair = (uint32_t)col_of(0, lr & ~1);
+                    auto pk = [](float lo, float hi) __attribute__((always_inline)) {
+                        return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)lo) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)hi) << 16);
+                    };
+#pragma unroll
+                    for (int t = 0; t < KT; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; i += 2) {
+                            const uint32_t w0 = pk(S[0][t][i], S[1][t][i]);
+                            const uint32_t w1 = pk(S[0][t][i + 1], S[1][t][i + 1]);
+                            // quad_perm [1, 0, 3, 2]: the pair partner's word
+                            const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(
+                                0, (int)(odd ? w0 : w1), 0xB1, 0xf, 0xf, false);
+                            const uint32_t ch = (uint32_t)tile_channel(t, 4 * lg + i + (odd ? 1 : 0));
+                            const uint2 val = odd ? uint2{recv, w1} : uint2{w0, recv};
+                            *reinterpret_cast<uint2*>(sbase + (ch * V + cpair) * 2u) = val;
+                        }
+                }
+            }
             // 1/||k|| of the lane's tokens 16 bb + 4 lg + i (the record holds the
             // raw keys and queries; phase B wrote these for the chunk)
             const float* invn = reinterpret_cast<const float*>(lds + L::INVN) + opaque_uniform(x % 3) * 64;
@@ -947,7 +984,7 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
 #pragma unroll
                         for (int ct = 0; ct < CT; ++ct) Y[ct][bb] = mfma32(kgo, sb[ct], Y[ct][bb]);
                     }
-                    if (outs) {
+                    if (want_o) {
 #pragma unroll
                         for (int ob = 0; ob < 2; ++ob) {
                             const bf16x8 qg = *reinterpret_cast<const bf16x8*>(
@@ -1001,7 +1038,7 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
                     }
                 // O^T = S^T QG^T (+ U'^T Aqk^T below), raw queries: scaled by
                 // 1/||q|| at the store
-                if (outs) {
+                if (want_o) {
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -1036,6 +1073,19 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
                     yc[ct][i] = (bf16)Y[ct][0][i];
                     yc[ct][4 + i] = (bf16)Y[ct][1][i];
                 }
+            if constexpr (STORE) {
+                // V - KG S into chunk_u [slots, H, V, C]: token 16 bb + 4 lg + i
+                // of column col_of(ct, lr) at position 8 lg + 4 bb + i (the
+                // k-slot order of the 32-token operands), 16 bytes a tile
+                if (outs) {
+                    const int64_t sslot = (int64_t)n * ((a.T + C - 1) / C) + x0 + x;
+                    char* ubase = reinterpret_cast<char*>(a.chunk_u + (sslot * a.H + h) * V * C);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        *reinterpret_cast<bf16xEL*>(
+                            ubase + ((uint32_t)col_of(ct, lr) * C + 8u * lg) * 2u) = yc[ct];
+                }
+            }
             floatx4 U[CT][2];
             {
                 const bf16xEL tb0 = *reinterpret_cast<const bf16xEL*>(buf + R::TB + lane * (2 * EL));
@@ -1063,7 +1113,7 @@ __global__ __launch_bounds__(64 * (K / 32 + (GDN ? 8 : 4))) void kda_fused_kerne
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) S[ct][t] = mfma_tok(kdt, uc[ct], S[ct][t]);
             }
-            if (!outs) return;
+            if (!want_o) return;
 #pragma unroll
             for (int ob = 0; ob < 2; ++ob) {
                 const bf16xEL aqk =
@@ -1244,11 +1294,17 @@ static void launch_fused_t(const FusedArgs& a, int n_groups, hipStream_t stream,
                            const LaunchEvents* ev) {
     using Lay = FusedLayout<K, V, GDN>;
     const dim3 grid((unsigned)n_groups), block(Lay::NT);
+    if constexpr (!GDN && Lay::CT == 2) {
+        if (a.chunk_state) {
+            hipLaunchKernelGGL((kda_fused_kernel<K, V, false, true>), grid, block, 0, stream, a);
+            return;
+        }
+    }
     if (ev)
-        hipExtLaunchKernelGGL((kda_fused_kernel<K, V, GDN>), grid, block, 0, stream, ev->start,
-                              ev->stop, 0, a);
+        hipExtLaunchKernelGGL((kda_fused_kernel<K, V, GDN, false>), grid, block, 0, stream,
+                              ev->start, ev->stop, 0, a);
     else
-        hipLaunchKernelGGL((kda_fused_kernel<K, V, GDN>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((kda_fused_kernel<K, V, GDN, false>), grid, block, 0, stream, a);
 }
 
 void launch_fused(const FusedArgs& a, int K, int V, bool gdn, int n_groups, hipStream_t stream,

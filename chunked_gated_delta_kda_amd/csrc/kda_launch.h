@@ -139,6 +139,11 @@ struct FusedArgs {
     int32_t warm_chunks_retry;  // the second attempt's warm-up (after a failed bound)
     float bound_limit;          // log2: a warm-up whose transitions are below this suffices
     int64_t tok_limit;          // tokens in the batch
+    // KDA of fixed length with V = 128 only (null otherwise): with chunk_state
+    // set, every chunk's entering state and V - KG S are stored, in the layouts
+    // of RecurArgs' fields of the same names, and o may be null (no outputs)
+    uint16_t* chunk_state;      // [slots, H, K, V] bf16
+    uint16_t* chunk_u;          // [slots, H, V, C] bf16, tokens in k-slot order
 };
 
 // Backward pass: the chunk-parallel gradient kernel (kda_bwd.hip).
